@@ -1,0 +1,272 @@
+/*
+ * ec.h - lossless fixed-codebook entropy coding of 8-bit e4m3 tensor bytes
+ *        on AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ *
+ * Codecs
+ *   QLC          Quad Length Codes: "Quad Length Codes for Lossless
+ *                Compression of e4m3", section 2.  Symbols ranked by
+ *                decreasing probability, 8 areas chosen by a 3-bit prefix,
+ *                one code length per area, 256-entry LUT encode, prefix ->
+ *                length decode.
+ *   Huffman      single-stage Huffman: "Single-Stage Huffman Encoder for ML
+ *                Compression", TL;DR and abstract.  One fixed codebook built
+ *                from the average distribution of earlier batches, stored on
+ *                the device, never sent with the data.
+ *   Exp-Golomb   order-k Exp-Golomb on the QLC rank, the universal-code
+ *                baseline of the QLC page, section 1.
+ *
+ * Memory and ownership
+ *   - Every pointer named d_* is device memory that the caller allocates and
+ *     owns.  Input and output buffers must be 16-byte aligned.
+ *   - ec_codebook is an opaque, library-owned handle made by a *_build_*
+ *     function and released with ec_codebook_free.  Its device tables are
+ *     allocated on the current device at its first GPU use and freed with
+ *     the handle.
+ *   - The encoder keeps a small look-back scratch buffer per device (8 bytes
+ *     per chunk), allocated at first use and kept until the process ends.
+ *     GPU calls that overlap in time on one device (different streams) share
+ *     it and race: order them (one stream, or events).
+ *
+ * Errors
+ *   - Functions return an ec_error code for argument, allocation and launch
+ *     problems; GPU work is enqueued asynchronously on the given stream.
+ *   - Data-dependent problems found on the device are OR-ed into a caller
+ *     zeroed status word (EC_S_* bits), readable after the stream syncs.
+ *     When a status bit is set, the output contents are unspecified.
+ *
+ * Stream container (this library's own; the pages fix the codes, not a byte
+ * format).  All integers little-endian.
+ *   offset 0   u32 magic 0x53384345 ("EC8S")    4  u16 version 1
+ *          6   u8  codec (ec_codec)             7  u8  flags (bit 0: code lengths embedded)
+ *          8   u64 n_symbols                   16  u32 chunk_symbols C (multiple of 256)
+ *         20   u32 n_chunks = ceil(n / C)      24  u64 payload_offset (multiple of 256)
+ *         32   u64 payload_bytes               40  u64 codebook_id
+ *         48   16 zero bytes
+ *         64   u64 chunk_off[n_chunks + 1]: byte offset of each chunk in the
+ *              payload; each a multiple of 16
+ *              u32 sub_end[n_chunks][C / 256]: bit offset, from the chunk's
+ *              start, where each 256-symbol sub-chunk ends; sub-chunks past
+ *              n hold the chunk's total bit count
+ *              u8 code_len[256] (only with flags bit 0)
+ *              zero bytes up to payload_offset
+ *   payload: chunk c occupies [chunk_off[c], chunk_off[c+1]); its bits form
+ *   32-bit little-endian words, bit i of the chunk being bit (31 - i % 32)
+ *   of word i / 32; codes are written most significant bit first in symbol
+ *   order; bits after the last code up to the 16-byte boundary are zero.
+ */
+#ifndef EC_H
+#define EC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of every int-returning function. */
+typedef enum ec_error {
+    EC_OK = 0,
+    EC_E_INVAL = 1,        /* bad argument: NULL, size, alignment, layout */
+    EC_E_UNSUPPORTED = 2,  /* e.g. a Huffman code longer than EC_MAX_CODE_LEN bits */
+    EC_E_NOMEM = 3,        /* host or device allocation failed */
+    EC_E_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+    EC_E_CAPACITY = 5      /* out_cap cannot even hold the header and index */
+} ec_error;
+
+/* Device status bits (OR-ed into *d_status). */
+#define EC_S_CAPACITY 0x1u          /* encoded stream longer than out_cap; nothing past out_cap written */
+#define EC_S_CORRUPT 0x2u           /* payload or index does not decode consistently */
+#define EC_S_BAD_HEADER 0x4u        /* magic, version, sizes or layout wrong */
+#define EC_S_CODEBOOK_MISMATCH 0x8u /* stream made with another codebook or codec */
+#define EC_S_INTERNAL 0x10u         /* encoder look-back wait expired (overlapping calls on one
+                                       device); the chunk's payload was not written */
+
+typedef enum ec_codec {
+    EC_CODEC_QLC = 1,
+    EC_CODEC_HUFFMAN = 2,
+    EC_CODEC_EXP_GOLOMB = 3
+} ec_codec;
+
+#define EC_MAX_CODE_LEN 40      /* longest Huffman code the GPU path supports */
+#define EC_MAX_BATCH 128        /* segments per batch call */
+
+typedef struct ec_codebook ec_codebook;
+
+/* ---------------------------------------------------------------------------
+ * Codebook builders (host only, no GPU needed).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * Quad Length Code ("Quad Length Codes for Lossless Compression of e4m3",
+ * section 2: areas, LUT encode; section 3: adapted area sizes).
+ *   counts[256]      byte frequencies; symbols are ranked by decreasing count,
+ *                    equal counts by increasing byte value
+ *   area_size[8]     symbols in area a = 0..7; must sum to 256
+ *   suffix_bits[8]   bits after the 3-bit prefix in area a, 0..8, with
+ *                    area_size[a] <= 2^suffix_bits[a]
+ * Rank r in area a is coded as a (3 bits) then r - first_rank(a)
+ * (suffix_bits[a] bits).  Base scheme: sizes 8,8,8,8,8,16,32,168 with suffix
+ * bits 3,3,3,3,3,4,5,8.  Returns EC_E_INVAL on a bad layout.
+ */
+int qlc_build_codebook(const uint64_t counts[256], const uint16_t area_size[8],
+                       const uint8_t suffix_bits[8], ec_codebook **out);
+
+/*
+ * Huffman codebook ("Single-Stage Huffman Encoder for ML Compression",
+ * abstract and method steps 2-3: one tree built from the average
+ * distribution of earlier batches).
+ *   counts[256]  summed byte counts of the calibration data (for shards of
+ *                equal size this is proportional to their average PMF).
+ *                Every symbol is weighted counts[s] + 1 so that symbols not
+ *                seen in calibration still get a code.
+ * The tree merges the two lightest nodes, ties ordered by (weight, leaves
+ * before internal nodes, byte value / creation order); codes are canonical
+ * in (length, byte) order.  EC_E_UNSUPPORTED if a code exceeds
+ * EC_MAX_CODE_LEN bits.
+ */
+int huff_build_codebook(const uint64_t counts[256], ec_codebook **out);
+
+/*
+ * Huffman codebook from 256 code lengths (as embedded in a stream by the
+ * three-stage path, single-stage Huffman page, abstract: the codebook
+ * transmitted with the data).  Lengths must form a complete prefix code
+ * (Kraft sum exactly 1) of at most EC_MAX_CODE_LEN bits, else EC_E_INVAL.
+ */
+int huff_build_codebook_from_lengths(const uint8_t code_len[256], ec_codebook **out);
+
+/*
+ * Exp-Golomb on rank (QLC page, section 1: universal codes such as
+ * Exponential-Golomb).  Symbols ranked as for QLC; rank r is coded with
+ * order k: v = r + 2^k, m = floor(log2 v), m - k zeros then v in m + 1 bits.
+ *   k in 0..8, or -1 to pick the k that minimises sum(counts * length),
+ *   ties to the smaller k.
+ */
+int eg_build_codebook(const uint64_t counts[256], int k, ec_codebook **out);
+
+/*
+ * Huffman code lengths for n (2..256) positive weights, same tree rule as
+ * huff_build_codebook but without the +1 smoothing and without a length
+ * cap.  len_out[n].
+ */
+int huff_code_lengths(const uint64_t *weights, uint32_t n, uint8_t *len_out);
+
+/*
+ * Describe a codebook.  Any output pointer may be NULL.
+ *   code[256]         code value of each byte (len low bits, MSB first)
+ *   code_len[256]     code length of each byte in bits
+ *   rank_to_sym[256]  QLC / Exp-Golomb rank order (zeros for Huffman)
+ *   eg_k              Exp-Golomb order (-1 for other codecs)
+ */
+int ec_codebook_info(const ec_codebook *cb, uint32_t *codec, uint32_t *max_len,
+                     uint64_t *codebook_id, uint8_t code_len[256], uint64_t code[256],
+                     uint8_t rank_to_sym[256], int32_t *eg_k);
+
+void ec_codebook_free(ec_codebook *cb);
+
+/* ---------------------------------------------------------------------------
+ * Stream sizing (host only).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes before the payload: header + index (+256 with embedded lengths),
+ * rounded up to 256.  0 on bad arguments. */
+uint64_t entropy_index_bytes(uint64_t n, uint32_t chunk_symbols, uint32_t embed_lengths);
+
+/* Largest possible stream for n symbols with this codebook.  0 on bad args. */
+uint64_t entropy_max_encoded_bytes(const ec_codebook *cb, uint64_t n, uint32_t chunk_symbols,
+                                   uint32_t embed_lengths);
+
+/* ---------------------------------------------------------------------------
+ * GPU operations: asynchronous on `stream` (0 = the null stream).
+ * ------------------------------------------------------------------------- */
+
+/*
+ * Encode n bytes (QLC page, section 2: "the encoder looks up the code in the
+ * table"; single-stage Huffman page, method step 4: encode directly with the
+ * precomputed codebook).
+ *   d_in           n input bytes
+ *   chunk_symbols  C: multiple of 256, 256..65536; chunks are coded
+ *                  independently and sub-chunk offsets every 256 symbols let
+ *                  the decoder start 256-symbol runs in parallel
+ *   d_out          out_cap bytes; receives the stream
+ *   d_out_len      device u64: the stream length, also when it exceeds
+ *                  out_cap (EC_S_CAPACITY is then set and nothing past
+ *                  out_cap is written)
+ *   d_status       device u32, caller-zeroed; may be NULL
+ * Returns EC_E_CAPACITY if out_cap < entropy_index_bytes(n, C, 0).
+ */
+int entropy_encode(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols,
+                   uint8_t *d_out, uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status,
+                   hipStream_t stream);
+
+/*
+ * Decode a stream made by entropy_encode with the same codebook (QLC page,
+ * section 2: read the 3-bit area code, which fixes the length, then the
+ * rest; area offset; second LUT.  Huffman: two-level table lookup instead of
+ * a bit-serial tree walk).
+ *   d_in    the stream; in_len = bytes readable at d_in (>= stream length)
+ *   d_out   n bytes; n must equal the stream's n_symbols
+ *   d_status  device u32, caller-zeroed; may be NULL.  Header, codebook and
+ *           consistency failures set EC_S_* bits; decoding never reads
+ *           outside [d_in, d_in + in_len).
+ */
+int entropy_decode(const ec_codebook *cb, const uint8_t *d_in, uint64_t in_len,
+                   uint8_t *d_out, uint64_t n, uint32_t *d_status, hipStream_t stream);
+
+/*
+ * Encode n_seg (1..EC_MAX_BATCH) segments of seg_n bytes in one launch.
+ * Segment s is read at d_in + s * in_stride and coded with cbs[s] (all
+ * entries may be the same handle: single-stage path; or one per shard:
+ * three-stage path, single-stage Huffman page, abstract).  Its stream goes
+ * to d_out + s * out_stride (out_stride bytes of capacity), its length to
+ * d_out_len[s], its status bits to d_status[s] (may be NULL).
+ * embed_lengths = 1 stores the 256 code lengths in each stream (the
+ * "codebook transmitted with the data" of the three-stage design).
+ */
+int entropy_encode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in,
+                         uint64_t seg_n, uint64_t in_stride, uint32_t chunk_symbols,
+                         uint32_t embed_lengths, uint8_t *d_out, uint64_t out_stride,
+                         uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream);
+
+/* Decode n_seg streams at d_in + s * in_stride (in_stride readable bytes
+ * each) into d_out + s * out_stride (seg_n bytes each). */
+int entropy_decode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in,
+                         uint64_t in_stride, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride,
+                         uint32_t *d_status, hipStream_t stream);
+
+/*
+ * Byte histogram of n_seg segments (single-stage Huffman page, method step
+ * 1 and the abstract's "frequency analysis" stage):
+ * d_counts[s * 256 + b] = number of bytes equal to b in segment s, read at
+ * d_in + s * in_stride (seg_n bytes; any alignment).  d_counts is
+ * overwritten.
+ */
+int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
+                   uint64_t *d_counts, hipStream_t stream);
+
+/*
+ * Average PMF of n_seg count rows (single-stage Huffman page, TL;DR and
+ * method step 2): d_pmf[b] = (1/S) sum_s counts[s][b] / sum_b' counts[s][b'],
+ * computed in fp32.  Rows with no counts contribute zero.
+ */
+int pmf_average(const uint64_t *d_counts, uint32_t n_seg, float *d_pmf, hipStream_t stream);
+
+/*
+ * KL divergence of each row from a reference (single-stage Huffman page,
+ * TL;DR and figure 3: KL of shard PMFs from the average PMF), in bits:
+ * d_kl_bits[s] = sum_{P_b > 0} P_b log2(P_b / Q_b), P the row's PMF,
+ * Q_b = (q_b + q_add) / sum(q + q_add).  fp32 result from a
+ * cancellation-free form; +inf when some Q_b = 0 < P_b.
+ */
+int pmf_kl(const uint64_t *d_p, uint32_t n_seg, const uint64_t *d_q, uint32_t q_add,
+           float *d_kl_bits, hipStream_t stream);
+
+/* Static text for an ec_error value or for a set of EC_S_* status bits. */
+const char *ec_error_string(int code);
+const char *ec_status_string(uint32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EC_H */

@@ -1,0 +1,332 @@
+// C ABI of libec: argument checks, per-device state and kernel launches.
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "dev_common.h"
+
+namespace ec {
+namespace {
+
+constexpr uint64_t kMaxSegSymbols = 1ull << 33;   // per stream
+constexpr int kMaxDevices = 16;
+
+// Look-back scratch of one device: one 64-bit flag word per chunk of a
+// launch and the chunk ticket counter.  Grown by doubling; retired buffers
+// are kept (a kernel still in flight may use them) until the process ends.
+struct DeviceState {
+    std::mutex mu;
+    uint64_t *flags = nullptr;
+    uint64_t capacity = 0;           // flag words
+    uint32_t *ticket = nullptr;
+    std::atomic<uint32_t> epoch{0};
+    std::vector<void *> retired;
+};
+
+DeviceState g_dev[kMaxDevices];
+
+int current_device(int *dev) {
+    if (hipGetDevice(dev) != hipSuccess) return EC_E_HIP;
+    if (*dev < 0 || *dev >= kMaxDevices) return EC_E_UNSUPPORTED;
+    return EC_OK;
+}
+
+// Flag words for `chunks` chunks and the epoch tagging this launch.
+int lookback_scratch(uint64_t chunks, hipStream_t s, uint64_t **flags, uint32_t **ticket, uint32_t *epoch) {
+    int dev;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lock(d.mu);
+    if (!d.ticket) {
+        if (hipMalloc(&d.ticket, 256) != hipSuccess) return EC_E_NOMEM;
+        if (hipMemset(d.ticket, 0, 256) != hipSuccess) return EC_E_HIP;
+    }
+    if (chunks > d.capacity) {
+        uint64_t cap = d.capacity ? d.capacity : 65536;
+        while (cap < chunks) cap *= 2;
+        uint64_t *p = nullptr;
+        if (hipMalloc(&p, cap * 8) != hipSuccess) return EC_E_NOMEM;
+        if (hipMemset(p, 0, cap * 8) != hipSuccess) return EC_E_HIP;   // epoch 0 is never current
+        if (d.flags) d.retired.push_back(d.flags);
+        d.flags = p;
+        d.capacity = cap;
+    }
+    uint32_t e = (d.epoch.fetch_add(1) + 1) & 0x3fffffffu;
+    if (e == 0) {
+        // the 30-bit tag wrapped: clear the words so old tags cannot match
+        if (launch_fill_u64(d.flags, d.capacity, 0, s) != hipSuccess) return EC_E_HIP;
+        e = (d.epoch.fetch_add(1) + 1) & 0x3fffffffu;
+    }
+    *flags = d.flags;
+    *ticket = d.ticket;
+    *epoch = e;
+    return EC_OK;
+}
+
+// Device copy of a codebook's tables on the current device.
+int device_tables(const ec_codebook *cbc, const DevTables **out) {
+    ec_codebook *cb = const_cast<ec_codebook *>(cbc);
+    int dev;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(cb->mu);
+    if (!cb->dev[dev]) {
+        DevTables *p = nullptr;
+        if (hipMalloc(&p, sizeof(DevTables)) != hipSuccess) return EC_E_NOMEM;
+        if (hipMemcpy(p, &cb->host, sizeof(DevTables), hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(p);
+            return EC_E_HIP;
+        }
+        cb->dev[dev] = p;
+    }
+    *out = cb->dev[dev];
+    return EC_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+bool chunk_ok(uint32_t C) { return C >= kMinChunk && C <= kMaxChunk && C % kSub == 0; }
+
+struct Layout {
+    uint64_t n_chunks, sub_at, index_end, payload_offset;
+};
+
+Layout layout(uint64_t n, uint32_t C, uint32_t embed) {
+    Layout l;
+    l.n_chunks = (n + C - 1) / C;
+    l.sub_at = kHeaderBytes + 8 * (l.n_chunks + 1);
+    l.index_end = l.sub_at + 4 * l.n_chunks * (C / kSub) + (embed ? 256 : 0);
+    l.payload_offset = (l.index_end + 255) / 256 * 256;
+    return l;
+}
+
+uint64_t max_payload(uint64_t n, uint32_t C, uint32_t max_len) {
+    const uint64_t full = n / C, rest = n % C;
+    auto chunk_bytes = [&](uint64_t syms) { return ((syms * max_len + 7) / 8 + 15) / 16 * 16; };
+    return full * chunk_bytes(C) + (rest ? chunk_bytes(rest) : 0);
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? EC_OK : EC_E_HIP; }
+
+int encode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
+                uint64_t in_stride, uint32_t C, uint32_t embed, uint8_t *d_out, uint64_t out_stride,
+                uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t s) {
+    if (!cbs || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_out || !d_out_len || !chunk_ok(C)) return EC_E_INVAL;
+    if (seg_n > kMaxSegSymbols || (seg_n && !d_in)) return EC_E_INVAL;
+    if (!aligned16(d_in) || !aligned16(d_out)) return EC_E_INVAL;
+    if (n_seg > 1 && (in_stride % 16 || out_stride % 16 || in_stride < seg_n || out_stride < out_cap))
+        return EC_E_INVAL;
+    const Layout L = layout(seg_n, C, embed);
+    if (L.payload_offset >= (1ull << 32) || L.n_chunks * n_seg >= (1ull << 31)) return EC_E_UNSUPPORTED;
+    if (out_cap < L.payload_offset) return EC_E_CAPACITY;
+
+    EncodeArgs a;
+    memset(&a, 0, sizeof(a));
+    uint32_t max_len = 1;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        if (!cbs[i]) return EC_E_INVAL;
+        int rc = device_tables(cbs[i], &a.tabs[i]);
+        if (rc) return rc;
+        max_len = cbs[i]->host.max_len > max_len ? cbs[i]->host.max_len : max_len;
+        if (embed && cbs[i]->host.codec != EC_CODEC_HUFFMAN) return EC_E_INVAL;
+    }
+    a.in = d_in;
+    a.in_stride = in_stride;
+    a.seg_n = seg_n;
+    a.out = d_out;
+    a.out_stride = out_stride;
+    a.out_cap = out_cap;
+    a.out_len = d_out_len;
+    a.status = d_status;
+    a.chunk_symbols = C;
+    a.chunks_per_seg = (uint32_t)L.n_chunks;
+    a.n_seg = n_seg;
+    a.payload_offset = (uint32_t)L.payload_offset;
+    a.sub_at = (uint32_t)L.sub_at;
+    a.embed_lengths = embed ? 1 : 0;
+    a.max_len = max_len;
+    if (L.n_chunks == 0) return hip_rc(launch_header_only(a, s));
+    int rc = lookback_scratch(L.n_chunks * n_seg, s, &a.flags, &a.ticket, &a.epoch);
+    if (rc) return rc;
+    return hip_rc(launch_encode(a, cbs[0]->host.codec, s));
+}
+
+int decode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t in_stride,
+                uint64_t in_len, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride, uint32_t *d_status,
+                hipStream_t s) {
+    if (!cbs || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_in || in_len < kHeaderBytes) return EC_E_INVAL;
+    if (seg_n > kMaxSegSymbols || (seg_n && !d_out)) return EC_E_INVAL;
+    if (!aligned16(d_in) || !aligned16(d_out)) return EC_E_INVAL;
+    if (n_seg > 1 && (in_stride % 16 || out_stride % 16 || in_stride < in_len || out_stride < seg_n))
+        return EC_E_INVAL;
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    const uint32_t codec = cbs[0] ? cbs[0]->host.codec : 0;
+    for (uint32_t i = 0; i < n_seg; ++i) {
+        if (!cbs[i] || cbs[i]->host.codec != codec) return EC_E_INVAL;
+        int rc = device_tables(cbs[i], &a.tabs[i]);
+        if (rc) return rc;
+    }
+    a.in = d_in;
+    a.in_stride = in_stride;
+    a.in_len = in_len;
+    a.out = d_out;
+    a.out_stride = out_stride;
+    a.seg_n = seg_n;
+    a.status = d_status;
+    a.n_seg = n_seg;
+    a.blocks_per_seg = (uint32_t)((seg_n + kSub - 1) / kSub);
+    return hip_rc(launch_decode(a, codec, cbs[0]->host.max_len, s));
+}
+
+}  // namespace
+}  // namespace ec
+
+using namespace ec;
+
+extern "C" {
+
+const char *ec_error_string(int code) {
+    switch (code) {
+        case EC_OK: return "ok";
+        case EC_E_INVAL: return "invalid argument";
+        case EC_E_UNSUPPORTED: return "unsupported";
+        case EC_E_NOMEM: return "out of memory";
+        case EC_E_HIP: return "HIP runtime error";
+        case EC_E_CAPACITY: return "output capacity too small for header and index";
+        default: return "unknown error";
+    }
+}
+
+const char *ec_status_string(uint32_t st) {
+    if (st == 0) return "ok";
+    if (st & EC_S_INTERNAL) return "internal: encoder look-back wait expired";
+    if (st & EC_S_BAD_HEADER) return "bad stream header";
+    if (st & EC_S_CODEBOOK_MISMATCH) return "stream made with another codebook";
+    if (st & EC_S_CORRUPT) return "corrupt stream";
+    if (st & EC_S_CAPACITY) return "output capacity exceeded";
+    return "unknown status";
+}
+
+int qlc_build_codebook(const uint64_t counts[256], const uint16_t area_size[8], const uint8_t suffix_bits[8],
+                       ec_codebook **out) {
+    return build_qlc(counts, area_size, suffix_bits, out);
+}
+
+int huff_build_codebook(const uint64_t counts[256], ec_codebook **out) {
+    if (!counts || !out) return EC_E_INVAL;
+    uint64_t w[256];
+    for (int s = 0; s < 256; ++s) {
+        if (counts[s] == UINT64_MAX) return EC_E_INVAL;
+        w[s] = counts[s] + 1;
+    }
+    uint8_t len[256];
+    int rc = huffman_lengths(w, 256, len);
+    if (rc) return rc;
+    return build_huffman_lengths(len, out);
+}
+
+int huff_build_codebook_from_lengths(const uint8_t code_len[256], ec_codebook **out) {
+    return build_huffman_lengths(code_len, out);
+}
+
+int eg_build_codebook(const uint64_t counts[256], int k, ec_codebook **out) { return build_eg(counts, k, out); }
+
+int huff_code_lengths(const uint64_t *weights, uint32_t n, uint8_t *len_out) {
+    return huffman_lengths(weights, n, len_out);
+}
+
+int ec_codebook_info(const ec_codebook *cb, uint32_t *codec, uint32_t *max_len, uint64_t *codebook_id,
+                     uint8_t code_len[256], uint64_t code[256], uint8_t rank_to_sym[256], int32_t *eg_k) {
+    if (!cb) return EC_E_INVAL;
+    const DevTables &t = cb->host;
+    if (codec) *codec = t.codec;
+    if (max_len) *max_len = t.max_len;
+    if (codebook_id) *codebook_id = t.codebook_id;
+    if (code_len) memcpy(code_len, t.code_len, 256);
+    if (code)
+        for (int s = 0; s < 256; ++s) code[s] = t.enc64[s] & ((1ull << 56) - 1);
+    if (rank_to_sym) {
+        if (t.codec == EC_CODEC_HUFFMAN)
+            memset(rank_to_sym, 0, 256);
+        else
+            memcpy(rank_to_sym, t.sym, 256);
+    }
+    if (eg_k) *eg_k = t.eg_k;
+    return EC_OK;
+}
+
+void ec_codebook_free(ec_codebook *cb) {
+    if (!cb) return;
+    for (int d = 0; d < kMaxDevices; ++d)
+        if (cb->dev[d]) {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            (void)hipSetDevice(d);
+            (void)hipFree(cb->dev[d]);
+            (void)hipSetDevice(cur);
+        }
+    delete cb;
+}
+
+uint64_t entropy_index_bytes(uint64_t n, uint32_t chunk_symbols, uint32_t embed_lengths) {
+    if (!chunk_ok(chunk_symbols) || n > kMaxSegSymbols) return 0;
+    return layout(n, chunk_symbols, embed_lengths).payload_offset;
+}
+
+uint64_t entropy_max_encoded_bytes(const ec_codebook *cb, uint64_t n, uint32_t chunk_symbols,
+                                   uint32_t embed_lengths) {
+    if (!cb || !chunk_ok(chunk_symbols) || n > kMaxSegSymbols) return 0;
+    return layout(n, chunk_symbols, embed_lengths).payload_offset + max_payload(n, chunk_symbols, cb->host.max_len);
+}
+
+int entropy_encode(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols, uint8_t *d_out,
+                   uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream) {
+    const ec_codebook *cbs[1] = {cb};
+    return encode_impl(cbs, 1, d_in, n, 0, chunk_symbols, 0, d_out, 0, out_cap, d_out_len, d_status, stream);
+}
+
+int entropy_decode(const ec_codebook *cb, const uint8_t *d_in, uint64_t in_len, uint8_t *d_out, uint64_t n,
+                   uint32_t *d_status, hipStream_t stream) {
+    const ec_codebook *cbs[1] = {cb};
+    return decode_impl(cbs, 1, d_in, 0, in_len, d_out, n, 0, d_status, stream);
+}
+
+int entropy_encode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
+                         uint64_t in_stride, uint32_t chunk_symbols, uint32_t embed_lengths, uint8_t *d_out,
+                         uint64_t out_stride, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream) {
+    return encode_impl(cbs, n_seg, d_in, seg_n, in_stride, chunk_symbols, embed_lengths, d_out, out_stride,
+                       out_stride, d_out_len, d_status, stream);
+}
+
+int entropy_decode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t in_stride,
+                         uint8_t *d_out, uint64_t seg_n, uint64_t out_stride, uint32_t *d_status,
+                         hipStream_t stream) {
+    return decode_impl(cbs, n_seg, d_in, in_stride, in_stride, d_out, seg_n, out_stride, d_status, stream);
+}
+
+int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride, uint64_t *d_counts,
+                   hipStream_t stream) {
+    if (!d_counts || n_seg == 0 || n_seg > 65535 || (seg_n && !d_in)) return EC_E_INVAL;
+    if (n_seg > 1 && in_stride < seg_n) return EC_E_INVAL;
+    if (seg_n >= (1ull << 40)) return EC_E_UNSUPPORTED;
+    return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, stream));
+}
+
+int pmf_average(const uint64_t *d_counts, uint32_t n_seg, float *d_pmf, hipStream_t stream) {
+    if (!d_pmf || (n_seg && !d_counts)) return EC_E_INVAL;
+    return hip_rc(launch_pmf_average(d_counts, n_seg, d_pmf, stream));
+}
+
+int pmf_kl(const uint64_t *d_p, uint32_t n_seg, const uint64_t *d_q, uint32_t q_add, float *d_kl_bits,
+           hipStream_t stream) {
+    if (!d_q || !d_kl_bits || (n_seg && !d_p) || n_seg > (1u << 30)) return EC_E_INVAL;
+    return hip_rc(launch_pmf_kl(d_p, n_seg, d_q, q_add, d_kl_bits, stream));
+}
+
+}  // extern "C"

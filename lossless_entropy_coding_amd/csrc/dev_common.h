@@ -1,0 +1,99 @@
+// Device-side helpers and launch interfaces shared by the libec kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "ec_internal.h"
+
+namespace ec {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B..E-1, so that
+// register arrays indexed by I stay in registers.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Table pointer of segment `seg`, read straight from the kernel-argument
+// segment (constant address space).  Indexing the by-value argument with a
+// run-time index would make the compiler copy the whole argument block
+// (with its 128 pointers) into per-lane scratch memory.
+template <class Args>
+__device__ __forceinline__ const DevTables *seg_tables(uint32_t seg) {
+    typedef __attribute__((address_space(4))) const Args CArgs;
+    const CArgs *p = (const CArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    return p->tabs[seg];
+}
+
+// Relaxed atomics at device (agent) scope: visible across the eight XCDs'
+// separate L2 caches without whole-cache writebacks.
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void or_status(uint32_t *status, uint32_t bits) {
+    if (status) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- launches
+
+struct EncodeArgs {
+    const uint8_t *in;
+    uint64_t in_stride;
+    uint64_t seg_n;
+    uint8_t *out;
+    uint64_t out_stride;
+    uint64_t out_cap;
+    uint64_t *out_len;        // [n_seg]
+    uint32_t *status;         // [n_seg] or null
+    uint64_t *flags;          // look-back words, one per chunk of the launch
+    uint32_t *ticket;         // chunk ticket counter (zero between launches)
+    uint32_t epoch;           // tag of this launch's look-back words
+    uint32_t chunk_symbols;
+    uint32_t chunks_per_seg;
+    uint32_t n_seg;
+    uint32_t payload_offset;
+    uint32_t sub_at;          // byte offset of sub_end[] in a stream
+    uint32_t embed_lengths;
+    uint32_t max_len;         // longest code over the launch's codebooks
+    const DevTables *tabs[EC_MAX_BATCH];
+};
+
+struct DecodeArgs {
+    const uint8_t *in;
+    uint64_t in_stride;
+    uint64_t in_len;          // readable bytes per stream
+    uint8_t *out;
+    uint64_t out_stride;
+    uint64_t seg_n;
+    uint32_t *status;         // [n_seg] or null
+    uint32_t n_seg;
+    uint32_t blocks_per_seg;  // 256-symbol runs per segment
+    const DevTables *tabs[EC_MAX_BATCH];
+};
+
+hipError_t launch_encode(const EncodeArgs &a, uint32_t codec, hipStream_t s);
+hipError_t launch_header_only(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t max_len, hipStream_t s);
+hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
+                            uint64_t *counts, hipStream_t s);
+hipError_t launch_pmf_average(const uint64_t *counts, uint32_t n_seg, float *pmf, hipStream_t s);
+hipError_t launch_pmf_kl(const uint64_t *p, uint32_t n_seg, const uint64_t *q, uint32_t q_add,
+                         float *kl, hipStream_t s);
+hipError_t launch_fill_u64(uint64_t *p, uint64_t n, uint64_t v, hipStream_t s);
+
+}  // namespace ec

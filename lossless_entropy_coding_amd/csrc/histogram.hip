@@ -1,0 +1,198 @@
+// Byte histogram and the PMF statistics kernels.
+//
+// Histogram: each workgroup counts a contiguous slice of one segment into
+// LDS bins privatised per wave and per lane group (so the skewed e4m3
+// distributions, where a few bytes dominate, do not serialise the LDS
+// atomics), then adds its bins to the 64-bit global counts.
+#include "dev_common.h"
+
+namespace ec {
+
+namespace {
+
+constexpr int kHistThreads = 256;
+constexpr int kHistCopies = 4;                 // LDS copies per wave
+constexpr int kHistVecPerThread = 16;          // 16-byte loads per thread per block
+
+__global__ void fill_u64_kernel(uint64_t *p, uint64_t n, uint64_t v) {
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
+                                                                 uint64_t seg_n, uint64_t in_stride,
+                                                                 uint64_t vec_per_block,
+                                                                 uint64_t *__restrict__ counts) {
+    __shared__ uint32_t bins[kHistThreads / 64 * kHistCopies][256];
+    const uint32_t tid = threadIdx.x;
+    uint32_t *mine = bins[(tid >> 6) * kHistCopies + (tid & (kHistCopies - 1))];
+    for (uint32_t i = tid; i < sizeof(bins) / 4; i += kHistThreads) (&bins[0][0])[i] = 0;
+    __syncthreads();
+
+    const uint32_t seg = blockIdx.y;
+    const uint8_t *base = in + (uint64_t)seg * in_stride;
+    // bytes before the first 16-byte boundary, then whole vectors, then a tail
+    const uint32_t head_max = (uint32_t)((16 - ((uintptr_t)base & 15)) & 15);
+    const uint64_t head = head_max < seg_n ? head_max : seg_n;
+    const uint8_t *vbase = base + head;
+    const uint64_t n_vec = (seg_n - head) / 16;
+    const uint64_t tail = (seg_n - head) % 16;
+    const uint64_t v0 = (uint64_t)blockIdx.x * vec_per_block;
+    const uint64_t v1 = v0 + vec_per_block < n_vec ? v0 + vec_per_block : n_vec;
+    const uint4 *vp = reinterpret_cast<const uint4 *>(vbase);
+    for (uint64_t v = v0 + tid; v < v1; v += kHistThreads) {
+        uint4 q = vp[v];
+        uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            atomicAdd(&mine[w[k] & 0xff], 1u);
+            atomicAdd(&mine[(w[k] >> 8) & 0xff], 1u);
+            atomicAdd(&mine[(w[k] >> 16) & 0xff], 1u);
+            atomicAdd(&mine[w[k] >> 24], 1u);
+        }
+    }
+    if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid]], 1u);
+    if (blockIdx.x == 0 && tid < tail) atomicAdd(&mine[vbase[n_vec * 16 + tid]], 1u);
+    __syncthreads();
+
+    uint32_t sum = 0;
+#pragma unroll
+    for (int c = 0; c < kHistThreads / 64 * kHistCopies; ++c) sum += bins[c][tid];
+    if (sum) atomicAdd(reinterpret_cast<unsigned long long *>(counts + (uint64_t)seg * 256 + tid),
+                       (unsigned long long)sum);
+}
+
+// ------------------------------------------------------------ PMF average
+
+// Block reduction of a 64-bit value over 256 threads (fixed order).
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t *scratch) {
+    const uint32_t tid = threadIdx.x;
+    scratch[tid] = v;
+    __syncthreads();
+    for (uint32_t s = 128; s > 0; s >>= 1) {
+        if (tid < s) scratch[tid] += scratch[tid + s];
+        __syncthreads();
+    }
+    uint64_t r = scratch[0];
+    __syncthreads();
+    return r;
+}
+
+// d_pmf[b] = mean over rows of counts[row][b] / total(row), fp32 with a
+// compensated (Kahan) running sum over the rows.
+__global__ __launch_bounds__(256) void pmf_average_kernel(const uint64_t *__restrict__ counts,
+                                                          uint32_t n_seg, float *__restrict__ pmf) {
+    __shared__ uint64_t scratch[256];
+    const uint32_t b = threadIdx.x;
+    float sum = 0.f, comp = 0.f;
+    for (uint32_t s = 0; s < n_seg; ++s) {
+        uint64_t c = counts[(uint64_t)s * 256 + b];
+        uint64_t total = block_sum_u64(c, scratch);
+        if (total == 0) continue;
+        float p = (float)c / (float)total;
+        float y = p - comp;
+        float t = sum + y;
+        comp = (t - sum) - y;
+        sum = t;
+    }
+    pmf[b] = n_seg ? sum / (float)n_seg : 0.f;
+}
+
+// ------------------------------------------------------------------ KL
+
+// phi(d) = (1 + d) ln(1 + d) - d >= 0, the Bregman term of KL in the ratio
+// r = 1 + d.  A series for small |d| avoids the cancellation of the closed
+// form: phi(d) = sum_{j>=2} (-1)^j d^j / (j (j - 1)).
+__device__ float kl_phi(float d) {
+    if (d <= -1.f) return 1.f;
+    if (fabsf(d) < 0.25f) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 14; j >= 3; --j) acc = 1.f / (float)(j * (j - 1)) - d * acc;
+        // acc = 1/6 - d/12 + d^2/20 - ... ; phi = d^2 (1/2 - d * acc)
+        return d * d * (0.5f - d * acc);
+    }
+    return (1.f + d) * log1pf(d) - d;
+}
+
+// One workgroup per row: D(P_row || Q) = sum_b Q_b phi(P_b / Q_b - 1) / ln 2,
+// which equals sum P log2(P / Q) because both distributions sum to one.
+// d = (p Nq - q Np) / (q Np) comes from exact integer products.
+__global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict__ pc, uint32_t n_seg,
+                                                     const uint64_t *__restrict__ qc, uint32_t q_add,
+                                                     float *__restrict__ kl) {
+    __shared__ uint64_t scratch[256];
+    __shared__ float fs[256];
+    const uint32_t b = threadIdx.x;
+    const uint32_t row = blockIdx.x;
+    const uint64_t p = pc[(uint64_t)row * 256 + b];
+    const uint64_t q = qc[b] + q_add;
+    const uint64_t np = block_sum_u64(p, scratch);
+    const uint64_t nq = block_sum_u64(q, scratch);
+    float term;
+    bool inf = false;
+    if (np == 0) {
+        term = 0.f;
+    } else if (q == 0) {
+        term = 0.f;
+        inf = p > 0;
+    } else if (p == 0) {
+        term = (float)q / (float)nq;               // phi(-1) = 1
+    } else {
+        float d;
+        if (np < (1ull << 31) && nq < (1ull << 31)) {
+            int64_t num = (int64_t)(p * nq) - (int64_t)(q * np);
+            uint64_t den = q * np;
+            d = (float)num / (float)den;
+        } else {
+            double r = ((double)p * (double)nq) / ((double)q * (double)np);
+            d = (float)(r - 1.0);
+        }
+        term = ((float)q / (float)nq) * kl_phi(d);
+    }
+    fs[b] = term;
+    __shared__ int any_inf;
+    if (b == 0) any_inf = 0;
+    __syncthreads();
+    if (inf) any_inf = 1;
+    for (uint32_t s = 128; s > 0; s >>= 1) {
+        if (b < s) fs[b] += fs[b + s];
+        __syncthreads();
+    }
+    if (b == 0) kl[row] = any_inf ? __builtin_inff() : fs[0] * 1.4426950408889634f;  // 1 / ln 2
+}
+
+}  // namespace
+
+hipError_t launch_fill_u64(uint64_t *p, uint64_t n, uint64_t v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
+                            uint64_t *counts, hipStream_t s) {
+    hipError_t e = launch_fill_u64(counts, (uint64_t)n_seg * 256, 0, s);
+    if (e != hipSuccess) return e;
+    const uint64_t n_vec = seg_n / 16;
+    const uint64_t per_block = (uint64_t)kHistThreads * kHistVecPerThread;
+    uint64_t blocks = (n_vec + per_block - 1) / per_block;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(histogram_kernel, dim3((unsigned)blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n,
+                       in_stride, per_block, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_pmf_average(const uint64_t *counts, uint32_t n_seg, float *pmf, hipStream_t s) {
+    hipLaunchKernelGGL(pmf_average_kernel, dim3(1), dim3(256), 0, s, counts, n_seg, pmf);
+    return hipGetLastError();
+}
+
+hipError_t launch_pmf_kl(const uint64_t *p, uint32_t n_seg, const uint64_t *q, uint32_t q_add, float *kl,
+                         hipStream_t s) {
+    if (n_seg == 0) return hipSuccess;
+    hipLaunchKernelGGL(pmf_kl_kernel, dim3(n_seg), dim3(256), 0, s, p, n_seg, q, q_add, kl);
+    return hipGetLastError();
+}
+
+}  // namespace ec

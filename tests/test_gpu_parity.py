@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact on streams, decoded bytes and histograms; PMF averages and KL
+divergences within 1e-5 relative (fp32 GPU vs fp64 oracle).
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codebooks as cbm
+from oracle import stats
+from oracle import stream as st
+
+from _util import deep_counts
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ec():
+    import lossless_entropy_coding_amd as ec
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ec.lib()
+    return ec
+
+
+DEV = "cuda:0"
+
+
+def _calib_counts(recipe="normal", seed=1, n=1 << 18):
+    return [int(c) for c in stats.histogram(synth.draw(recipe, seed, n))]
+
+
+def _pair(ec, name, counts):
+    if name == "qlc":
+        return ec.Codebook.qlc(counts), cbm.qlc_codebook(counts)
+    if name == "qlc_adapted":
+        return (ec.Codebook.qlc(counts, *ec.QLC_ADAPTED),
+                cbm.qlc_codebook(counts, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX))
+    if name == "huffman":
+        return ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
+    if name == "eg":
+        return ec.Codebook.exp_golomb(counts, -1), cbm.eg_codebook(counts)
+    if name == "eg0":
+        return ec.Codebook.exp_golomb(counts, 0), cbm.eg_codebook(counts, 0)
+    if name == "eg8":
+        return ec.Codebook.exp_golomb(counts, 8), cbm.eg_codebook(counts, 8)
+    raise KeyError(name)
+
+
+def _gpu_encode(ec, cb, x, C):
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if x.size else torch.zeros(16, dtype=torch.uint8,
+                                                                                      device=DEV)[:0]
+    out, out_len, status = ec.encode(cb, xd, C)
+    torch.cuda.synchronize()
+    L = int(out_len.item())
+    return out[:L].cpu().numpy().tobytes(), int(status.item())
+
+
+def _gpu_decode(ec, cb, stream_bytes, n):
+    d = torch.frombuffer(bytearray(stream_bytes), dtype=torch.uint8).to(DEV)
+    y, status = ec.decode(cb, d, n)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), int(status.item())
+
+
+CODECS = ["qlc", "qlc_adapted", "huffman", "eg", "eg0", "eg8"]
+SIZES = [(1, 256), (255, 4096), (256, 256), (257, 256), (4095, 4096), (4096, 4096), (4097, 4096),
+         (3 * 4096 + 17, 4096), (16384 * 3 + 999, 16384), (100_000, 1024), (70_001, 8192), (50_000, 12288)]
+
+
+@pytest.mark.parametrize("n,C", SIZES)
+@pytest.mark.parametrize("name", CODECS)
+def test_stream_and_round_trip_match_oracle(ec, name, n, C):
+    print("case", name, n, C, flush=True)
+    counts = _calib_counts()
+    cb, ocb = _pair(ec, name, counts)
+    x = synth.draw("ffn1", 7 + n, n)
+    want = st.encode_stream(x, ocb, C)
+    got, status = _gpu_encode(ec, cb, x, C)
+    assert status == 0
+    assert got == want
+    y, dstatus = _gpu_decode(ec, cb, want, n)
+    assert dstatus == 0
+    assert np.array_equal(y, x)
+
+
+def test_empty_input(ec):
+    counts = _calib_counts()
+    for name in ("qlc", "huffman", "eg"):
+        cb, ocb = _pair(ec, name, counts)
+        x = np.zeros(0, dtype=np.uint8)
+        want = st.encode_stream(x, ocb, 16384)
+        got, status = _gpu_encode(ec, cb, x, 16384)
+        assert status == 0 and got == want
+        y, dstatus = _gpu_decode(ec, cb, want, 0)
+        assert dstatus == 0 and y.size == 0
+
+
+@pytest.mark.parametrize("name", CODECS)
+def test_all_symbols_and_one_repeated_symbol(ec, name):
+    counts = _calib_counts()
+    cb, ocb = _pair(ec, name, counts)
+    for x in (np.tile(np.arange(256, dtype=np.uint8), 97), np.full(40000, 0x7E, dtype=np.uint8),
+              np.full(40000, np.argmax(ocb.length), dtype=np.uint8)):
+        want = st.encode_stream(x, ocb, 4096)
+        got, status = _gpu_encode(ec, cb, x, 4096)
+        assert status == 0 and got == want
+        y, dstatus = _gpu_decode(ec, cb, want, x.size)
+        assert dstatus == 0 and np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("depth", [24, 25, 33, 39, 40])
+def test_deep_huffman_codes(ec, depth):
+    counts = [int(c) for c in deep_counts(depth)]
+    cb, ocb = ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
+    assert ocb.max_len == depth
+    rng = np.random.default_rng(depth)
+    x = rng.integers(0, 256, 60000).astype(np.uint8)
+    x[::7] = np.argmax(ocb.length)                 # the deepest code, often
+    x[3::11] = 0                                   # and the shortest
+    want = st.encode_stream(x, ocb, 16384)
+    got, status = _gpu_encode(ec, cb, x, 16384)
+    assert status == 0 and got == want
+    y, dstatus = _gpu_decode(ec, cb, want, x.size)
+    assert dstatus == 0 and np.array_equal(y, x)
+
+
+def test_encode_is_deterministic(ec):
+    counts = _calib_counts()
+    cb, _ = _pair(ec, "huffman", counts)
+    x = torch.from_numpy(synth.draw("ffn1", 3, 1 << 22)).to(DEV)
+    ref = None
+    for _ in range(10):
+        out, out_len, status = ec.encode(cb, x, 16384)
+        torch.cuda.synchronize()
+        s = out[: int(out_len.item())].clone()
+        if ref is None:
+            ref = s
+        assert int(status.item()) == 0 and torch.equal(s, ref)
+
+
+@pytest.mark.parametrize("segs,seg_n", [(1, 1000), (3, 4 << 20), (8, 12345), (2, 1 << 16)])
+def test_histogram_matches_oracle(ec, segs, seg_n):
+    x = np.stack([synth.draw("ffn2", 50 + s, seg_n) for s in range(segs)])
+    h = ec.byte_histogram(torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    got = h.cpu().numpy().astype(np.uint64)
+    for s in range(segs):
+        assert np.array_equal(got[s], stats.histogram(x[s]))
+
+
+def test_pmf_average_and_kl_match_oracle(ec):
+    rows = [stats.histogram(synth.draw("ffn1", 100 + s, 1 << 20)) for s in range(8)]
+    shards = [stats.histogram(synth.batch_shards(1, 1 << 20, first_seed=1000 + i)[0]) for i in range(6)]
+    rows_t = torch.from_numpy(np.stack(rows).astype(np.int64)).to(DEV)
+    avg = ec.pmf_average(rows_t)
+    pooled = sum(r.astype(np.int64) for r in rows)
+    p_t = torch.from_numpy(np.stack(shards).astype(np.int64)).to(DEV)
+    q_t = torch.from_numpy(pooled.astype(np.int64)).to(DEV)
+    kl = ec.pmf_kl(p_t, q_t, q_add=1)
+    kl0 = ec.pmf_kl(rows_t[:1], rows_t[0], q_add=0)
+    torch.cuda.synchronize()
+    want_avg = stats.average_pmf(rows)
+    got_avg = avg.cpu().numpy().astype(np.float64)
+    for s in range(256):
+        if want_avg[s] > 0:
+            assert abs(got_avg[s] - want_avg[s]) <= 1e-5 * want_avg[s]
+        else:
+            assert got_avg[s] == 0
+    got_kl = kl.cpu().numpy().astype(np.float64)
+    for i, sh in enumerate(shards):
+        want = stats.kl_bits(sh, pooled, q_add=1)
+        assert want > 0 and abs(got_kl[i] - want) <= 1e-5 * want, (i, got_kl[i], want)
+    assert abs(float(kl0.item())) <= 1e-7       # D(P || P) = 0
+
+
+def test_kl_closed_forms(ec):
+    p = np.zeros(256, np.int64)
+    q = np.zeros(256, np.int64)
+    p[0], p[1] = 300_000, 700_000
+    q[0], q[1] = 400_000, 600_000
+    kl = ec.pmf_kl(torch.from_numpy(p).to(DEV), torch.from_numpy(q).to(DEV))
+    torch.cuda.synchronize()
+    want = 0.3 * np.log2(0.3 / 0.4) + 0.7 * np.log2(0.7 / 0.6)
+    assert abs(float(kl.item()) - want) <= 1e-5 * want
+    q[1] = 0     # a hole in Q under mass of P: infinite
+    kl = ec.pmf_kl(torch.from_numpy(p).to(DEV), torch.from_numpy(q).to(DEV))
+    torch.cuda.synchronize()
+    assert np.isinf(float(kl.item()))
+
+
+@pytest.mark.parametrize("per_segment", [False, True])
+@pytest.mark.parametrize("embed", [False, True])
+def test_batch_matches_oracle(ec, per_segment, embed):
+    S, seg_n, C = 5, 70_000, 16384
+    x = np.stack([synth.draw("ffn1", 200 + s, seg_n) for s in range(S)])
+    if per_segment:
+        cnts = [[int(c) for c in stats.histogram(x[s])] for s in range(S)]
+    else:
+        cnts = [_calib_counts("ffn1", 100)] * S
+    cbs = [ec.Codebook.huffman(c) for c in cnts]
+    ocbs = [cbm.huffman_codebook(c) for c in cnts]
+    xd = torch.from_numpy(x).to(DEV)
+    out, out_len, status = ec.encode_batch(cbs, xd, C, embed_lengths=embed)
+    torch.cuda.synchronize()
+    lens = out_len.cpu().numpy()
+    assert (status.cpu().numpy() == 0).all()
+    for s in range(S):
+        want = st.encode_stream(x[s], ocbs[s], C, embed_lengths=embed)
+        assert out[s, : int(lens[s])].cpu().numpy().tobytes() == want
+    y, dstatus = ec.decode_batch(cbs, out, seg_n)
+    torch.cuda.synchronize()
+    assert (dstatus.cpu().numpy() == 0).all()
+    assert np.array_equal(y.cpu().numpy(), x)
+
+
+def test_capacity_overflow_reports_required_length(ec):
+    counts = _calib_counts()
+    cb, ocb = _pair(ec, "qlc", counts)
+    x = synth.draw("ffn1", 11, 200_000)
+    want = st.encode_stream(x, ocb, 4096)
+    xd = torch.from_numpy(x).to(DEV)
+    cap = (len(want) - 1000) // 16 * 16
+    big = torch.full((cap + 8192,), 0xCD, dtype=torch.uint8, device=DEV)
+    out, guard = big[:cap], big[cap:]
+    _, out_len, status = ec.encode(cb, xd, 4096, out=out)
+    torch.cuda.synchronize()
+    assert int(status.item()) & ec.S_CAPACITY
+    assert int(out_len.item()) == len(want)
+    assert bool((guard == 0xCD).all())
+    with pytest.raises(ec.ECError):       # cannot even hold the index
+        ec.encode(cb, xd, 4096, out=torch.empty(100, dtype=torch.uint8, device=DEV))
+
+
+def test_corruption_and_header_errors_are_reported(ec):
+    counts = _calib_counts()
+    x = synth.draw("ffn1", 12, 100_000)
+    for name in ("qlc", "huffman", "eg"):
+        cb, ocb = _pair(ec, name, counts)
+        s = bytearray(st.encode_stream(x, ocb, 4096))
+        h = st.parse_header(bytes(s))
+        rng = np.random.default_rng(0)
+        for _ in range(8):
+            t = bytearray(s)
+            pos = h["payload_offset"] + int(rng.integers(0, h["payload_bytes"]))
+            t[pos] ^= 1 << int(rng.integers(0, 8))
+            y, status = _gpu_decode(ec, cb, bytes(t), x.size)
+            assert status & ec.S_CORRUPT or not np.array_equal(y, x)
+        t = bytearray(s)
+        t[0] ^= 1
+        assert _gpu_decode(ec, cb, bytes(t), x.size)[1] & ec.S_BAD_HEADER
+        same_codec_other, _ = _pair(ec, name, _calib_counts("ffn2", 5))
+        assert _gpu_decode(ec, same_codec_other, bytes(s), x.size)[1] & ec.S_CODEBOOK_MISMATCH
+        other_codec, _ = _pair(ec, "huffman" if name != "huffman" else "qlc", counts)
+        assert _gpu_decode(ec, other_codec, bytes(s), x.size)[1] & ec.S_CODEBOOK_MISMATCH
+        # a stream cut short: the header no longer fits the buffer
+        d = torch.frombuffer(bytearray(s), dtype=torch.uint8).to(DEV)
+        _, status = ec.decode(cb, d, x.size, in_len=len(s) - 16)
+        torch.cuda.synchronize()
+        assert int(status.item()) & ec.S_BAD_HEADER
+        # index pointing past the payload
+        t = bytearray(s)
+        t[64 + 8 * 3: 64 + 8 * 4] = (h["payload_bytes"] + 4096).to_bytes(8, "little")
+        assert _gpu_decode(ec, cb, bytes(t), x.size)[1] & ec.S_CORRUPT
+        # wrong n
+        d = torch.frombuffer(bytearray(s), dtype=torch.uint8).to(DEV)
+        _, status = ec.decode(cb, d, x.size - 1)
+        torch.cuda.synchronize()
+        assert int(status.item()) & ec.S_BAD_HEADER
+
+
+def test_qlc_unused_suffix_is_corrupt(ec):
+    counts = _calib_counts()
+    cb, ocb = _pair(ec, "qlc", counts)
+    x = np.zeros(256, dtype=np.uint8) + ocb.rank_to_sym[0]    # 256 six-bit zero codes
+    s = bytearray(st.encode_stream(x, ocb, 256))
+    h = st.parse_header(bytes(s))
+    po = h["payload_offset"]
+    # first code -> area 7 (prefix 111) with suffix 255 (>= 168: not a codeword)
+    word = int.from_bytes(s[po:po + 4], "little") | (0b11111111111 << 21)
+    s[po:po + 4] = word.to_bytes(4, "little")
+    y, status = _gpu_decode(ec, cb, bytes(s), x.size)
+    assert status & ec.S_CORRUPT
