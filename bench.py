@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Encode & decode throughput of e4m3 entropy coding on one MI355X.
+
+One step = the whole hot path over one synthetic shard, all on the GPU:
+  byte_histogram (distribution monitor) -> pmf_kl against the calibration
+  average -> for each codec of the workload: entropy_encode, entropy_decode.
+The codebooks are built once from calibration shards before timing (the
+single-stage design builds them off the critical path).
+
+value = uncompressed bytes round-tripped per second (codecs x N / step time).
+
+Prints ONE JSON line.  Options: --workload {ffn1,tiny_qlc,ffn2,grad,batch}.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encode & decode GB/s (uncompressed e4m3) on 1 MI355X, % HBM roofline; compression %"
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOAD_TEXT = {
+    "tiny_qlc": "tiny base-scheme QLC: 2^20 e4m3 bytes, N(0,1), seed 0; codebook from a 2^20 calibration draw (seed 1)",
+    "ffn1": "FFN1-activation-like shard 4096x16384 e4m3 (64 MiB): N(0,0.5^2) with 1% N(0,8^2) outliers, seed 2; "
+            "codebooks from 8 calibration shards of 2^22 (seeds 100-107)",
+    "ffn2": "FFN2-input-like shard 4096x16384 e4m3 (64 MiB): 0.25*GELU(N(0,1)), seed 3; calibration seeds 100-107",
+    "grad": "gradient-like shard 2048x16384 e4m3 (32 MiB): Laplace(0,0.02)*2^(6+e) per 128 block, seed 4; "
+            "calibration seeds 100-107",
+    "batch": "64 shards x 4 MiB FFN1-like e4m3 (256 MiB), sigma~U(0.4,0.6), seeds 1000-1063",
+}
+CODECS = {
+    "tiny_qlc": ["qlc"],
+    "ffn1": ["qlc", "huffman"],
+    "ffn2": ["qlc_adapted", "qlc", "huffman"],
+    "grad": ["eg", "qlc", "huffman"],
+}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="ffn1", choices=list(WORKLOAD_TEXT))
+    p.add_argument("--sets", type=int, default=3, help="buffer sets rotated per step (defeats the 256 MB MALL)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--copy-ref", action="store_true", help="also run plain device copies (counter calibration)")
+    p.add_argument("--verbose", action="store_true")
+    return p.parse_args()
+
+
+def log(args, *a):
+    if args.verbose:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def make_codebook(ec, name, counts):
+    if name == "qlc":
+        return ec.Codebook.qlc(counts)
+    if name == "qlc_adapted":
+        return ec.Codebook.qlc(counts, *ec.QLC_ADAPTED)
+    if name == "huffman":
+        return ec.Codebook.huffman(counts)
+    if name == "eg":
+        return ec.Codebook.exp_golomb(counts, -1)
+    raise KeyError(name)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "lossless_entropy_coding_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_file, workload, op):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    cur = source_hash(kernel_file)
+    for line in open(path):
+        m = re.match(r"^traffic\s+(\S+)\s+src=(\S+)\s+bytes=(\d+)", line)
+        if m and m.group(1) == op and m.group(2) == cur:
+            return int(m.group(3))
+    return None
+
+
+# ---------------------------------------------------------------- CPU leg
+
+def cpu_baseline(x, counts, codec_names, chunk, calib_rows):
+    """The oracle as it stands (single-threaded C + Python), timed on the
+    host over the same step on the same shard."""
+    from oracle import codebooks as cbm
+    from oracle import stats
+    from oracle import stream as st
+    builders = {
+        "qlc": lambda c: cbm.qlc_codebook(c),
+        "qlc_adapted": lambda c: cbm.qlc_codebook(c, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX),
+        "huffman": lambda c: cbm.huffman_codebook(c),
+        "eg": lambda c: cbm.eg_codebook(c),
+    }
+    cbs = [builders[n](counts) for n in codec_names]
+    t0 = time.perf_counter()
+    h = stats.histogram(x)
+    stats.kl_bits(h, counts, q_add=1)
+    for cb in cbs:
+        s = st.encode_stream(x, cb, chunk)
+        y = st.decode_stream(s, cb)
+        assert np.array_equal(y, x)
+    dt = time.perf_counter() - t0
+    return dict(value=round(len(codec_names) * x.size / dt / 1e9, 5), unit="GB/s", cores=1, kind="oracle",
+                sample="one full step on the same %d-byte shard (histogram, KL, %s encode+decode), "
+                       "single-threaded, %.1f s, host %s" % (x.size, "/".join(codec_names), dt,
+                                                             platform.processor() or platform.machine()))
+
+
+# ---------------------------------------------------------------- GPU leg
+
+def run_single(args, ec, torch):
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    codec_names = CODECS[args.workload]
+    C = w.chunk_symbols
+    t = time.perf_counter()
+    x = synth.workload(args.workload)
+    calib = synth.calibration_shards(args.workload)
+    log(args, "data %.1f s, sha256 %s" % (time.perf_counter() - t, synth.sha256(x)[:16]))
+    N = x.size
+
+    # calibration (off the critical path): GPU histograms, host codebook build
+    calib_d = torch.from_numpy(calib).to(dev)
+    rows_d = ec.byte_histogram(calib_d)
+    pooled_d = ec.byte_histogram(calib_d.view(-1))[0]
+    avg_pmf_d = ec.pmf_average(rows_d)
+    torch.cuda.synchronize()
+    counts = [int(c) for c in pooled_d.cpu().numpy().astype(np.uint64)]
+    t = time.perf_counter()
+    cbs = [make_codebook(ec, n, counts) for n in codec_names]
+    build_us = (time.perf_counter() - t) * 1e6
+    del calib_d
+
+    x_d = torch.from_numpy(x).to(dev)
+    sets = []
+    for i in range(args.sets):
+        xi = x_d if i == 0 else x_d.clone()
+        bufs = []
+        for cb in cbs:
+            cap = ec.max_encoded_bytes(cb, N, C)
+            bufs.append(dict(s=torch.empty(cap, dtype=torch.uint8, device=dev),
+                             y=torch.empty(N, dtype=torch.uint8, device=dev),
+                             n=torch.zeros(1, dtype=torch.int64, device=dev)))
+        sets.append(dict(x=xi, bufs=bufs, hist=torch.empty((1, 256), dtype=torch.int64, device=dev),
+                         kl=torch.empty(1, dtype=torch.float32, device=dev)))
+    status = torch.zeros(2 * len(cbs), dtype=torch.int32, device=dev)
+    nops = 2 + 2 * len(cbs)
+
+    def step(S, events=None):
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        rec(0)
+        ec.byte_histogram(S["x"], out=S["hist"])
+        rec(1)
+        ec.pmf_kl(S["hist"], pooled_d, q_add=1, out=S["kl"])
+        rec(2)
+        for j, cb in enumerate(cbs):
+            B = S["bufs"][j]
+            ec.encode(cb, S["x"], C, out=B["s"], out_len=B["n"], status=status[2 * j:2 * j + 1])
+            rec(3 + 2 * j)
+            ec.decode(cb, B["s"], N, out=B["y"], status=status[2 * j + 1:2 * j + 2], in_len=B["s"].numel())
+            rec(4 + 2 * j)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.copy_ref:   # plain copies of N bytes, for the hardware-counter scale factor
+        dst = torch.empty_like(x_d)
+        for _ in range(5):
+            dst.copy_(sets[-1]["x"])
+        torch.cuda.synchronize()
+
+    # correctness of what was timed
+    st = status.cpu().numpy()
+    if st.any():
+        raise SystemExit("device status bits set: %s" % st)
+    for S in sets:
+        for B in S["bufs"]:
+            if not torch.equal(B["y"], S["x"]):
+                raise SystemExit("round trip mismatch")
+    hist_ok = np.array_equal(sets[0]["hist"].cpu().numpy()[0], np.bincount(x, minlength=256))
+
+    op_names = ["byte_histogram", "pmf_kl"]
+    for n in codec_names:
+        op_names += ["%s_encode" % n, "%s_decode" % n]
+    per_op = {o: [] for o in op_names}
+    for e in evs:
+        for k, o in enumerate(op_names):
+            per_op[o].append(e[k].elapsed_time(e[k + 1]) * 1e3)   # us
+    stream_len = [int(B["n"].item()) for B in sets[0]["bufs"]]
+    kernels = {}
+    for o in op_names:
+        us = statistics.mean(per_op[o])
+        d = dict(us=round(us, 2), us_median=round(statistics.median(per_op[o]), 2))
+        if o == "byte_histogram":
+            moved = N + 256 * 8
+        elif o.endswith("_encode") or o.endswith("_decode"):
+            j = codec_names.index(o.rsplit("_", 1)[0])
+            moved = N + stream_len[j]
+        else:
+            moved = 2 * 256 * 8
+        d["GBps_uncompressed"] = round(N / us / 1e3, 1) if o != "pmf_kl" else None
+        d["hbm_GBps"] = round(moved / us / 1e3, 1)
+        d["roofline_frac"] = round(moved / us / 1e3 / HBM_PEAK_GBPS, 4)
+        kernels[o] = d
+
+    compression = {}
+    idx = ec.index_bytes(N, C)
+    for j, n in enumerate(codec_names):
+        payload = stream_len[j] - idx
+        compression[n] = dict(stream_bytes=stream_len[j], payload_pct=round(100 * (1 - payload / N), 3),
+                              stream_pct=round(100 * (1 - stream_len[j] / N), 3),
+                              max_code_len=cbs[j].max_len)
+
+    ms_per_step = wall / args.steps * 1e3
+    value = len(codec_names) * N / (wall / args.steps) / 1e9
+    dominant = max((o for o in op_names if o.endswith("code")), key=lambda o: kernels[o]["us"])
+    j = codec_names.index(dominant.rsplit("_", 1)[0])
+    moved = N + stream_len[j]
+    kfile = "decode.hip" if dominant.endswith("decode") else "encode.hip"
+    traffic = load_traffic(kfile, args.workload, dominant)
+    roofline = dict(kernel=dominant, bound="hbm", achieved=round(moved / kernels[dominant]["us"] / 1e3, 1),
+                    peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(moved / kernels[dominant]["us"] / 1e3 / HBM_PEAK_GBPS, 4),
+                    traffic=traffic, algorithmic_bytes=moved, avg_us=kernels[dominant]["us"])
+
+    kl = float(sets[0]["kl"].item())
+    out = dict(metric=METRIC, value=round(value, 2), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="u8", data="synthetic",
+               config=dict(workload=WORKLOAD_TEXT[args.workload], name=args.workload, n_bytes=N, chunk_symbols=C,
+                           codecs=codec_names, buffer_sets=args.sets,
+                           step="byte_histogram + pmf_kl + per codec entropy_encode + entropy_decode"),
+               roofline=roofline, kernels=kernels, compression=compression,
+               extra=dict(kl_bits_vs_calibration=kl, histogram_exact=hist_ok, codebook_build_us=round(build_us, 1),
+                          avg_pmf_top=float(avg_pmf_d.max().item()), numpy=np.__version__,
+                          input_sha256=synth.sha256(x)[:16]))
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(x, counts, codec_names, C, None)
+    else:
+        out["cpu_baseline"] = None
+    return out
+
+
+def run_batch(args, ec, torch):
+    """64 x 4 MiB shards: single-stage (one fixed avg-PMF Huffman codebook)
+    against three-stage (per-shard histogram, per-shard codebook built on the
+    host, codebook lengths embedded in each stream)."""
+    import synth
+    dev = torch.device("cuda:0")
+    C = 16384
+    t = time.perf_counter()
+    x = synth.batch_shards(64, 1 << 22)
+    calib = synth.calibration_shards("ffn1")
+    log(args, "data %.1f s" % (time.perf_counter() - t))
+    S, n = x.shape
+    x_d = torch.from_numpy(x).to(dev)
+    pooled_d = ec.byte_histogram(torch.from_numpy(calib).to(dev).view(-1))[0]
+    torch.cuda.synchronize()
+    counts = [int(c) for c in pooled_d.cpu().numpy()]
+    fixed = ec.Codebook.huffman(counts)
+    stride = (ec.max_encoded_bytes(fixed, n, C, True) + 255) // 256 * 256 + 4096
+    out = torch.empty((S, stride), dtype=torch.uint8, device=dev)
+    y = torch.empty((S, n), dtype=torch.uint8, device=dev)
+    lens = torch.zeros(S, dtype=torch.int64, device=dev)
+    status = torch.zeros(S, dtype=torch.int32, device=dev)
+    hist = torch.empty((S, 256), dtype=torch.int64, device=dev)
+    kl = torch.empty(S, dtype=torch.float32, device=dev)
+
+    def single():
+        ec.byte_histogram(x_d, out=hist)
+        ec.pmf_kl(hist, pooled_d, q_add=1, out=kl)
+        ec.encode_batch(fixed, x_d, C, out=out, out_len=lens, status=status)
+        ec.decode_batch(fixed, out, n, out=y, status=status)
+
+    def three():
+        ec.byte_histogram(x_d, out=hist)
+        h = hist.cpu().numpy()          # frequency analysis -> host
+        cbs = [ec.Codebook.huffman([int(c) for c in row]) for row in h]   # codebook generation
+        ec.encode_batch(cbs, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
+        ec.decode_batch(cbs, out, n, out=y, status=status)
+        return cbs
+
+    res = {}
+    for name, fn in (("single_stage", single), ("three_stage", three)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            keep = fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        if status.cpu().numpy().any() or not torch.equal(y, x_d):
+            raise SystemExit("batch round trip failed (%s)" % name)
+        L = lens.cpu().numpy()
+        res[name] = dict(ms_per_step=round(dt * 1e3, 4), GBps=round(S * n / dt / 1e9, 2),
+                         stream_pct=round(100 * (1 - L.sum() / (S * n)), 3))
+        del keep
+    klv = kl.cpu().numpy()
+    value = res["single_stage"]["GBps"]
+    return dict(metric=METRIC, value=value, unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=res["single_stage"]["ms_per_step"], higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="u8", data="synthetic",
+                config=dict(workload=WORKLOAD_TEXT["batch"], name="batch", n_bytes=S * n, chunk_symbols=C,
+                            codecs=["huffman"], step="histogram + KL + batch encode + batch decode"),
+                paths=res, kl_bits=dict(min=float(klv.min()), max=float(klv.max()), mean=float(klv.mean())),
+                roofline=None, cpu_baseline=None)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py: this engine runs on one GPU; --gpus %d is not supported (multi-GPU sharding is a "
+              "design note only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import lossless_entropy_coding_amd as ec
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ec.lib()
+    out = run_batch(args, ec, torch) if args.workload == "batch" else run_single(args, ec, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

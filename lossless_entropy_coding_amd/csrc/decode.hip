@@ -2,14 +2,18 @@
 //
 // Every 256-symbol sub-chunk starts at a bit offset recorded in the stream
 // index, so one lane decodes one sub-chunk serially and a wave64 decodes 64
-// of them side by side.  Each lane streams its bits through a 64-bit
-// MSB-aligned buffer refilled 32 bits at a time from a two-word prefetch
-// queue (loads are clamped to the payload, so a corrupt index can never make
-// a lane read outside the stream).
-//   QLC      the 3-bit prefix gives the code length through a packed
-//            constant (no memory access on the dependency chain); the top 11
-//            bits index a 2048-entry LDS table that yields the byte or flags
-//            an unused suffix.
+// consecutive sub-chunks side by side.  Their compressed bits form one
+// contiguous span of the payload (about 14 KiB at 16384-symbol chunks), which
+// the wave first copies into its own LDS region with coalesced 16-byte loads.
+// The decode loop then reads only LDS: a 32-bit window at any bit position is
+// one two-word LDS read plus a funnel shift and serves two codes of up to 16
+// bits each.  (A global load inside the loop would stall on the output
+// stores too: one counter tracks both.)  A span larger than the LDS region
+// (data that barely compresses) is decoded straight from global memory.
+//   QLC      the 3-bit prefix gives the code length through a packed constant
+//            (no memory access on the dependency chain); the top 11 bits index
+//            a 2048-entry LDS table that yields the byte or flags an unused
+//            suffix.
 //   Huffman  the top 11 bits index an LDS table: codes of up to 11 bits
 //            resolve there; longer codes point to a per-prefix second-level
 //            LDS table of up to 8 more bits; deeper codes (rare) are found by
@@ -25,62 +29,84 @@ namespace ec {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr uint32_t kSpanBytes = 16384;               // LDS staging per wave
+constexpr uint32_t kSpanRegion = kSpanBytes + 32;    // + a leading zero block and a trailing block
+constexpr uint32_t kGuardBytes = 1536;               // > 256 codes x 40 bits of overrun
 
-struct BitReader {
+// Bits of a lane's sub-chunk staged in LDS.  The wave's span is copied to
+// words 1.. of its region (word 0 is a zero guard), and x = 31 + the bit
+// position in the span, so the word holding the bit before the read position
+// is x >> 5 >= 0 and a 32-bit window never needs a special case.  Positions
+// only move forward from a validated start by at most 40 bits a code, and the
+// region is followed by guard words, so reads stay inside the allocation even
+// for corrupt streams.
+struct SpanBits {
+    static constexpr bool kStaged = true;
+    const uint32_t *words;   // region word 0 (the guard)
+    uint32_t x;
+
+    __device__ __forceinline__ uint32_t at(uint32_t xx) const {
+        const uint32_t *w = words + (xx >> 5);
+        return __builtin_amdgcn_alignbit(w[0], w[1], ~xx);
+    }
+    __device__ __forceinline__ uint32_t win() const { return at(x); }
+    __device__ __forceinline__ uint64_t win64() const { return ((uint64_t)at(x) << 32) | at(x + 32u); }
+    __device__ __forceinline__ void adv(uint32_t l) { x += l; }
+    __device__ __forceinline__ void prepare() {}
+    __device__ __forceinline__ uint64_t bit() const { return x - 31u; }
+};
+
+// Bits of a lane's sub-chunk read straight from global memory (spans that
+// do not fit in LDS): a 64-bit MSB-aligned buffer refilled 32 bits at a time,
+// loads clamped to the payload.
+struct GlobalBits {
+    static constexpr bool kStaged = false;
     const uint32_t *base;   // lane's first payload word
     uint32_t last;          // last readable word, relative to base
     uint64_t buf;           // next stream bits, MSB-aligned
-    uint32_t nb;            // valid bits in buf
-    uint32_t q0, q1;        // the following two words
+    uint32_t nb;            // valid bits in buf (>= 32 between calls)
     uint32_t nxt;           // next word to fetch, relative to base
-    uint64_t base0;         // absolute index of the lane's first word
+    uint64_t base0;         // absolute index of base
 
     __device__ __forceinline__ uint32_t word(uint32_t i) const { return base[i < last ? i : last]; }
-
-    __device__ __forceinline__ void init(const uint32_t *payload, uint32_t n_words, uint64_t bitpos) {
+    __device__ __forceinline__ void init(const uint32_t *payload, uint64_t n_words, uint64_t bitpos) {
         const uint64_t w0 = bitpos >> 5;
         const uint64_t lastw = n_words - 1;
         const uint64_t b = w0 < lastw ? w0 : lastw;
         base = payload + b;
         last = (uint32_t)(lastw - b);
+        base0 = w0;
         const uint32_t o = (uint32_t)(bitpos & 31);
         buf = (((uint64_t)word(0) << 32) | word(1)) << o;
         nb = 64 - o;
-        q0 = word(2);
-        q1 = word(3);
-        nxt = 4;
-        base0 = w0;
+        nxt = 2;
+        fill();
     }
-
-    // keep at least 32 valid bits
-    __device__ __forceinline__ void refill() {
-        if (nb <= 32) {
-            buf |= (uint64_t)q0 << (32 - nb);
+    __device__ __forceinline__ void fill() {
+        while (nb <= 32) {
+            buf |= (uint64_t)word(nxt) << (32 - nb);
             nb += 32;
-            q0 = q1;
-            q1 = word(nxt);
             ++nxt;
         }
     }
-    __device__ __forceinline__ uint32_t top() const { return (uint32_t)(buf >> 32); }
-    __device__ __forceinline__ void skip(uint32_t l) {
+    __device__ __forceinline__ uint32_t win() const { return (uint32_t)(buf >> 32); }
+    __device__ __forceinline__ uint64_t win64() const {
+        return buf | (nb <= 32 ? (uint64_t)word(nxt) << (32 - nb) : (uint64_t)word(nxt) >> (nb - 32));
+    }
+    __device__ __forceinline__ void adv(uint32_t l) {
+        if (l >= nb) {   // codes longer than the buffered bits (deep Huffman codes)
+            l -= nb;
+            buf = 0;
+            nb = 0;
+            fill();
+        }
         buf <<= l;
         nb -= l;
+        fill();
     }
-    // skip l > nb bits (only codes longer than 32 bits can need this)
-    __device__ void skip_long(uint32_t l) {
-        const uint32_t rest = l - nb;
-        buf = 0;
-        nb = 0;
-        refill();
-        skip(rest);
-    }
-    // 64 stream bits from the current position (valid when nb >= 8)
-    __device__ __forceinline__ uint64_t window64() const {
-        return buf | (nb <= 32 ? (uint64_t)q0 << (32 - nb) : (uint64_t)q0 >> (nb - 32));
-    }
-    // absolute bit position of the next unread bit
-    __device__ __forceinline__ uint64_t pos() const { return (base0 + nxt - 2) * 32 - nb; }
+    __device__ __forceinline__ void prepare() {}
+    __device__ __forceinline__ uint64_t bit() const { return (base0 + nxt) * 32 - nb; }
 };
 
 // Huffman code longer than the two table levels: canonical limit search on
@@ -95,24 +121,146 @@ __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DevTables *tab
     return tab->sym[idx & 255] | (l << 8);
 }
 
-template <int CODEC, int PERIOD>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
-    __shared__ uint4 l1v[kL1Size * 2 / 16];
-    __shared__ uint4 l2v[CODEC == EC_CODEC_HUFFMAN ? kL2Size * 2 / 16 : 1];
-    __shared__ uint8_t symtab[256];
-    __shared__ uint32_t s_ok, s_C, s_nch, s_spc;
-    __shared__ uint64_t s_po, s_pb;
-    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(l1v);
-    const uint16_t *l2 = reinterpret_cast<const uint16_t *>(l2v);
+// Huffman lookup for a window whose first-level entry e marks a long code:
+// second-level table, then (rare) the canonical limit search on 64 bits
+// taken at the source's current position.
+template <class Src>
+__device__ __forceinline__ uint32_t huff_long(uint32_t w, uint32_t e, const uint16_t *l2, const Src &S,
+                                              const DevTables *tab) {
+    const uint32_t w2 = ((e >> 12) & 7u) + 1u;
+    e = l2[(e & 0x7ffu) + ((w << kL1Bits) >> (32u - w2))];
+    if ((e >> 8) == 0) e = huff_deep(S.win64(), tab);
+    return e;
+}
 
-    const uint32_t tid = threadIdx.x;
+// Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
+// run) from source S into dst; returns the bits of the QLC / EG "not a
+// codeword" flags (bit 8 and up).
+template <int CODEC, int PAIRS, class Src>
+__device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *dst, const uint16_t *l1,
+                                               const uint16_t *l2, const uint8_t *symtab, const DevTables *tab,
+                                               uint32_t lens, uint32_t k_eg) {
+    uint32_t bad = 0;
+    // symbol | length << 8 of the code that starts the window w
+    auto sym_at = [&](uint32_t w) __attribute__((always_inline)) -> uint32_t {
+        if (CODEC == EC_CODEC_QLC) {
+            const uint32_t e = l1[w >> 21];
+            bad |= e;
+            return (e & 0xffu) | (((lens >> ((w >> 29) << 2)) & 15u) << 8);
+        } else if (CODEC == EC_CODEC_HUFFMAN) {
+            uint32_t e = l1[w >> 21];
+            if (e & kL1Long) e = huff_long(w, e, l2, S, tab);
+            return e;
+        } else {
+            const uint32_t zr = __clz(w);
+            const uint32_t z = zr < 8u ? zr : 8u;   // more zeros: not a codeword
+            const uint32_t l = 2 * z + k_eg + 1;
+            const uint32_t rank = (w >> (32 - l)) - (1u << k_eg);
+            bad |= rank | (zr > 8u ? kQlcInvalid : 0u);
+            return symtab[rank & 255u] | (l << 8);
+        }
+    };
+    auto one = [&]() __attribute__((always_inline)) -> uint32_t {
+        const uint32_t e = sym_at(S.win());
+        S.adv(e >> 8);
+        return e & 0xffu;
+    };
+    // two codes from one window when both fit in it; returns byte0 | byte1 << 8
+    auto two = [&]() __attribute__((always_inline)) -> uint32_t {
+        const uint32_t w = S.win();
+        const uint32_t e1 = sym_at(w);
+        const uint32_t n1 = e1 >> 8;
+        uint32_t e2;
+        if (CODEC == EC_CODEC_HUFFMAN) {
+            // the second code comes from the same window when the first left
+            // at least 11 bits and the second is a first-level code
+            S.adv(n1);
+            const uint32_t w2 = n1 <= 21u ? w << n1 : S.win();
+            e2 = l1[w2 >> 21];
+            if (e2 & kL1Long) {
+                const uint32_t wf = S.win();
+                e2 = huff_long(wf, l1[wf >> 21], l2, S, tab);
+            }
+            S.adv(e2 >> 8);
+        } else {
+            e2 = sym_at(w << n1);
+            S.adv(n1 + (e2 >> 8));
+        }
+        return __builtin_amdgcn_perm(e2, e1, 0x0c0c0400u);   // byte 0 of e1, byte 0 of e2
+    };
+    // eight codes -> two output words
+    auto eight = [&](uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {
+        S.prepare();
+        if (PAIRS) {
+            const uint32_t p0 = two(), p1 = two(), p2 = two(), p3 = two();
+            lo = p0 | (p1 << 16);
+            hi = p2 | (p3 << 16);
+        } else {
+            uint32_t b[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) b[k] = one();
+            lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+            hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+        }
+    };
+
+    if (cnt == kSub && Src::kStaged) {
+        // 128 decoded bytes are collected in registers and written as one
+        // whole cache line: 16-byte stores to 64 lanes' separate lines leave
+        // partial lines in L2 that get written back more than once
+        for (int half = 0; half < 2; ++half) {
+            uint32_t o[32];
+            static_for<0, 16>([&](auto hc) __attribute__((always_inline)) {
+                constexpr int h = decltype(hc)::value;
+                eight(o[2 * h], o[2 * h + 1]);
+                // keep each group's table reads next to their use (without
+                // this the scheduler hoists all 128 symbols' reads and spills)
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            uint4 *line = reinterpret_cast<uint4 *>(dst + 128 * half);
+            static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                line[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+            });
+        }
+    } else if (cnt == kSub) {
+        for (int i = 0; i < kSub / 16; ++i) {
+            uint32_t o[4];
+            eight(o[0], o[1]);
+            eight(o[2], o[3]);
+            *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
+        for (uint32_t k = 0; k < cnt; ++k) dst[k] = (uint8_t)one();
+    }
+    return bad;
+}
+
+template <int CODEC, int PAIRS>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
+    // tables first, so that their addresses fit the LDS instructions' offset field
+    struct Smem {
+        uint4 l1v[CODEC == EC_CODEC_EXP_GOLOMB ? 1 : kL1Size * 2 / 16];
+        uint4 l2v[CODEC == EC_CODEC_HUFFMAN ? kL2Size * 2 / 16 : 1];
+        uint8_t symtab[256];
+        uint64_t po, pb;
+        uint32_t ok, nch, spc;
+        uint32_t pad_;
+        uint4 spans[kWaves][kSpanRegion / 16];
+        uint4 guard[kGuardBytes / 16];
+    };
+    __shared__ Smem sm;
+    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.l1v);
+    const uint16_t *l2 = reinterpret_cast<const uint16_t *>(sm.l2v);
+    uint8_t *symtab = sm.symtab;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t seg = blockIdx.y;
     const DevTables *tab = seg_tables<DecodeArgs>(seg);
     const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
     uint32_t *status = a.status ? a.status + seg : nullptr;
 
-    if (CODEC != EC_CODEC_EXP_GOLOMB) l1v[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
-    if (CODEC == EC_CODEC_HUFFMAN) l2v[tid] = reinterpret_cast<const uint4 *>(tab->l2)[tid];
+    if (CODEC != EC_CODEC_EXP_GOLOMB) sm.l1v[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
+    if (CODEC == EC_CODEC_HUFFMAN) sm.l2v[tid] = reinterpret_cast<const uint4 *>(tab->l2)[tid];
     if (CODEC == EC_CODEC_EXP_GOLOMB) symtab[tid] = tab->sym[tid];
 
     if (tid == 0) {
@@ -132,114 +280,112 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
         } else {
             uint64_t end = kHeaderBytes + 8ull * (nch + 1) + 4ull * nch * (C / kSub) + ((flags & 1) ? 256 : 0);
             end = (end + 255) / 256 * 256;
-            if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0)) bits = EC_S_BAD_HEADER;
+            if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
+                bits = EC_S_BAD_HEADER;
         }
-        s_ok = bits == 0;
+        sm.ok = bits == 0;
         if (bits && blockIdx.x == 0) or_status(status, bits);
-        s_C = C;
-        s_nch = nch;
-        s_spc = C / kSub;
-        s_po = po;
-        s_pb = pb;
+        sm.nch = nch;
+        sm.spc = C / kSub;
+        sm.po = po;
+        sm.pb = pb;
     }
     __syncthreads();
-    if (!s_ok) return;
+    if (!sm.ok) return;
 
-    const uint32_t g = blockIdx.x * kThreads + tid;   // 256-symbol run within the segment
-    if (g >= a.blocks_per_seg) return;
-    const uint32_t spc = s_spc;
-    const uint32_t c = g / spc, j = g - c * spc;
+    // this lane's run and its place in the index
+    const uint32_t g0 = blockIdx.x * kThreads + wave * 64;   // the wave's first run
+    if (g0 >= a.blocks_per_seg) return;                      // whole wave idle
+    const uint32_t g = g0 + lane;
+    const bool active = g < a.blocks_per_seg;
+    const uint32_t spc = sm.spc;
+    const uint64_t pb = sm.pb;
     const uint64_t *chunk_off = reinterpret_cast<const uint64_t *>(stream + kHeaderBytes);
-    const uint32_t *sub_end = reinterpret_cast<const uint32_t *>(stream + kHeaderBytes + 8ull * (s_nch + 1));
+    const uint32_t *sub_end = reinterpret_cast<const uint32_t *>(stream + kHeaderBytes + 8ull * (sm.nch + 1));
+    const uint32_t gl = active ? g : a.blocks_per_seg - 1;
+    const uint32_t c = gl / spc, j = gl - c * spc;
     const uint64_t co0 = chunk_off[c], co1 = chunk_off[c + 1];
     const uint32_t e_end = sub_end[(uint64_t)c * spc + j];
     const uint32_t e_start = j ? sub_end[(uint64_t)c * spc + j - 1] : 0u;
-    if (co0 > co1 || co1 > s_pb || (co0 & 15) || (uint64_t)e_end > (co1 - co0) * 8 || e_start > e_end) {
-        or_status(status, EC_S_CORRUPT);
-        return;
-    }
+    const bool ok = active && co0 <= co1 && co1 <= pb && !(co0 & 15) && (uint64_t)e_end <= (co1 - co0) * 8 &&
+                    e_start <= e_end;
+    if (active && !ok) or_status(status, EC_S_CORRUPT);
+
+    // the wave's span: from the first lane's chunk start to the last lane's chunk end
+    const uint32_t g_last = (g0 + 63 < a.blocks_per_seg ? g0 + 63 : a.blocks_per_seg - 1);
+    const uint64_t span_lo = chunk_off[g0 / spc] & ~15ull;
+    const uint64_t span_hi = chunk_off[g_last / spc + 1];
+    bool fits = span_lo <= span_hi && span_hi <= pb && span_hi - span_lo <= kSpanBytes;
+    fits = fits && __ballot(ok && (co0 < span_lo || co1 > span_hi)) == 0;
+
     const uint64_t first_sym = (uint64_t)g * kSub;
-    const uint32_t cnt = a.seg_n - first_sym < kSub ? (uint32_t)(a.seg_n - first_sym) : (uint32_t)kSub;
-
-    BitReader R;
-    R.init(reinterpret_cast<const uint32_t *>(stream + s_po), (uint32_t)(s_pb >> 2), co0 * 8 + e_start);
-
+    const uint32_t cnt = !active ? 0u
+                         : (a.seg_n - first_sym < kSub ? (uint32_t)(a.seg_n - first_sym) : (uint32_t)kSub);
+    uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + first_sym;
     const uint32_t lens = tab->qlc_lens;
     const uint32_t k_eg = (uint32_t)tab->eg_k;
+    const uint4 *payload = reinterpret_cast<const uint4 *>(stream + sm.po);
     uint32_t bad = 0;
+    uint64_t end_pos = 0, want_pos = 0;
 
-    auto step = [&]() -> uint32_t {
-        const uint32_t t = R.top();
-        if (CODEC == EC_CODEC_QLC) {
-            const uint32_t e = l1[t >> 21];
-            bad |= e;
-            R.skip((lens >> ((t >> 29) << 2)) & 15u);
-            return e & 0xffu;
-        } else if (CODEC == EC_CODEC_HUFFMAN) {
-            uint32_t e = l1[t >> 21];
-            if (e & kL1Long) {
-                const uint32_t w2 = ((e >> 12) & 7u) + 1u;
-                e = l2[(e & 0x7ffu) + ((t << kL1Bits) >> (32u - w2))];
-                if ((e >> 8) == 0) e = huff_deep(R.window64(), tab);
-            }
-            const uint32_t l = e >> 8;
-            if (l <= R.nb)
-                R.skip(l);
-            else
-                R.skip_long(l);
-            return e & 0xffu;
-        } else {
-            uint32_t z = __clz(t);
-            if (z > 8) {
-                bad |= kQlcInvalid;
-                z = 8;
-            }
-            const uint32_t l = 2 * z + k_eg + 1;
-            const uint32_t rank = (t >> (32 - l)) - (1u << k_eg);
-            if (rank > 255) bad |= kQlcInvalid;
-            R.skip(l);
-            return symtab[rank & 255u];
+    if (fits) {
+        // coalesced copy of the span into this wave's LDS region: region
+        // block 0 is zero (its last word is the guard before the span), the
+        // span follows from block 1, and a zero block closes it
+        uint4 *region = sm.spans[wave];
+        const uint32_t nblk = (uint32_t)((span_hi - span_lo + 15) >> 4);
+        const uint4 *src = payload + (span_lo >> 4);
+        for (uint32_t i = lane; i < nblk; i += 256) {   // four 1 KiB loads in flight per pass
+            const uint32_t last = nblk - 1;
+            const uint4 v0 = src[min(i, last)], v1 = src[min(i + 64, last)];
+            const uint4 v2 = src[min(i + 128, last)], v3 = src[min(i + 192, last)];
+            region[1 + i] = v0;
+            if (i + 64 < nblk) region[1 + i + 64] = v1;
+            if (i + 128 < nblk) region[1 + i + 128] = v2;
+            if (i + 192 < nblk) region[1 + i + 192] = v3;
         }
-    };
-
-    uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + first_sym;
-    if (cnt == kSub) {
-        for (int i = 0; i < kSub / 16; ++i) {
-            uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                if (k % PERIOD == 0) R.refill();
-                w[k >> 2] |= step() << (8 * (k & 3));
-            }
-            *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (lane == 0) region[0] = make_uint4(0u, 0u, 0u, 0u);
+        if (lane == 1) region[1 + nblk] = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (ok) {
+            SpanBits S;
+            S.words = reinterpret_cast<const uint32_t *>(region) + 3;   // the guard word before the span
+            S.x = (uint32_t)((co0 - span_lo) * 8 + e_start) + 31u;
+            bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, l2, symtab, tab, lens, k_eg);
+            end_pos = S.bit();
+            want_pos = (co0 - span_lo) * 8 + e_end;
         }
-    } else {
-        for (uint32_t k = 0; k < cnt; ++k) {
-            R.refill();
-            dst[k] = (uint8_t)step();
-        }
+    } else if (ok) {
+        GlobalBits S;
+        S.init(reinterpret_cast<const uint32_t *>(payload), pb >> 2, co0 * 8 + e_start);
+        bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, l2, symtab, tab, lens, k_eg);
+        end_pos = S.bit();
+        want_pos = co0 * 8 + e_end;
     }
-    if ((bad & kQlcInvalid) || R.pos() != ((uint64_t)co0 * 8 + e_end)) or_status(status, EC_S_CORRUPT);
+    if (ok && ((bad & ~0xffu) || end_pos != want_pos)) or_status(status, EC_S_CORRUPT);
 }
 
-template <int CODEC, int PERIOD>
+template <int CODEC, int PAIRS>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
     uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads;
     if (gx == 0) gx = 1;   // still validate the header
-    hipLaunchKernelGGL((decode_kernel<CODEC, PERIOD>), dim3(gx, a.n_seg), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<CODEC, PAIRS>), dim3(gx, a.n_seg), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t /*max_len*/, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t max_len, hipStream_t s) {
     switch (codec) {
         case EC_CODEC_QLC:
-            return launch_one<EC_CODEC_QLC, 2>(a, s);   // codes <= 11 bits: 2 per 32 buffered bits
+            return launch_one<EC_CODEC_QLC, 1>(a, s);        // codes <= 11 bits
         case EC_CODEC_HUFFMAN:
-            return launch_one<EC_CODEC_HUFFMAN, 1>(a, s);
+            return launch_one<EC_CODEC_HUFFMAN, 1>(a, s);    // pairs when they fit, else one per window
         default:
-            return launch_one<EC_CODEC_EXP_GOLOMB, 1>(a, s);
+            if (max_len <= 16) return launch_one<EC_CODEC_EXP_GOLOMB, 1>(a, s);
+            return launch_one<EC_CODEC_EXP_GOLOMB, 0>(a, s);
     }
 }
 

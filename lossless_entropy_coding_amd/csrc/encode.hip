@@ -29,6 +29,7 @@ constexpr int kRowSyms = kThreads * kPiece;    // 4096
 constexpr uint64_t kFlagAgg = 1ull << 62;      // chunk size published, prefix not yet known
 constexpr uint64_t kFlagPrefix = 2ull << 62;   // inclusive prefix published
 constexpr uint32_t kMaxSpins = 1u << 22;       // look-back wait bound (about 0.1-1 s)
+constexpr int kLookGroups = 4;                 // look-back reads 4 x 64 predecessors per pass
 
 // Byte K (compile-time) of a 16-byte piece, in memory order.
 template <int K>
@@ -61,56 +62,64 @@ __device__ __forceinline__ uint32_t piece_len(const uint4 &v, uint32_t vb, const
     return x;
 }
 
-// Append the l low bits of c (l <= 32) to the accumulator; a finished 32-bit
-// word is OR-ed into the LDS buffer (its neighbours' bits may share it).
-__device__ __forceinline__ void put_bits(uint32_t c, uint32_t l, uint64_t &acc, uint32_t &n, uint32_t &widx,
-                                         uint32_t *buf) {
-    acc |= (uint64_t)c << (64 - n - l);
-    n += l;
-    if (n >= 32) {
-        atomicOr(&buf[widx], (uint32_t)(acc >> 32));
-        acc <<= 32;
-        n -= 32;
-        ++widx;
-    }
-}
-
-template <bool WIDE>
-__device__ __forceinline__ void put_symbol(uint32_t b, const uint32_t *lut32, const uint64_t *lut64, uint64_t &acc,
-                                           uint32_t &n, uint32_t &widx, uint32_t *buf) {
-    if (WIDE) {
-        const uint64_t e = lut64[b];
-        const uint32_t l = (uint32_t)(e >> 56);
-        const uint64_t c = e & ((1ull << 56) - 1);
-        if (l > 32) {
-            put_bits((uint32_t)(c >> 32), l - 32, acc, n, widx, buf);
-            put_bits((uint32_t)c, 32, acc, n, widx, buf);
-        } else {
-            put_bits((uint32_t)c, l, acc, n, widx, buf);
-        }
-    } else {
-        const uint32_t e = lut32[b];
-        put_bits(e & 0xffffffu, e >> 24, acc, n, widx, buf);
-    }
+// OR the l low bits of c (l <= 32) into the zeroed LDS word buffer at bit
+// position pos (MSB first); a code spans at most two words, and OR-ing the
+// (possibly zero) second word keeps the step branch-free.
+__device__ __forceinline__ void or_bits(uint32_t *buf, uint32_t pos, uint32_t c, uint32_t l) {
+    const uint32_t w = pos >> 5;
+    const uint64_t v = (uint64_t)c << (64u - (pos & 31u) - l);
+    atomicOr(&buf[w], (uint32_t)(v >> 32));
+    atomicOr(&buf[w + 1], (uint32_t)v);
 }
 
 // OR the codes of the first vb bytes of a piece into buf from bit `bitoff`.
-template <bool WIDE>
+// All LUT entries are read first: the buffer ORs that follow are LDS stores
+// the compiler cannot move table reads past.  Codes of up to 16 bits are
+// joined in pairs (at most 32 bits) before they are placed.
+template <bool WIDE, bool PAIRS>
 __device__ __forceinline__ void emit_piece(const uint4 &v, uint32_t vb, uint32_t bitoff, const uint32_t *lut32,
                                            const uint64_t *lut64, uint32_t *buf) {
-    uint32_t widx = bitoff >> 5, n = bitoff & 31;
-    uint64_t acc = 0;
-    if (vb == kPiece) {
+    uint32_t pos = bitoff;
+    if (!WIDE) {
+        uint32_t e[kPiece];
         static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
-            put_symbol<WIDE>(byte_k<decltype(kc)::value>(v), lut32, lut64, acc, n, widx, buf);
+            constexpr int k = decltype(kc)::value;
+            e[k] = (uint32_t)k < vb ? lut32[byte_k<k>(v)] : 0u;   // length 0: nothing to place
         });
+        if (PAIRS) {
+            static_for<0, kPiece / 2>([&](auto pc) __attribute__((always_inline)) {
+                constexpr int p = decltype(pc)::value;
+                const uint32_t l1 = e[2 * p] >> 24, l2 = e[2 * p + 1] >> 24;
+                const uint32_t c = ((e[2 * p] & 0xffffffu) << l2) | (e[2 * p + 1] & 0xffffffu);
+                const uint32_t l = l1 + l2;
+                if (l) or_bits(buf, pos, c, l);
+                pos += l;
+            });
+        } else {
+            static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                const uint32_t l = e[k] >> 24;
+                if (l) or_bits(buf, pos, e[k] & 0xffffffu, l);
+                pos += l;
+            });
+        }
     } else {
         static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            if ((uint32_t)k < vb) put_symbol<WIDE>(byte_k<k>(v), lut32, lut64, acc, n, widx, buf);
+            if ((uint32_t)k < vb) {
+                const uint64_t e = lut64[byte_k<k>(v)];
+                const uint32_t l = (uint32_t)(e >> 56);
+                const uint64_t c = e & ((1ull << 56) - 1);
+                if (l > 32) {
+                    or_bits(buf, pos, (uint32_t)(c >> 32), l - 32);
+                    or_bits(buf, pos + (l - 32), (uint32_t)c, 32);
+                } else {
+                    or_bits(buf, pos, (uint32_t)c, l);
+                }
+                pos += l;
+            }
         });
     }
-    if (n) atomicOr(&buf[widx], (uint32_t)(acc >> 32));
 }
 
 // Header fields, chunk_off[0] and the zero fill up to the payload (and the
@@ -145,7 +154,7 @@ __device__ __forceinline__ void write_stream_head(const EncodeArgs &a, uint32_t 
     for (uint32_t i = pad_from + tid; i < a.payload_offset; i += nthreads) out[i] = 0;
 }
 
-template <int ROWS, bool WIDE>
+template <int ROWS, bool WIDE, bool PAIRS>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
     extern __shared__ uint32_t rowbuf[];
     __shared__ uint64_t lut64[WIDE ? 256 : 1];
@@ -228,7 +237,84 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
     });
     const uint32_t chunk_bits = total;
 
-    // sub-chunk ends: the last piece of each 256-symbol sub-chunk
+    // 5. look-back for the chunk's byte offset (in 16-byte units): wave 0
+    //    reads the flags of 64 predecessors at a time, the nearest published
+    //    prefix ends the walk, the sizes in between are summed
+    if (wave == 0) {
+        const uint32_t units = (chunk_bits + 127) >> 7;
+        const uint64_t ep = (uint64_t)a.epoch << 32;
+        uint32_t acc = 0;
+        bool timed_out = false;
+        if (lc == 0) {
+            if (lane == 0) st_agent(&a.flags[chunk], kFlagPrefix | ep | units);
+        } else {
+            if (lane == 0) st_agent(&a.flags[chunk], kFlagAgg | ep | units);
+            const int64_t first = (int64_t)(chunk - lc);    // the segment's first chunk
+            int64_t top = (int64_t)chunk - 1;
+            uint32_t spins = 0;
+            for (;;) {
+                // predecessors top - (lane + 64 g), g = 0..kLookGroups-1, all requested at once
+                uint64_t f[kLookGroups];
+#pragma unroll
+                for (int g = 0; g < kLookGroups; ++g) {
+                    const int64_t k = top - (int64_t)lane - 64 * g;
+                    f[g] = k >= first ? ld_agent(&a.flags[k]) : (kFlagPrefix | ep);
+                }
+                bool retry = false, found = false;
+                uint32_t sum = 0, whole = 0;   // sum over complete groups / their count
+#pragma unroll
+                for (int g = 0; g < kLookGroups; ++g) {
+                    if (found || retry) break;
+                    const bool valid = ((f[g] >> 32) & 0x3fffffffu) == a.epoch;
+                    const uint64_t pref = __ballot(valid && (f[g] >> 62) == 2);
+                    const uint64_t inval = __ballot(!valid);
+                    const uint32_t stop = pref ? (uint32_t)__builtin_ctzll(pref) : 64u;
+                    const uint64_t need = stop >= 63 ? ~0ull : ((2ull << stop) - 1);
+                    if (inval & need) {
+                        retry = true;
+                        break;
+                    }
+                    uint32_t v = lane <= stop ? (uint32_t)f[g] : 0u;
+#pragma unroll
+                    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+                    sum += v;
+                    found = stop < 64;
+                    whole += found ? 0u : 1u;
+                }
+                // groups without a published prefix are consumed; the walk
+                // continues below them (or waits on the group that is not ready)
+                acc += sum;
+                top -= 64 * (int64_t)whole;
+                if (found) break;
+                if (retry) {
+                    // bounded wait: a chunk that never publishes is a bug, not a hang
+                    if (++spins > kMaxSpins) {
+                        timed_out = true;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (lane == 0 && !timed_out) st_agent(&a.flags[chunk], kFlagPrefix | ep | (uint64_t)(acc + units));
+        }
+        if (lane == 0) {
+            s_excl = acc;
+            uint64_t *chunk_off = reinterpret_cast<uint64_t *>(out + kHeaderBytes);
+            chunk_off[lc] = (uint64_t)acc * 16;
+            const uint64_t end = (uint64_t)a.payload_offset + ((uint64_t)acc + units) * 16;
+            s_skip = end > a.out_cap || timed_out;
+            if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
+            if (timed_out) or_status(a.status ? a.status + seg : nullptr, EC_S_INTERNAL);
+            if (lc == a.chunks_per_seg - 1) {
+                chunk_off[lc + 1] = ((uint64_t)acc + units) * 16;
+                reinterpret_cast<uint64_t *>(out)[4] = ((uint64_t)acc + units) * 16;   // payload_bytes
+                a.out_len[seg] = end;
+            }
+        }
+    }
+    if (lc == 0) write_stream_head(a, seg, tab, tid, kThreads);
+    // sub-chunk ends: the last piece of each 256-symbol sub-chunk (written
+    // after the look-back, whose flag loads would otherwise wait on them)
     const uint32_t spc = a.chunk_symbols / kSub;
     uint32_t *sub_end = reinterpret_cast<uint32_t *>(out + a.sub_at) + (uint64_t)lc * spc;
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
@@ -236,50 +322,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
         const uint32_t q = (uint32_t)r * kThreads + tid;
         if ((tid & 15) == 15 && q < a.chunk_symbols / kPiece) sub_end[q >> 4] = excl[r] + plen[r];
     });
-
-    // 5. look-back for the chunk's byte offset (in 16-byte units)
-    if (tid == 0) {
-        const uint32_t units = (chunk_bits + 127) >> 7;
-        const uint64_t ep = (uint64_t)a.epoch << 32;
-        uint32_t acc = 0;
-        bool timed_out = false;
-        if (lc == 0) {
-            st_agent(&a.flags[chunk], kFlagPrefix | ep | units);
-        } else {
-            st_agent(&a.flags[chunk], kFlagAgg | ep | units);
-            uint32_t k = chunk - 1;
-            uint32_t spins = 0;
-            for (;;) {
-                const uint64_t f = ld_agent(&a.flags[k]);
-                if (((f >> 32) & 0x3fffffffu) != a.epoch) {
-                    // bounded wait: a chunk that never publishes is a bug, not a hang
-                    if (++spins > kMaxSpins) {
-                        timed_out = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                acc += (uint32_t)f;
-                if ((f >> 62) == 2) break;
-                --k;
-            }
-            if (!timed_out) st_agent(&a.flags[chunk], kFlagPrefix | ep | (uint64_t)(acc + units));
-        }
-        s_excl = acc;
-        uint64_t *chunk_off = reinterpret_cast<uint64_t *>(out + kHeaderBytes);
-        chunk_off[lc] = (uint64_t)acc * 16;
-        const uint64_t end = (uint64_t)a.payload_offset + ((uint64_t)acc + units) * 16;
-        s_skip = end > a.out_cap || timed_out;
-        if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
-        if (timed_out) or_status(a.status ? a.status + seg : nullptr, EC_S_INTERNAL);
-        if (lc == a.chunks_per_seg - 1) {
-            chunk_off[lc + 1] = ((uint64_t)acc + units) * 16;
-            reinterpret_cast<uint64_t *>(out)[4] = ((uint64_t)acc + units) * 16;   // payload_bytes
-            a.out_len[seg] = end;
-        }
-    }
-    if (lc == 0) write_stream_head(a, seg, tab, tid, kThreads);
     __syncthreads();
     if (s_skip) return;
 
@@ -295,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
         const uint32_t nbuf = (last ? total_words : (re + 31) >> 5) - wbase;
         for (uint32_t i = tid; i < nbuf; i += kThreads) rowbuf[i] = i == 0 ? carry : 0u;
         __syncthreads();
-        if (plen[r]) emit_piece<WIDE>(v[r], vb[r], excl[r] - wbase * 32, lut32, lut64, rowbuf);
+        if (plen[r]) emit_piece<WIDE, PAIRS>(v[r], vb[r], excl[r] - wbase * 32, lut32, lut64, rowbuf);
         __syncthreads();
         const uint32_t nwrite = last ? nbuf : (re >> 5) - wbase;
         for (uint32_t i = tid; i < nwrite; i += kThreads) dst[wbase + i] = rowbuf[i];
@@ -312,11 +354,13 @@ __global__ void header_only_kernel(const EncodeArgs a) {
 }
 
 template <int ROWS>
-hipError_t launch_rows(const EncodeArgs &a, bool wide, uint32_t grid, uint32_t lds, hipStream_t s) {
-    if (wide)
-        hipLaunchKernelGGL((encode_kernel<ROWS, true>), dim3(grid), dim3(kThreads), lds, s, a);
+hipError_t launch_rows(const EncodeArgs &a, uint32_t max_len, uint32_t grid, uint32_t lds, hipStream_t s) {
+    if (max_len > (uint32_t)kNarrowMaxLen)
+        hipLaunchKernelGGL((encode_kernel<ROWS, true, false>), dim3(grid), dim3(kThreads), lds, s, a);
+    else if (max_len > 16)
+        hipLaunchKernelGGL((encode_kernel<ROWS, false, false>), dim3(grid), dim3(kThreads), lds, s, a);
     else
-        hipLaunchKernelGGL((encode_kernel<ROWS, false>), dim3(grid), dim3(kThreads), lds, s, a);
+        hipLaunchKernelGGL((encode_kernel<ROWS, false, true>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -324,15 +368,15 @@ hipError_t launch_rows(const EncodeArgs &a, bool wide, uint32_t grid, uint32_t l
 
 hipError_t launch_encode(const EncodeArgs &a, uint32_t /*codec*/, hipStream_t s) {
     const uint32_t grid = a.n_seg * a.chunks_per_seg;
-    const bool wide = a.max_len > (uint32_t)kNarrowMaxLen;
     const uint32_t rows = (a.chunk_symbols + kRowSyms - 1) / kRowSyms;
-    // row buffer: one row's bits plus the carried word and the final padding
+    // row buffer: one row's bits plus the carried word, the final padding and
+    // the spare word the two-word ORs may touch
     const uint32_t lds = (kRowSyms * a.max_len / 32 + 8) * 4;
-    if (rows <= 1) return launch_rows<1>(a, wide, grid, lds, s);
-    if (rows <= 2) return launch_rows<2>(a, wide, grid, lds, s);
-    if (rows <= 4) return launch_rows<4>(a, wide, grid, lds, s);
-    if (rows <= 8) return launch_rows<8>(a, wide, grid, lds, s);
-    return launch_rows<16>(a, wide, grid, lds, s);
+    if (rows <= 1) return launch_rows<1>(a, a.max_len, grid, lds, s);
+    if (rows <= 2) return launch_rows<2>(a, a.max_len, grid, lds, s);
+    if (rows <= 4) return launch_rows<4>(a, a.max_len, grid, lds, s);
+    if (rows <= 8) return launch_rows<8>(a, a.max_len, grid, lds, s);
+    return launch_rows<16>(a, a.max_len, grid, lds, s);
 }
 
 hipError_t launch_header_only(const EncodeArgs &a, hipStream_t s) {
