@@ -2,7 +2,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <atomic>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -15,15 +14,17 @@ namespace {
 constexpr uint64_t kMaxSegSymbols = 1ull << 33;   // per stream
 constexpr int kMaxDevices = 16;
 
-// Look-back scratch of one device: one 64-bit flag word per chunk of a
-// launch and the chunk ticket counter.  Grown by doubling; retired buffers
-// are kept (a kernel still in flight may use them) until the process ends.
+// Scratch of one device, one buffer per use (so that an encode and a
+// histogram in flight on different streams never share one): the encoder's
+// chunk sizes and the histogram's partial counts.  Grown by doubling;
+// retired buffers are kept (a kernel still in flight may use them) until the
+// process ends.
+enum ScratchSlot { kScratchSizes = 0, kScratchHist = 1, kScratchSlots = 2 };
+
 struct DeviceState {
     std::mutex mu;
-    uint64_t *flags = nullptr;
-    uint64_t capacity = 0;           // flag words
-    uint32_t *ticket = nullptr;
-    std::atomic<uint32_t> epoch{0};
+    void *buf[kScratchSlots] = {};
+    uint64_t bytes[kScratchSlots] = {};
     std::vector<void *> retired;
 };
 
@@ -35,36 +36,23 @@ int current_device(int *dev) {
     return EC_OK;
 }
 
-// Flag words for `chunks` chunks and the epoch tagging this launch.
-int lookback_scratch(uint64_t chunks, hipStream_t s, uint64_t **flags, uint32_t **ticket, uint32_t *epoch) {
+// At least `bytes` of scratch `slot` on the current device.
+int device_scratch(int slot, uint64_t bytes, void **out) {
     int dev;
     int rc = current_device(&dev);
     if (rc) return rc;
     DeviceState &d = g_dev[dev];
     std::lock_guard<std::mutex> lock(d.mu);
-    if (!d.ticket) {
-        if (hipMalloc(&d.ticket, 256) != hipSuccess) return EC_E_NOMEM;
-        if (hipMemset(d.ticket, 0, 256) != hipSuccess) return EC_E_HIP;
+    if (bytes > d.bytes[slot]) {
+        uint64_t cap = d.bytes[slot] ? d.bytes[slot] : (1u << 18);
+        while (cap < bytes) cap *= 2;
+        void *p = nullptr;
+        if (hipMalloc(&p, cap) != hipSuccess) return EC_E_NOMEM;
+        if (d.buf[slot]) d.retired.push_back(d.buf[slot]);
+        d.buf[slot] = p;
+        d.bytes[slot] = cap;
     }
-    if (chunks > d.capacity) {
-        uint64_t cap = d.capacity ? d.capacity : 65536;
-        while (cap < chunks) cap *= 2;
-        uint64_t *p = nullptr;
-        if (hipMalloc(&p, cap * 8) != hipSuccess) return EC_E_NOMEM;
-        if (hipMemset(p, 0, cap * 8) != hipSuccess) return EC_E_HIP;   // epoch 0 is never current
-        if (d.flags) d.retired.push_back(d.flags);
-        d.flags = p;
-        d.capacity = cap;
-    }
-    uint32_t e = (d.epoch.fetch_add(1) + 1) & 0x3fffffffu;
-    if (e == 0) {
-        // the 30-bit tag wrapped: clear the words so old tags cannot match
-        if (launch_fill_u64(d.flags, d.capacity, 0, s) != hipSuccess) return EC_E_HIP;
-        e = (d.epoch.fetch_add(1) + 1) & 0x3fffffffu;
-    }
-    *flags = d.flags;
-    *ticket = d.ticket;
-    *epoch = e;
+    *out = d.buf[slot];
     return EC_OK;
 }
 
@@ -150,10 +138,13 @@ int encode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_
     a.sub_at = (uint32_t)L.sub_at;
     a.embed_lengths = embed ? 1 : 0;
     a.max_len = max_len;
-    if (L.n_chunks == 0) return hip_rc(launch_header_only(a, s));
-    int rc = lookback_scratch(L.n_chunks * n_seg, s, &a.flags, &a.ticket, &a.epoch);
-    if (rc) return rc;
-    return hip_rc(launch_encode(a, cbs[0]->host.codec, s));
+    if (L.n_chunks) {
+        void *p = nullptr;
+        int rc = device_scratch(kScratchSizes, L.n_chunks * n_seg * 4, &p);
+        if (rc) return rc;
+        a.sizes = static_cast<uint32_t *>(p);
+    }
+    return hip_rc(launch_encode(a, s));
 }
 
 int decode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t in_stride,
@@ -250,7 +241,7 @@ int ec_codebook_info(const ec_codebook *cb, uint32_t *codec, uint32_t *max_len, 
     if (codebook_id) *codebook_id = t.codebook_id;
     if (code_len) memcpy(code_len, t.code_len, 256);
     if (code)
-        for (int s = 0; s < 256; ++s) code[s] = t.enc64[s] & ((1ull << 56) - 1);
+        for (int s = 0; s < 256; ++s) code[s] = t.code_len[s] ? t.enc64[s] >> (64 - t.code_len[s]) : 0;
     if (rank_to_sym) {
         if (t.codec == EC_CODEC_HUFFMAN)
             memset(rank_to_sym, 0, 256);
@@ -315,7 +306,10 @@ int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t
     if (!d_counts || n_seg == 0 || n_seg > 65535 || (seg_n && !d_in)) return EC_E_INVAL;
     if (n_seg > 1 && in_stride < seg_n) return EC_E_INVAL;
     if (seg_n >= (1ull << 40)) return EC_E_UNSUPPORTED;
-    return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, stream));
+    void *partial = nullptr;
+    int rc = device_scratch(kScratchHist, (uint64_t)histogram_blocks(seg_n, n_seg) * n_seg * 1024, &partial);
+    if (rc) return rc;
+    return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, static_cast<uint32_t *>(partial), stream));
 }
 
 int pmf_average(const uint64_t *d_counts, uint32_t n_seg, float *d_pmf, hipStream_t stream) {

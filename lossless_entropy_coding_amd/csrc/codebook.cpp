@@ -47,13 +47,14 @@ ec_codebook *new_codebook(uint32_t codec) {
 void fill_encode_luts(DevTables &t, const uint64_t code[256], const uint8_t len[256]) {
     uint32_t mx = 0;
     for (int s = 0; s < 256; ++s) {
-        t.enc64[s] = ((uint64_t)len[s] << 56) | code[s];
+        // code left-aligned (first code bit at bit 63 / 31), length in the low byte
+        t.enc64[s] = (code[s] << (64 - len[s])) | len[s];
         t.code_len[s] = len[s];
         mx = std::max<uint32_t>(mx, len[s]);
     }
     t.max_len = mx;
     for (int s = 0; s < 256; ++s)
-        t.enc32[s] = mx <= (uint32_t)kNarrowMaxLen ? ((uint32_t)len[s] << 24) | (uint32_t)code[s] : 0u;
+        t.enc32[s] = mx <= (uint32_t)kNarrowMaxLen ? ((uint32_t)code[s] << (32 - len[s])) | len[s] : 0u;
 }
 
 }  // namespace

@@ -31,20 +31,8 @@ __device__ __forceinline__ const DevTables *seg_tables(uint32_t seg) {
     return p->tabs[seg];
 }
 
-// Relaxed atomics at device (agent) scope: visible across the eight XCDs'
-// separate L2 caches without whole-cache writebacks.
-__device__ __forceinline__ uint64_t ld_agent(const uint64_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t add_agent(uint32_t *p, uint32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent32(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Status bits are OR-ed at device (agent) scope: visible across the eight
+// XCDs' separate L2 caches.
 __device__ __forceinline__ void or_status(uint32_t *status, uint32_t bits) {
     if (status) __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -60,9 +48,7 @@ struct EncodeArgs {
     uint64_t out_cap;
     uint64_t *out_len;        // [n_seg]
     uint32_t *status;         // [n_seg] or null
-    uint64_t *flags;          // look-back words, one per chunk of the launch
-    uint32_t *ticket;         // chunk ticket counter (zero between launches)
-    uint32_t epoch;           // tag of this launch's look-back words
+    uint32_t *sizes;          // chunk sizes in 16-byte units, one per chunk of the launch
     uint32_t chunk_symbols;
     uint32_t chunks_per_seg;
     uint32_t n_seg;
@@ -86,14 +72,14 @@ struct DecodeArgs {
     const DevTables *tabs[EC_MAX_BATCH];
 };
 
-hipError_t launch_encode(const EncodeArgs &a, uint32_t codec, hipStream_t s);
-hipError_t launch_header_only(const EncodeArgs &a, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t max_len, hipStream_t s);
+// Partial-count rows per segment of a histogram launch (uint32 x 256 each).
+uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg);
 hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
-                            uint64_t *counts, hipStream_t s);
+                            uint64_t *counts, uint32_t *partial, hipStream_t s);
 hipError_t launch_pmf_average(const uint64_t *counts, uint32_t n_seg, float *pmf, hipStream_t s);
 hipError_t launch_pmf_kl(const uint64_t *p, uint32_t n_seg, const uint64_t *q, uint32_t q_add,
                          float *kl, hipStream_t s);
-hipError_t launch_fill_u64(uint64_t *p, uint64_t n, uint64_t v, hipStream_t s);
 
 }  // namespace ec

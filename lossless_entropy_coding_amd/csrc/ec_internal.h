@@ -33,8 +33,8 @@ constexpr uint16_t kL1Long = 0x8000;
 
 // Everything a kernel needs about one codebook, uploaded as one blob.
 struct alignas(16) DevTables {
-    uint64_t enc64[256];      // (len << 56) | code, any length <= 40
-    uint32_t enc32[256];      // (len << 24) | code, when max_len <= 24
+    uint64_t enc64[256];      // code << (64 - len) | len: left-aligned code, any length <= 40
+    uint32_t enc32[256];      // code << (32 - len) | len, when max_len <= 24
     uint16_t l1[kL1Size];     // decode level 1
     uint16_t l2[kL2Size];     // decode level 2 (Huffman)
     uint64_t limit[48];       // Huffman: 40-bit left-justified end of codes of length l

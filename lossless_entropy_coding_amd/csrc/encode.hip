@@ -1,22 +1,23 @@
-// Chunked fixed-codebook encoder.
+// Chunked fixed-codebook encoder: three launches on the caller's stream.
 //
-// One workgroup (256 threads, four wave64s) codes one chunk of C symbols in a
-// single pass over HBM:
-//   1. take a ticket (chunks are handed out in launch order, so every chunk
-//      a workgroup waits for below is already running);
-//   2. load the chunk as 16-byte pieces, piece q = r * 256 + thread, so each
-//      load instruction of a wave reads 1 KiB of contiguous bytes;
-//   3. sum each piece's code lengths from the codebook's LUT held in LDS;
-//   4. exclusive scan of piece lengths (wave scan + LDS across the four
-//      waves) gives every piece's bit offset in the chunk and the end bit of
-//      each 256-symbol sub-chunk, which goes straight into the stream index;
-//   5. decoupled look-back over earlier chunks' published sizes (agent-scope
-//      relaxed atomics, tagged with a per-launch epoch so the flag words
-//      never need clearing) gives the chunk's byte offset in the payload;
-//   6. for each row of 4096 symbols the pieces OR their codes into an LDS
-//      word buffer (64-bit accumulator per thread, MSB first), and the
-//      workgroup stores the finished words with coalesced 32-bit stores;
-//      the partial last word is carried to the next row.
+//   1. encode_sizes_kernel (one workgroup of 256 threads per chunk): loads
+//      the chunk as 16-byte pieces (piece q = r * 256 + thread, so each load
+//      instruction of a wave reads 1 KiB of contiguous bytes), sums each
+//      piece's code lengths from a byte table in LDS, scans the piece lengths
+//      over the workgroup and writes the chunk's sub_end[] entries (end bit
+//      of every 256-symbol sub-chunk) and its size in 16-byte units.
+//   2. encode_offsets_kernel (one workgroup per stream): exclusive scan of
+//      the stream's chunk sizes -> chunk_off[], payload_bytes and the stream
+//      length; writes the header, the embedded code lengths and the zero
+//      padding in front of the payload; flags a stream that does not fit.
+//   3. encode_pack_*_kernel (one workgroup per chunk): loads the chunk again,
+//      looks each symbol's code up in the codebook's LUT in LDS (code
+//      left-aligned, length in the low byte), scans the piece lengths, ORs the
+//      codes into a zeroed LDS bit buffer (MSB first) and stores the finished
+//      chunk at its offset with coalesced stores.
+// Every chunk knows its place before it is packed, so no workgroup ever
+// waits on another one: the launches need no co-residency, tickets or
+// spinning, at the price of reading the input twice.
 #include "dev_common.h"
 
 namespace ec {
@@ -26,10 +27,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPiece = 16;                     // symbols per piece (one 16-byte load)
 constexpr int kRowSyms = kThreads * kPiece;    // 4096
-constexpr uint64_t kFlagAgg = 1ull << 62;      // chunk size published, prefix not yet known
-constexpr uint64_t kFlagPrefix = 2ull << 62;   // inclusive prefix published
-constexpr uint32_t kMaxSpins = 1u << 22;       // look-back wait bound (about 0.1-1 s)
-constexpr int kLookGroups = 4;                 // look-back reads 4 x 64 predecessors per pass
 
 // Byte K (compile-time) of a 16-byte piece, in memory order.
 template <int K>
@@ -39,176 +36,60 @@ __device__ __forceinline__ uint32_t byte_k(const uint4 &v) {
     return (x >> sh) & 0xffu;
 }
 
-// Code length of byte b.
-template <bool WIDE>
-__device__ __forceinline__ uint32_t code_len(const uint32_t *lut32, const uint64_t *lut64, uint32_t b) {
-    if (WIDE) return (uint32_t)(lut64[b] >> 56);
-    return lut32[b] >> 24;
-}
+// Where chunk t of the launch lives.
+struct ChunkPos {
+    uint32_t seg, lc, cn;
+    const uint8_t *src;
+    uint8_t *out;
+};
 
-// Sum of the code lengths of the first vb bytes of a piece.
-template <bool WIDE>
-__device__ __forceinline__ uint32_t piece_len(const uint4 &v, uint32_t vb, const uint32_t *lut32,
-                                              const uint64_t *lut64) {
-    uint32_t x = 0;
-    if (vb == kPiece) {
-        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) { x += code_len<WIDE>(lut32, lut64, byte_k<decltype(kc)::value>(v)); });
-    } else {
-        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            if ((uint32_t)k < vb) x += code_len<WIDE>(lut32, lut64, byte_k<k>(v));
-        });
-    }
-    return x;
-}
-
-// OR the l low bits of c (l <= 32) into the zeroed LDS word buffer at bit
-// position pos (MSB first); a code spans at most two words, and OR-ing the
-// (possibly zero) second word keeps the step branch-free.
-__device__ __forceinline__ void or_bits(uint32_t *buf, uint32_t pos, uint32_t c, uint32_t l) {
-    const uint32_t w = pos >> 5;
-    const uint64_t v = (uint64_t)c << (64u - (pos & 31u) - l);
-    atomicOr(&buf[w], (uint32_t)(v >> 32));
-    atomicOr(&buf[w + 1], (uint32_t)v);
-}
-
-// OR the codes of the first vb bytes of a piece into buf from bit `bitoff`.
-// All LUT entries are read first: the buffer ORs that follow are LDS stores
-// the compiler cannot move table reads past.  Codes of up to 16 bits are
-// joined in pairs (at most 32 bits) before they are placed.
-template <bool WIDE, bool PAIRS>
-__device__ __forceinline__ void emit_piece(const uint4 &v, uint32_t vb, uint32_t bitoff, const uint32_t *lut32,
-                                           const uint64_t *lut64, uint32_t *buf) {
-    uint32_t pos = bitoff;
-    if (!WIDE) {
-        uint32_t e[kPiece];
-        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            e[k] = (uint32_t)k < vb ? lut32[byte_k<k>(v)] : 0u;   // length 0: nothing to place
-        });
-        if (PAIRS) {
-            static_for<0, kPiece / 2>([&](auto pc) __attribute__((always_inline)) {
-                constexpr int p = decltype(pc)::value;
-                const uint32_t l1 = e[2 * p] >> 24, l2 = e[2 * p + 1] >> 24;
-                const uint32_t c = ((e[2 * p] & 0xffffffu) << l2) | (e[2 * p + 1] & 0xffffffu);
-                const uint32_t l = l1 + l2;
-                if (l) or_bits(buf, pos, c, l);
-                pos += l;
-            });
-        } else {
-            static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
-                constexpr int k = decltype(kc)::value;
-                const uint32_t l = e[k] >> 24;
-                if (l) or_bits(buf, pos, e[k] & 0xffffffu, l);
-                pos += l;
-            });
-        }
-    } else {
-        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            if ((uint32_t)k < vb) {
-                const uint64_t e = lut64[byte_k<k>(v)];
-                const uint32_t l = (uint32_t)(e >> 56);
-                const uint64_t c = e & ((1ull << 56) - 1);
-                if (l > 32) {
-                    or_bits(buf, pos, (uint32_t)(c >> 32), l - 32);
-                    or_bits(buf, pos + (l - 32), (uint32_t)c, 32);
-                } else {
-                    or_bits(buf, pos, (uint32_t)c, l);
-                }
-                pos += l;
-            }
-        });
-    }
-}
-
-// Header fields, chunk_off[0] and the zero fill up to the payload (and the
-// embedded code lengths): written once per stream by the thread block that
-// owns the stream's first chunk (or by the header-only kernel when n = 0).
-__device__ __forceinline__ void write_stream_head(const EncodeArgs &a, uint32_t seg, const DevTables *tab, uint32_t tid,
-                                  uint32_t nthreads) {
-    uint8_t *out = a.out + (uint64_t)seg * a.out_stride;
-    const uint32_t spc = a.chunk_symbols / kSub;
-    const uint32_t index_end = a.sub_at + 4u * a.chunks_per_seg * spc;
-    if (tid == 0) {
-        uint64_t *h = reinterpret_cast<uint64_t *>(out);
-        h[0] = (uint64_t)kMagic | ((uint64_t)kVersion << 32) | ((uint64_t)tab->codec << 48) |
-               ((uint64_t)(a.embed_lengths ? 1 : 0) << 56);
-        h[1] = a.seg_n;
-        h[2] = (uint64_t)a.chunk_symbols | ((uint64_t)a.chunks_per_seg << 32);
-        h[3] = a.payload_offset;
-        h[5] = tab->codebook_id;
-        h[6] = 0;
-        h[7] = 0;
-        if (a.chunks_per_seg == 0) {
-            h[4] = 0;          // payload_bytes
-            h[8] = 0;          // chunk_off[0]
-            a.out_len[seg] = a.payload_offset;
-        }
-    }
-    uint32_t pad_from = index_end;
-    if (a.embed_lengths) {
-        for (uint32_t i = tid; i < 256; i += nthreads) out[index_end + i] = tab->code_len[i];
-        pad_from += 256;
-    }
-    for (uint32_t i = pad_from + tid; i < a.payload_offset; i += nthreads) out[i] = 0;
-}
-
-template <int ROWS, bool WIDE, bool PAIRS>
-__global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
-    extern __shared__ uint32_t rowbuf[];
-    __shared__ uint64_t lut64[WIDE ? 256 : 1];
-    __shared__ uint32_t lut32[WIDE ? 1 : 256];
-    __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
-    __shared__ uint32_t s_chunk, s_excl, s_skip;
-
-    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) {
-        const uint32_t t = add_agent(a.ticket, 1u);
-        if (t == gridDim.x - 1) st_agent32(a.ticket, 0u);   // every ticket is taken: reset for the next launch
-        s_chunk = t;
-    }
-    __syncthreads();
-    const uint32_t chunk = s_chunk;
-    const uint32_t seg = chunk / a.chunks_per_seg;
-    const uint32_t lc = chunk - seg * a.chunks_per_seg;
-    const DevTables *tab = seg_tables<EncodeArgs>(seg);
-    if (WIDE)
-        lut64[tid] = tab->enc64[tid];
-    else
-        lut32[tid] = tab->enc32[tid];
-
-    const uint64_t first = (uint64_t)lc * a.chunk_symbols;
+__device__ __forceinline__ ChunkPos chunk_pos(const EncodeArgs &a, uint32_t t) {
+    ChunkPos p;
+    p.seg = t / a.chunks_per_seg;
+    p.lc = t - p.seg * a.chunks_per_seg;
+    const uint64_t first = (uint64_t)p.lc * a.chunk_symbols;
     const uint64_t left = a.seg_n - first;
-    const uint32_t cn = left < a.chunk_symbols ? (uint32_t)left : a.chunk_symbols;
-    const uint8_t *src = a.in + (uint64_t)seg * a.in_stride + first;
-    uint8_t *out = a.out + (uint64_t)seg * a.out_stride;
+    p.cn = left < a.chunk_symbols ? (uint32_t)left : a.chunk_symbols;
+    p.src = a.in + (uint64_t)p.seg * a.in_stride + first;
+    p.out = a.out + (uint64_t)p.seg * a.out_stride;
+    return p;
+}
 
-    // 2. load pieces
-    uint4 v[ROWS];
-    uint32_t vb[ROWS];
+// Load the chunk's pieces: piece q = r * 256 + tid, vb[r] valid bytes.  A
+// piece holding the segment's last byte is read as its whole 16-byte block
+// (the input is 16-byte aligned, so the block never crosses a page); bytes
+// past the end are ignored through vb.  Pieces past the end read nothing.
+template <int ROWS>
+__device__ __forceinline__ void load_pieces(const uint8_t *src, uint32_t cn, uint32_t tid, uint4 (&v)[ROWS],
+                                            uint32_t (&vb)[ROWS]) {
+    if (cn == (uint32_t)(ROWS * kRowSyms)) {   // whole chunk present: plain loads
+        static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            vb[r] = kPiece;
+            v[r] = *reinterpret_cast<const uint4 *>(src + (uint32_t)(r * kThreads + tid) * kPiece);
+        });
+        return;
+    }
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         const uint32_t off = (uint32_t)(r * kThreads + tid) * kPiece;
         vb[r] = off < cn ? min(cn - off, (uint32_t)kPiece) : 0u;
-        if (vb[r] == kPiece) {
-            v[r] = *reinterpret_cast<const uint4 *>(src + off);
-        } else {
-            uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int k = 0; k < kPiece; ++k)
-                if ((uint32_t)k < vb[r]) w[k >> 2] |= (uint32_t)src[off + k] << (8 * (k & 3));
-            v[r] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        v[r] = make_uint4(0, 0, 0, 0);
+        if (off < cn) v[r] = *reinterpret_cast<const uint4 *>(src + off);
     });
-    __syncthreads();   // LUT in LDS
+}
 
-    // 3. piece lengths, 4. wave-inclusive scan per row
-    uint32_t plen[ROWS], incl[ROWS];
+// Scan of piece lengths over the workgroup: per row a wave-inclusive scan,
+// then the four waves' totals through LDS.  Gives every piece's exclusive
+// bit offset in the chunk, the rows' starts and lengths, and the chunk total.
+template <int ROWS>
+__device__ __forceinline__ uint32_t scan_pieces(const uint32_t (&plen)[ROWS], uint32_t lane, uint32_t wave,
+                                                uint32_t (*wave_tot)[kThreads / 64], uint32_t (&excl)[ROWS],
+                                                uint32_t (&row_start)[ROWS], uint32_t (&row_bits)[ROWS]) {
+    uint32_t incl[ROWS];
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        uint32_t x = piece_len<WIDE>(v[r], vb[r], lut32, lut64);
-        plen[r] = x;
+        uint32_t x = plen[r];
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const uint32_t y = __shfl_up(x, d, 64);
@@ -218,8 +99,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
         if (lane == 63) wave_tot[r][wave] = x;
     });
     __syncthreads();
-    // combine the four waves: piece offsets, row starts, chunk total
-    uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
     uint32_t total = 0;
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
@@ -235,99 +114,349 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
         excl[r] = total + before + incl[r] - plen[r];
         total += rt;
     });
-    const uint32_t chunk_bits = total;
+    return total;
+}
 
-    // 5. look-back for the chunk's byte offset (in 16-byte units): wave 0
-    //    reads the flags of 64 predecessors at a time, the nearest published
-    //    prefix ends the walk, the sizes in between are summed
-    if (wave == 0) {
-        const uint32_t units = (chunk_bits + 127) >> 7;
-        const uint64_t ep = (uint64_t)a.epoch << 32;
-        uint32_t acc = 0;
-        bool timed_out = false;
-        if (lc == 0) {
-            if (lane == 0) st_agent(&a.flags[chunk], kFlagPrefix | ep | units);
+// ---------------------------------------------------------------- 1. sizes
+
+template <int ROWS>
+__global__ __launch_bounds__(kThreads) void encode_sizes_kernel(const EncodeArgs a) {
+    __shared__ uint8_t len8[256];
+    __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const ChunkPos p = chunk_pos(a, blockIdx.x);
+    uint4 v[ROWS];
+    uint32_t vb[ROWS];
+    load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
+    len8[tid] = seg_tables<EncodeArgs>(p.seg)->code_len[tid];
+    __syncthreads();
+
+    uint32_t plen[ROWS];
+    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        uint32_t x = 0;
+        if (vb[r] == kPiece) {
+            static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
+                x += len8[byte_k<decltype(kc)::value>(v[r])];
+            });
         } else {
-            if (lane == 0) st_agent(&a.flags[chunk], kFlagAgg | ep | units);
-            const int64_t first = (int64_t)(chunk - lc);    // the segment's first chunk
-            int64_t top = (int64_t)chunk - 1;
-            uint32_t spins = 0;
-            for (;;) {
-                // predecessors top - (lane + 64 g), g = 0..kLookGroups-1, all requested at once
-                uint64_t f[kLookGroups];
-#pragma unroll
-                for (int g = 0; g < kLookGroups; ++g) {
-                    const int64_t k = top - (int64_t)lane - 64 * g;
-                    f[g] = k >= first ? ld_agent(&a.flags[k]) : (kFlagPrefix | ep);
-                }
-                bool retry = false, found = false;
-                uint32_t sum = 0, whole = 0;   // sum over complete groups / their count
-#pragma unroll
-                for (int g = 0; g < kLookGroups; ++g) {
-                    if (found || retry) break;
-                    const bool valid = ((f[g] >> 32) & 0x3fffffffu) == a.epoch;
-                    const uint64_t pref = __ballot(valid && (f[g] >> 62) == 2);
-                    const uint64_t inval = __ballot(!valid);
-                    const uint32_t stop = pref ? (uint32_t)__builtin_ctzll(pref) : 64u;
-                    const uint64_t need = stop >= 63 ? ~0ull : ((2ull << stop) - 1);
-                    if (inval & need) {
-                        retry = true;
-                        break;
-                    }
-                    uint32_t v = lane <= stop ? (uint32_t)f[g] : 0u;
-#pragma unroll
-                    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-                    sum += v;
-                    found = stop < 64;
-                    whole += found ? 0u : 1u;
-                }
-                // groups without a published prefix are consumed; the walk
-                // continues below them (or waits on the group that is not ready)
-                acc += sum;
-                top -= 64 * (int64_t)whole;
-                if (found) break;
-                if (retry) {
-                    // bounded wait: a chunk that never publishes is a bug, not a hang
-                    if (++spins > kMaxSpins) {
-                        timed_out = true;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            if (lane == 0 && !timed_out) st_agent(&a.flags[chunk], kFlagPrefix | ep | (uint64_t)(acc + units));
+            static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                x += (uint32_t)k < vb[r] ? (uint32_t)len8[byte_k<k>(v[r])] : 0u;
+            });
         }
-        if (lane == 0) {
-            s_excl = acc;
-            uint64_t *chunk_off = reinterpret_cast<uint64_t *>(out + kHeaderBytes);
-            chunk_off[lc] = (uint64_t)acc * 16;
-            const uint64_t end = (uint64_t)a.payload_offset + ((uint64_t)acc + units) * 16;
-            s_skip = end > a.out_cap || timed_out;
-            if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
-            if (timed_out) or_status(a.status ? a.status + seg : nullptr, EC_S_INTERNAL);
-            if (lc == a.chunks_per_seg - 1) {
-                chunk_off[lc + 1] = ((uint64_t)acc + units) * 16;
-                reinterpret_cast<uint64_t *>(out)[4] = ((uint64_t)acc + units) * 16;   // payload_bytes
-                a.out_len[seg] = end;
-            }
-        }
-    }
-    if (lc == 0) write_stream_head(a, seg, tab, tid, kThreads);
-    // sub-chunk ends: the last piece of each 256-symbol sub-chunk (written
-    // after the look-back, whose flag loads would otherwise wait on them)
+        plen[r] = x;
+    });
+    uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
+    const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
+    // sub_end[]: written by the thread holding a sub-chunk's last piece
     const uint32_t spc = a.chunk_symbols / kSub;
-    uint32_t *sub_end = reinterpret_cast<uint32_t *>(out + a.sub_at) + (uint64_t)lc * spc;
+    uint32_t *sub_end = reinterpret_cast<uint32_t *>(p.out + a.sub_at) + (uint64_t)p.lc * spc;
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
         const uint32_t q = (uint32_t)r * kThreads + tid;
         if ((tid & 15) == 15 && q < a.chunk_symbols / kPiece) sub_end[q >> 4] = excl[r] + plen[r];
     });
-    __syncthreads();
-    if (s_skip) return;
+    if (tid == 0) a.sizes[blockIdx.x] = (chunk_bits + 127) >> 7;
+}
 
-    // 6. pack rows into LDS and store finished words
-    uint32_t *dst = reinterpret_cast<uint32_t *>(out + a.payload_offset + (uint64_t)s_excl * 16);
-    const uint32_t total_words = ((chunk_bits + 127) >> 7) * 4;
+// -------------------------------------------------------------- 2. offsets
+
+constexpr int kScanThreads = 1024;
+
+// Header fields, chunk_off[], payload_bytes, the stream length, the embedded
+// code lengths and the zero fill up to the payload of stream `blockIdx.x`.
+__global__ __launch_bounds__(kScanThreads) void encode_offsets_kernel(const EncodeArgs a) {
+    __shared__ uint64_t wsum[kScanThreads / 64];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t seg = blockIdx.x;
+    const DevTables *tab = seg_tables<EncodeArgs>(seg);
+    uint8_t *out = a.out + (uint64_t)seg * a.out_stride;
+    const uint32_t n = a.chunks_per_seg;
+    const uint32_t *sz = a.sizes + (uint64_t)seg * n;
+    uint64_t *chunk_off = reinterpret_cast<uint64_t *>(out + kHeaderBytes);
+
+    // each thread owns a run of consecutive chunks
+    const uint32_t per = (n + kScanThreads - 1) / kScanThreads;
+    const uint32_t lo = min(n, tid * per), hi = min(n, lo + per);
+    uint64_t mine = 0;
+    for (uint32_t i = lo; i < hi; ++i) mine += sz[i];
+    uint64_t x = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t y = __shfl_up(x, d, 64);
+        if (lane >= (uint32_t)d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint64_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+        before += (uint32_t)w < wave ? wsum[w] : 0;
+        total += wsum[w];
+    }
+    uint64_t run = before + x - mine;   // units before chunk lo
+    for (uint32_t i = lo; i < hi; ++i) {
+        chunk_off[i] = run * 16;
+        run += sz[i];
+    }
+    const uint64_t payload = total * 16;
+    const uint64_t end = (uint64_t)a.payload_offset + payload;
+    if (tid == 0) {
+        chunk_off[n] = payload;
+        uint64_t *h = reinterpret_cast<uint64_t *>(out);
+        h[0] = (uint64_t)kMagic | ((uint64_t)kVersion << 32) | ((uint64_t)tab->codec << 48) |
+               ((uint64_t)(a.embed_lengths ? 1 : 0) << 56);
+        h[1] = a.seg_n;
+        h[2] = (uint64_t)a.chunk_symbols | ((uint64_t)n << 32);
+        h[3] = a.payload_offset;
+        h[4] = payload;
+        h[5] = tab->codebook_id;
+        h[6] = 0;
+        h[7] = 0;
+        a.out_len[seg] = end;
+        if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
+    }
+    const uint32_t index_end = a.sub_at + 4u * n * (a.chunk_symbols / kSub);
+    uint32_t pad_from = index_end;
+    if (a.embed_lengths) {
+        for (uint32_t i = tid; i < 256; i += kScanThreads) out[index_end + i] = tab->code_len[i];
+        pad_from += 256;
+    }
+    for (uint32_t i = pad_from + tid; i < a.payload_offset; i += kScanThreads) out[i] = 0;
+}
+
+// ----------------------------------------------------------------- 3. pack
+
+typedef __attribute__((address_space(3))) uint32_t lds_word;
+
+// LDS byte address of a shared-memory pointer.
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(T *p) {
+    return (uint32_t)(size_t)(lds_word *)p;
+}
+
+// OR a left-aligned code of up to 32 bits (c, zero below its last bit) into
+// a zeroed LDS bit buffer (MSB first).  The position is an absolute LDS bit
+// address (the buffer's byte address times 8 plus the bit position in the
+// buffer): the word address is then a shift and a mask, with no base to add.
+// The code spans at most two words; OR-ing the (possibly zero) second word
+// keeps the step branch-free.  The hardware shifts take the position modulo 32.
+__device__ __forceinline__ void or_code32_at(uint32_t abs_bit, uint32_t c) {
+    lds_word *p = (lds_word *)(size_t)((abs_bit >> 3) & ~3u);
+    __hip_atomic_fetch_or(p, c >> (abs_bit & 31u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(p + 1, __builtin_amdgcn_alignbit(c, 0u, abs_bit), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Same for a left-aligned code of up to 64 bits held as hi:lo (three words),
+// at a bit position relative to buf.
+__device__ __forceinline__ void or_code64(uint32_t *buf, uint32_t pos, uint32_t hi, uint32_t lo) {
+    const uint32_t w = pos >> 5;
+    atomicOr(&buf[w], hi >> (pos & 31u));
+    atomicOr(&buf[w + 1], __builtin_amdgcn_alignbit(hi, lo, pos));
+    atomicOr(&buf[w + 2], __builtin_amdgcn_alignbit(lo, 0u, pos));
+}
+
+// Byte offset of the chunk's payload in its stream, or ~0 when the chunk
+// must not be written (the stream does not fit in out_cap).
+__device__ __forceinline__ uint64_t chunk_dst(const EncodeArgs &a, const ChunkPos &p, uint32_t units) {
+    const uint64_t off = reinterpret_cast<const uint64_t *>(p.out + kHeaderBytes)[p.lc];
+    const uint64_t end = (uint64_t)a.payload_offset + off + (uint64_t)units * 16;
+    return end > a.out_cap ? ~0ull : (uint64_t)a.payload_offset + off;
+}
+
+// Staged packing, for chunks of up to 4 rows (16384 symbols) whose packed
+// bits fit in LDS: every LUT entry is read once and kept in registers as a
+// left-aligned code (pairs joined when codes are at most 16 bits) with its
+// length byte packed four to a register.
+
+enum { kModePairs = 0, kModeSingles = 1 };
+
+template <int ROWS, int MODE>
+struct CodeCache {
+    static constexpr int kUnits = MODE == kModePairs ? kPiece / 2 : kPiece;   // codes placed per piece
+    uint32_t c[ROWS][kUnits];          // left-aligned codes
+    uint32_t pk[ROWS][kUnits / 4];     // code lengths, one byte each
+};
+
+// Pass 1 over row r: cache codes and lengths; returns the piece's bit length.
+// All 16 bytes are looked up; bytes past the end of a piece are cleared
+// afterwards by clear_tail.
+template <int MODE, class Cache>
+__device__ __forceinline__ uint32_t cache_row(Cache &cc, int r, const uint4 &v, const uint32_t *lut32,
+                                              const uint64_t *lut64) {
+    constexpr int U = Cache::kUnits;
+    uint32_t pk[U / 4];
+#pragma unroll
+    for (int i = 0; i < U / 4; ++i) pk[i] = 0;
+    if (MODE == kModePairs) {
+        static_for<0, U>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int p = decltype(pc)::value;
+            const uint32_t e1 = lut32[byte_k<2 * p>(v)], e2 = lut32[byte_k<2 * p + 1>(v)];
+            // first code's length is at most 16: e1 & 31 is it exactly
+            cc.c[r][p] = (e1 & ~0xffu) | ((e2 & ~0xffu) >> (e1 & 31u));
+            pk[p >> 2] |= ((e1 + e2) & 0xffu) << (8 * (p & 3));
+        });
+    } else {
+        static_for<0, U>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            const uint64_t e = lut64[byte_k<k>(v)];
+            cc.c[r][k] = (uint32_t)(e >> 32);
+            pk[k >> 2] |= ((uint32_t)e & 0xffu) << (8 * (k & 3));
+        });
+    }
+    uint32_t len = 0;
+#pragma unroll
+    for (int i = 0; i < U / 4; ++i) {
+        cc.pk[r][i] = pk[i];
+        len = __builtin_amdgcn_sad_u8(pk[i], 0u, len);
+    }
+    return len;
+}
+
+// Drop the symbols at and after byte vb of a piece (vb < 16) from row r's
+// cache; returns the piece's new bit length.
+template <int MODE, class Cache>
+__device__ __forceinline__ uint32_t clear_tail(Cache &cc, int r, const uint4 &v_in, uint32_t vb, const uint32_t *lut32) {
+    constexpr int U = Cache::kUnits;
+    // Opaque copies: the compiler must not keep pass 1's table entries or
+    // addresses alive for this rare path (it recomputes them here instead).
+    uint4 v = v_in;
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    asm volatile("" ::: "memory");
+    static_for<0, U>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        constexpr uint32_t sh = 8 * (u & 3);
+        if (MODE == kModePairs) {
+            if ((uint32_t)(2 * u + 1) >= vb) {   // the pair keeps at most its first code
+                const uint32_t e1 = (uint32_t)(2 * u) < vb ? lut32[byte_k<2 * u>(v)] : 0u;
+                cc.c[r][u] = e1 & ~0xffu;
+                cc.pk[r][u >> 2] = (cc.pk[r][u >> 2] & ~(0xffu << sh)) | ((e1 & 0xffu) << sh);
+            }
+        } else {
+            if ((uint32_t)u >= vb) {
+                cc.c[r][u] = 0;
+                cc.pk[r][u >> 2] &= ~(0xffu << sh);
+            }
+        }
+    });
+    uint32_t len = 0;
+#pragma unroll
+    for (int i = 0; i < U / 4; ++i) len = __builtin_amdgcn_sad_u8(cc.pk[r][i], 0u, len);
+    return len;
+}
+
+// Pass 2 over row r: OR the cached codes into LDS from absolute bit address
+// pos (the buffer's byte address is a multiple of 16, so word boundaries of
+// the buffer and of the absolute address coincide).
+template <class Cache>
+__device__ __forceinline__ void emit_row(const Cache &cc, int r, uint32_t pos) {
+    constexpr int U = Cache::kUnits;
+    static_for<0, U>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        or_code32_at(pos, cc.c[r][u]);
+        pos += (cc.pk[r][u >> 2] >> (8 * (u & 3))) & 0xffu;
+    });
+}
+
+template <int ROWS, int MODE>
+__device__ __forceinline__ void encode_pack_staged(const EncodeArgs &a) {
+    extern __shared__ uint4 stage4[];
+    __shared__ uint64_t lut64[MODE == kModeSingles ? 256 : 1];
+    __shared__ uint32_t lut32[MODE == kModePairs ? 256 : 1];
+    __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const ChunkPos p = chunk_pos(a, blockIdx.x);
+    uint4 v[ROWS];
+    uint32_t vb[ROWS];
+    load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
+    const DevTables *tab = seg_tables<EncodeArgs>(p.seg);
+    if (MODE == kModeSingles)
+        lut64[tid] = tab->enc64[tid];
+    else
+        lut32[tid] = tab->enc32[tid];
+    // zero the chunk buffer (worst-case chunk plus the spare group the
+    // two-word ORs may touch) while the loads are in flight
+    const uint32_t stage_groups = (a.chunk_symbols * a.max_len + 127) / 128 + 1;
+    for (uint32_t i = tid; i < stage_groups; i += kThreads) stage4[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    CodeCache<ROWS, MODE> cc;
+    uint32_t plen[ROWS];
+    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        plen[r] = cache_row<MODE>(cc, r, v[r], lut32, lut64);
+    });
+    if (p.cn != (uint32_t)(ROWS * kRowSyms)) {   // the segment's last chunk: drop missing symbols
+        static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            if (vb[r] < (uint32_t)kPiece) plen[r] = clear_tail<MODE>(cc, r, v[r], vb[r], lut32);
+        });
+    }
+    uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
+    const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
+    const uint32_t units = (chunk_bits + 127) >> 7;
+
+    const uint32_t base_bit = lds_addr(stage4) * 8;
+    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        emit_row(cc, r, base_bit + excl[r]);
+    });
+    const uint64_t dst_at = chunk_dst(a, p, units);
+    __syncthreads();
+    if (dst_at == ~0ull) return;
+    uint4 *dst = reinterpret_cast<uint4 *>(p.out + dst_at);
+    for (uint32_t i = tid; i < units; i += kThreads) dst[i] = stage4[i];
+}
+
+// Pair mode keeps 40 cached registers per thread: held to 128 VGPRs so that
+// four workgroups fit on a CU.  Single-code mode is bounded by its LDS stage.
+template <int ROWS>
+__global__ __launch_bounds__(kThreads, 4) void encode_pack_pairs_kernel(const EncodeArgs a) {
+    encode_pack_staged<ROWS, kModePairs>(a);
+}
+template <int ROWS>
+__global__ __launch_bounds__(kThreads) void encode_pack_singles_kernel(const EncodeArgs a) {
+    encode_pack_staged<ROWS, kModeSingles>(a);
+}
+
+// Row-by-row packing, any chunk size and code length up to 40 bits: each
+// row of 4096 symbols is looked up (64-bit LUT entries), packed into LDS and
+// stored; the partial last word is carried to the next row.
+template <int ROWS>
+__global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const EncodeArgs a) {
+    extern __shared__ uint32_t rowbuf[];
+    __shared__ uint64_t lut64[256];
+    __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const ChunkPos p = chunk_pos(a, blockIdx.x);
+    uint4 v[ROWS];
+    uint32_t vb[ROWS];
+    load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
+    lut64[tid] = seg_tables<EncodeArgs>(p.seg)->enc64[tid];
+    __syncthreads();
+
+    uint32_t plen[ROWS];
+    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        uint32_t x = 0;
+        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            x += (uint32_t)k < vb[r] ? (uint32_t)lut64[byte_k<k>(v[r])] & 0xffu : 0u;
+        });
+        plen[r] = x;
+    });
+    uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
+    const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
+    const uint32_t units = (chunk_bits + 127) >> 7;
+    const uint64_t dst_at = chunk_dst(a, p, units);
+    if (dst_at == ~0ull) return;   // uniform over the workgroup: nobody reaches a later barrier
+
+    uint32_t *dst = reinterpret_cast<uint32_t *>(p.out + dst_at);
+    const uint32_t total_words = units * 4;
     uint32_t carry = 0;
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
@@ -337,7 +466,15 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
         const uint32_t nbuf = (last ? total_words : (re + 31) >> 5) - wbase;
         for (uint32_t i = tid; i < nbuf; i += kThreads) rowbuf[i] = i == 0 ? carry : 0u;
         __syncthreads();
-        if (plen[r]) emit_piece<WIDE, PAIRS>(v[r], vb[r], excl[r] - wbase * 32, lut32, lut64, rowbuf);
+        uint32_t pos = excl[r] - wbase * 32;
+        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            if ((uint32_t)k < vb[r]) {
+                const uint64_t e = lut64[byte_k<k>(v[r])];
+                or_code64(rowbuf, pos, (uint32_t)(e >> 32), (uint32_t)e & ~0xffu);
+                pos += (uint32_t)e & 0xffu;
+            }
+        });
         __syncthreads();
         const uint32_t nwrite = last ? nbuf : (re >> 5) - wbase;
         for (uint32_t i = tid; i < nwrite; i += kThreads) dst[wbase + i] = rowbuf[i];
@@ -348,40 +485,49 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const EncodeArgs a) {
     });
 }
 
-__global__ void header_only_kernel(const EncodeArgs a) {
-    const uint32_t seg = blockIdx.x;
-    write_stream_head(a, seg, seg_tables<EncodeArgs>(seg), threadIdx.x, blockDim.x);
-}
+// ---------------------------------------------------------------- launches
 
 template <int ROWS>
-hipError_t launch_rows(const EncodeArgs &a, uint32_t max_len, uint32_t grid, uint32_t lds, hipStream_t s) {
-    if (max_len > (uint32_t)kNarrowMaxLen)
-        hipLaunchKernelGGL((encode_kernel<ROWS, true, false>), dim3(grid), dim3(kThreads), lds, s, a);
-    else if (max_len > 16)
-        hipLaunchKernelGGL((encode_kernel<ROWS, false, false>), dim3(grid), dim3(kThreads), lds, s, a);
-    else
-        hipLaunchKernelGGL((encode_kernel<ROWS, false, true>), dim3(grid), dim3(kThreads), lds, s, a);
+hipError_t launch_chunks(const EncodeArgs &a, uint32_t n_chunks, uint32_t stage, bool staged, hipStream_t s) {
+    hipLaunchKernelGGL((encode_sizes_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(encode_offsets_kernel, dim3(a.n_seg), dim3(kScanThreads), 0, s, a);
+    bool done = false;
+    if constexpr (ROWS <= 4) {
+        if (staged) {
+            if (a.max_len <= 16)
+                hipLaunchKernelGGL((encode_pack_pairs_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), stage, s, a);
+            else
+                hipLaunchKernelGGL((encode_pack_singles_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), stage, s, a);
+            done = true;
+        }
+    }
+    if (!done) {
+        // row buffer: one row's bits plus the carried word, the final
+        // padding and the spare words the three-word ORs may touch
+        const uint32_t lds = (kRowSyms * a.max_len / 32 + 8) * 4;
+        hipLaunchKernelGGL((encode_pack_rows_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), lds, s, a);
+    }
     return hipGetLastError();
 }
+
+constexpr uint32_t kStageBudget = 60 * 1024;   // dynamic LDS of the staged packer
 
 }  // namespace
 
-hipError_t launch_encode(const EncodeArgs &a, uint32_t /*codec*/, hipStream_t s) {
-    const uint32_t grid = a.n_seg * a.chunks_per_seg;
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
+    const uint32_t n_chunks = a.n_seg * a.chunks_per_seg;
+    if (n_chunks == 0) {   // header only
+        hipLaunchKernelGGL(encode_offsets_kernel, dim3(a.n_seg), dim3(kScanThreads), 0, s, a);
+        return hipGetLastError();
+    }
     const uint32_t rows = (a.chunk_symbols + kRowSyms - 1) / kRowSyms;
-    // row buffer: one row's bits plus the carried word, the final padding and
-    // the spare word the two-word ORs may touch
-    const uint32_t lds = (kRowSyms * a.max_len / 32 + 8) * 4;
-    if (rows <= 1) return launch_rows<1>(a, a.max_len, grid, lds, s);
-    if (rows <= 2) return launch_rows<2>(a, a.max_len, grid, lds, s);
-    if (rows <= 4) return launch_rows<4>(a, a.max_len, grid, lds, s);
-    if (rows <= 8) return launch_rows<8>(a, a.max_len, grid, lds, s);
-    return launch_rows<16>(a, a.max_len, grid, lds, s);
-}
-
-hipError_t launch_header_only(const EncodeArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(header_only_kernel, dim3(a.n_seg), dim3(256), 0, s, a);
-    return hipGetLastError();
+    const uint32_t stage = ((a.chunk_symbols * a.max_len + 127) / 128 + 1) * 16;
+    const bool staged = rows <= 4 && a.max_len <= 32 && stage <= kStageBudget;
+    if (rows <= 1) return launch_chunks<1>(a, n_chunks, stage, staged, s);
+    if (rows <= 2) return launch_chunks<2>(a, n_chunks, stage, staged, s);
+    if (rows <= 4) return launch_chunks<4>(a, n_chunks, stage, staged, s);
+    if (rows <= 8) return launch_chunks<8>(a, n_chunks, stage, false, s);
+    return launch_chunks<16>(a, n_chunks, stage, false, s);
 }
 
 }  // namespace ec

@@ -1,9 +1,15 @@
 // Byte histogram and the PMF statistics kernels.
 //
-// Histogram: each workgroup counts a contiguous slice of one segment into
-// LDS bins privatised per wave and per lane group (so the skewed e4m3
-// distributions, where a few bytes dominate, do not serialise the LDS
-// atomics), then adds its bins to the 64-bit global counts.
+// Histogram, two launches:
+//   1. histogram_kernel: each workgroup counts a contiguous slice of one
+//      segment into LDS bins privatised per wave and per lane group (so the
+//      skewed e4m3 distributions, where a few bytes dominate, do not
+//      serialise the LDS atomics), then stores its 256 partial counts with
+//      plain stores;
+//   2. histogram_reduce_kernel: sums the partial rows of each segment into
+//      the 64-bit counts, a slice of 16 bins per workgroup.
+// No global atomics: same-address atomics from many workgroups serialise at
+// the memory side.
 #include "dev_common.h"
 
 namespace ec {
@@ -13,16 +19,12 @@ namespace {
 constexpr int kHistThreads = 256;
 constexpr int kHistCopies = 4;                 // LDS copies per wave
 constexpr int kHistVecPerThread = 16;          // 16-byte loads per thread per block
-
-__global__ void fill_u64_kernel(uint64_t *p, uint64_t n, uint64_t v) {
-    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
-}
+constexpr int kReduceBins = 16;                // bins per reduce workgroup
 
 __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
                                                                  uint64_t seg_n, uint64_t in_stride,
                                                                  uint64_t vec_per_block,
-                                                                 uint64_t *__restrict__ counts) {
+                                                                 uint32_t *__restrict__ partial) {
     __shared__ uint32_t bins[kHistThreads / 64 * kHistCopies][256];
     const uint32_t tid = threadIdx.x;
     uint32_t *mine = bins[(tid >> 6) * kHistCopies + (tid & (kHistCopies - 1))];
@@ -58,8 +60,28 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
     uint32_t sum = 0;
 #pragma unroll
     for (int c = 0; c < kHistThreads / 64 * kHistCopies; ++c) sum += bins[c][tid];
-    if (sum) atomicAdd(reinterpret_cast<unsigned long long *>(counts + (uint64_t)seg * 256 + tid),
-                       (unsigned long long)sum);
+    partial[((uint64_t)seg * gridDim.x + blockIdx.x) * 256 + tid] = sum;
+}
+
+// Workgroup (j, seg) sums bins [16 j, 16 j + 16) of segment seg over its
+// `rows` partial rows: thread t takes bin t % 16 and every 16th row from
+// t / 16, then the 16 row groups are added in LDS.
+__global__ __launch_bounds__(256) void histogram_reduce_kernel(const uint32_t *__restrict__ partial, uint32_t rows,
+                                                               uint64_t *__restrict__ counts) {
+    __shared__ uint64_t acc[256 / kReduceBins][kReduceBins];
+    const uint32_t tid = threadIdx.x, b = tid % kReduceBins, g = tid / kReduceBins;
+    const uint32_t bin = blockIdx.x * kReduceBins + b;
+    const uint32_t *src = partial + (uint64_t)blockIdx.y * rows * 256 + bin;
+    uint64_t s = 0;
+    for (uint32_t r = g; r < rows; r += 256 / kReduceBins) s += src[(uint64_t)r * 256];
+    acc[g][b] = s;
+    __syncthreads();
+    if (g == 0) {
+        uint64_t t = 0;
+#pragma unroll
+        for (int k = 0; k < 256 / kReduceBins; ++k) t += acc[k][b];
+        counts[(uint64_t)blockIdx.y * 256 + bin] = t;
+    }
 }
 
 // ------------------------------------------------------------ PMF average
@@ -164,22 +186,26 @@ __global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict_
 
 }  // namespace
 
-hipError_t launch_fill_u64(uint64_t *p, uint64_t n, uint64_t v, hipStream_t s) {
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
-    return hipGetLastError();
-}
-
-hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
-                            uint64_t *counts, hipStream_t s) {
-    hipError_t e = launch_fill_u64(counts, (uint64_t)n_seg * 256, 0, s);
-    if (e != hipSuccess) return e;
+// Workgroups per segment: one per 4096 16-byte vectors, at most 65536 rows
+// of partial counts over all segments (but at least one per segment).
+uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
     const uint64_t n_vec = seg_n / 16;
     const uint64_t per_block = (uint64_t)kHistThreads * kHistVecPerThread;
     uint64_t blocks = (n_vec + per_block - 1) / per_block;
-    if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(histogram_kernel, dim3((unsigned)blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n,
-                       in_stride, per_block, counts);
+    const uint64_t cap = n_seg < 65536 ? 65536 / n_seg : 1;
+    if (blocks > cap) blocks = cap;
+    return blocks ? (uint32_t)blocks : 1u;
+}
+
+hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
+                            uint64_t *counts, uint32_t *partial, hipStream_t s) {
+    const uint32_t blocks = histogram_blocks(seg_n, n_seg);
+    const uint64_t n_vec = seg_n / 16;
+    const uint64_t per_block = (n_vec + blocks - 1) / blocks;
+    hipLaunchKernelGGL(histogram_kernel, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n, in_stride,
+                       per_block, partial);
+    hipLaunchKernelGGL(histogram_reduce_kernel, dim3(256 / kReduceBins, n_seg), dim3(256), 0, s, partial, blocks,
+                       counts);
     return hipGetLastError();
 }
 
