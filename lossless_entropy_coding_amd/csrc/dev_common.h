@@ -31,6 +31,19 @@ __device__ __forceinline__ const DevTables *seg_tables(uint32_t seg) {
     return p->tabs[seg];
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within
+// each row of 16 lanes, then the row broadcasts of lanes 15 and 31 (lanes
+// whose DPP source is outside the row, or whose row is masked off, add 0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // Status bits are OR-ed at device (agent) scope: visible across the eight
 // XCDs' separate L2 caches.
 __device__ __forceinline__ void or_status(uint32_t *status, uint32_t bits) {

@@ -20,7 +20,7 @@ constexpr int kL1Bits = 11;              // first-level decode table index width
 constexpr int kL1Size = 1 << kL1Bits;
 constexpr int kL2Size = 2048;            // second-level decode table entries (Huffman)
 constexpr int kL2MaxBits = 8;            // bits indexed by one second-level sub-table
-constexpr int kNarrowMaxLen = 24;        // codes up to this length use 32-bit encode entries
+constexpr int kNarrowMaxLen = 26;        // codes up to this length use 32-bit encode entries (6-bit length field)
 
 // Decode table entry formats (uint16):
 //  QLC level 1   : bits 0-7 symbol, bit 8 set = suffix is not a codeword
@@ -34,7 +34,7 @@ constexpr uint16_t kL1Long = 0x8000;
 // Everything a kernel needs about one codebook, uploaded as one blob.
 struct alignas(16) DevTables {
     uint64_t enc64[256];      // code << (64 - len) | len: left-aligned code, any length <= 40
-    uint32_t enc32[256];      // code << (32 - len) | len, when max_len <= 24
+    uint32_t enc32[256];      // code << (32 - len) | len, when max_len <= 26 (0 otherwise)
     uint16_t l1[kL1Size];     // decode level 1
     uint16_t l2[kL2Size];     // decode level 2 (Huffman)
     uint64_t limit[48];       // Huffman: 40-bit left-justified end of codes of length l

@@ -89,12 +89,7 @@ __device__ __forceinline__ uint32_t scan_pieces(const uint32_t (&plen)[ROWS], ui
     uint32_t incl[ROWS];
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        uint32_t x = plen[r];
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t y = __shfl_up(x, d, 64);
-            if (lane >= (uint32_t)d) x += y;
-        }
+        const uint32_t x = wave_incl_scan(plen[r]);
         incl[r] = x;
         if (lane == 63) wave_tot[r][wave] = x;
     });
@@ -266,10 +261,10 @@ __device__ __forceinline__ uint64_t chunk_dst(const EncodeArgs &a, const ChunkPo
     return end > a.out_cap ? ~0ull : (uint64_t)a.payload_offset + off;
 }
 
-// Staged packing, for chunks of up to 4 rows (16384 symbols) whose packed
-// bits fit in LDS: every LUT entry is read once and kept in registers as a
-// left-aligned code (pairs joined when codes are at most 16 bits) with its
-// length byte packed four to a register.
+// Staged packing, for chunks of up to 4 rows (16384 symbols) of codes up to
+// 26 bits whose packed bits fit in LDS: every 32-bit LUT entry is read once
+// and kept in registers as a left-aligned code (pairs joined when codes are
+// at most 16 bits) with its length byte packed four to a register.
 
 enum { kModePairs = 0, kModeSingles = 1 };
 
@@ -284,8 +279,7 @@ struct CodeCache {
 // All 16 bytes are looked up; bytes past the end of a piece are cleared
 // afterwards by clear_tail.
 template <int MODE, class Cache>
-__device__ __forceinline__ uint32_t cache_row(Cache &cc, int r, const uint4 &v, const uint32_t *lut32,
-                                              const uint64_t *lut64) {
+__device__ __forceinline__ uint32_t cache_row(Cache &cc, int r, const uint4 &v, const uint32_t *lut32) {
     constexpr int U = Cache::kUnits;
     uint32_t pk[U / 4];
 #pragma unroll
@@ -299,11 +293,12 @@ __device__ __forceinline__ uint32_t cache_row(Cache &cc, int r, const uint4 &v, 
             pk[p >> 2] |= ((e1 + e2) & 0xffu) << (8 * (p & 3));
         });
     } else {
+        // codes of up to 26 bits: the length sits in the low 6 bits
         static_for<0, U>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            const uint64_t e = lut64[byte_k<k>(v)];
-            cc.c[r][k] = (uint32_t)(e >> 32);
-            pk[k >> 2] |= ((uint32_t)e & 0xffu) << (8 * (k & 3));
+            const uint32_t e = lut32[byte_k<k>(v)];
+            cc.c[r][k] = e & ~63u;
+            pk[k >> 2] |= (e & 63u) << (8 * (k & 3));
         });
     }
     uint32_t len = 0;
@@ -363,8 +358,7 @@ __device__ __forceinline__ void emit_row(const Cache &cc, int r, uint32_t pos) {
 template <int ROWS, int MODE>
 __device__ __forceinline__ void encode_pack_staged(const EncodeArgs &a) {
     extern __shared__ uint4 stage4[];
-    __shared__ uint64_t lut64[MODE == kModeSingles ? 256 : 1];
-    __shared__ uint32_t lut32[MODE == kModePairs ? 256 : 1];
+    __shared__ uint32_t lut32[256];
     __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -372,11 +366,7 @@ __device__ __forceinline__ void encode_pack_staged(const EncodeArgs &a) {
     uint4 v[ROWS];
     uint32_t vb[ROWS];
     load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
-    const DevTables *tab = seg_tables<EncodeArgs>(p.seg);
-    if (MODE == kModeSingles)
-        lut64[tid] = tab->enc64[tid];
-    else
-        lut32[tid] = tab->enc32[tid];
+    lut32[tid] = seg_tables<EncodeArgs>(p.seg)->enc32[tid];
     // zero the chunk buffer (worst-case chunk plus the spare group the
     // two-word ORs may touch) while the loads are in flight
     const uint32_t stage_groups = (a.chunk_symbols * a.max_len + 127) / 128 + 1;
@@ -387,7 +377,7 @@ __device__ __forceinline__ void encode_pack_staged(const EncodeArgs &a) {
     uint32_t plen[ROWS];
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        plen[r] = cache_row<MODE>(cc, r, v[r], lut32, lut64);
+        plen[r] = cache_row<MODE>(cc, r, v[r], lut32);
     });
     if (p.cn != (uint32_t)(ROWS * kRowSyms)) {   // the segment's last chunk: drop missing symbols
         static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
@@ -522,7 +512,7 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
     }
     const uint32_t rows = (a.chunk_symbols + kRowSyms - 1) / kRowSyms;
     const uint32_t stage = ((a.chunk_symbols * a.max_len + 127) / 128 + 1) * 16;
-    const bool staged = rows <= 4 && a.max_len <= 32 && stage <= kStageBudget;
+    const bool staged = rows <= 4 && a.max_len <= (uint32_t)kNarrowMaxLen && stage <= kStageBudget;
     if (rows <= 1) return launch_chunks<1>(a, n_chunks, stage, staged, s);
     if (rows <= 2) return launch_chunks<2>(a, n_chunks, stage, staged, s);
     if (rows <= 4) return launch_chunks<4>(a, n_chunks, stage, staged, s);

@@ -17,18 +17,21 @@ namespace ec {
 namespace {
 
 constexpr int kHistThreads = 256;
-constexpr int kHistCopies = 4;                 // LDS copies per wave
-constexpr int kHistVecPerThread = 16;          // 16-byte loads per thread per block
-constexpr int kReduceBins = 16;                // bins per reduce workgroup
+constexpr int kHistCopies = 8;                 // LDS copies per wave (lane & 7)
+constexpr int kHistStride = 257;               // words per copy: copies of one bin fall in different banks
+constexpr int kHistVecPerThread = 16;          // 16-byte loads per thread per block (64 KiB per block)
+constexpr int kReduceBins = 2;                 // bins per reduce workgroup
+constexpr int kReduceGroups = 256 / kReduceBins;
 
 __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
                                                                  uint64_t seg_n, uint64_t in_stride,
                                                                  uint64_t vec_per_block,
                                                                  uint32_t *__restrict__ partial) {
-    __shared__ uint32_t bins[kHistThreads / 64 * kHistCopies][256];
+    constexpr int kCopies = kHistThreads / 64 * kHistCopies;
+    __shared__ uint32_t bins[kCopies * kHistStride];
     const uint32_t tid = threadIdx.x;
-    uint32_t *mine = bins[(tid >> 6) * kHistCopies + (tid & (kHistCopies - 1))];
-    for (uint32_t i = tid; i < sizeof(bins) / 4; i += kHistThreads) (&bins[0][0])[i] = 0;
+    uint32_t *mine = bins + ((tid >> 6) * kHistCopies + (tid & (kHistCopies - 1))) * kHistStride;
+    for (uint32_t i = tid; i < kCopies * kHistStride; i += kHistThreads) bins[i] = 0;
     __syncthreads();
 
     const uint32_t seg = blockIdx.y;
@@ -42,9 +45,8 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
     const uint64_t v0 = (uint64_t)blockIdx.x * vec_per_block;
     const uint64_t v1 = v0 + vec_per_block < n_vec ? v0 + vec_per_block : n_vec;
     const uint4 *vp = reinterpret_cast<const uint4 *>(vbase);
-    for (uint64_t v = v0 + tid; v < v1; v += kHistThreads) {
-        uint4 q = vp[v];
-        uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    auto count = [&](const uint4 &q) __attribute__((always_inline)) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             atomicAdd(&mine[w[k] & 0xff], 1u);
@@ -52,36 +54,55 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
             atomicAdd(&mine[(w[k] >> 16) & 0xff], 1u);
             atomicAdd(&mine[w[k] >> 24], 1u);
         }
+    };
+    // four vectors in flight per thread
+    uint64_t v = v0 + tid;
+    for (; v + 3 * kHistThreads < v1; v += 4 * kHistThreads) {
+        const uint4 q0 = vp[v], q1 = vp[v + kHistThreads], q2 = vp[v + 2 * kHistThreads], q3 = vp[v + 3 * kHistThreads];
+        count(q0);
+        count(q1);
+        count(q2);
+        count(q3);
     }
+    for (; v < v1; v += kHistThreads) count(vp[v]);
     if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid]], 1u);
     if (blockIdx.x == 0 && tid < tail) atomicAdd(&mine[vbase[n_vec * 16 + tid]], 1u);
     __syncthreads();
 
     uint32_t sum = 0;
 #pragma unroll
-    for (int c = 0; c < kHistThreads / 64 * kHistCopies; ++c) sum += bins[c][tid];
+    for (int c = 0; c < kCopies; ++c) sum += bins[c * kHistStride + tid];
     partial[((uint64_t)seg * gridDim.x + blockIdx.x) * 256 + tid] = sum;
 }
 
-// Workgroup (j, seg) sums bins [16 j, 16 j + 16) of segment seg over its
-// `rows` partial rows: thread t takes bin t % 16 and every 16th row from
-// t / 16, then the 16 row groups are added in LDS.
+// Workgroup (j, seg) sums bins [2 j, 2 j + 2) of segment seg over its `rows`
+// partial rows: thread t takes bin t % 2 and every 128th row from t / 2
+// (eight loads in flight), then the 128 row groups are added in LDS.
 __global__ __launch_bounds__(256) void histogram_reduce_kernel(const uint32_t *__restrict__ partial, uint32_t rows,
                                                                uint64_t *__restrict__ counts) {
-    __shared__ uint64_t acc[256 / kReduceBins][kReduceBins];
+    __shared__ uint64_t acc[kReduceGroups][kReduceBins];
     const uint32_t tid = threadIdx.x, b = tid % kReduceBins, g = tid / kReduceBins;
     const uint32_t bin = blockIdx.x * kReduceBins + b;
     const uint32_t *src = partial + (uint64_t)blockIdx.y * rows * 256 + bin;
-    uint64_t s = 0;
-    for (uint32_t r = g; r < rows; r += 256 / kReduceBins) s += src[(uint64_t)r * 256];
-    acc[g][b] = s;
-    __syncthreads();
-    if (g == 0) {
-        uint64_t t = 0;
+    uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    uint32_t r = g;
+    for (; r + 7 * kReduceGroups < rows; r += 8 * kReduceGroups) {
+        uint32_t x[8];
 #pragma unroll
-        for (int k = 0; k < 256 / kReduceBins; ++k) t += acc[k][b];
-        counts[(uint64_t)blockIdx.y * 256 + bin] = t;
+        for (int k = 0; k < 8; ++k) x[k] = src[(uint64_t)(r + k * kReduceGroups) * 256];
+        s0 += (uint64_t)x[0] + x[1];
+        s1 += (uint64_t)x[2] + x[3];
+        s2 += (uint64_t)x[4] + x[5];
+        s3 += (uint64_t)x[6] + x[7];
     }
+    for (; r < rows; r += kReduceGroups) s0 += src[(uint64_t)r * 256];
+    acc[g][b] = s0 + s1 + s2 + s3;
+    __syncthreads();
+    for (uint32_t h = kReduceGroups / 2; h > 0; h >>= 1) {
+        if (g < h) acc[g][b] += acc[g + h][b];
+        __syncthreads();
+    }
+    if (g == 0) counts[(uint64_t)blockIdx.y * 256 + bin] = acc[0][b];
 }
 
 // ------------------------------------------------------------ PMF average
