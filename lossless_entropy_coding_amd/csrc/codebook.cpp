@@ -205,51 +205,14 @@ int build_huffman_lengths(const uint8_t len[256], ec_codebook **out) {
     for (uint32_t l = 1; l <= (uint32_t)EC_MAX_CODE_LEN; ++l)
         t.limit[l] = ((uint64_t)t.first_code[l] + bl_count[l]) << (EC_MAX_CODE_LEN - l);
 
-    // level 1: windows whose code has <= 11 bits
-    uint32_t long_max[kL1Size];   // longest code under a long 11-bit prefix (0: short)
-    for (int w = 0; w < kL1Size; ++w) long_max[w] = 0;
+    // 13-bit decode table: windows whose code has <= 13 bits; 0 marks the
+    // prefixes of longer codes (found by the canonical limit search)
+    for (int w = 0; w < kHuffSize; ++w) t.hl1[w] = 0;
     for (int s = 0; s < 256; ++s) {
         uint32_t l = len[s];
-        if (l <= (uint32_t)kL1Bits) {
-            uint32_t lo = (uint32_t)code[s] << (kL1Bits - l), hi = lo + (1u << (kL1Bits - l));
-            for (uint32_t w = lo; w < hi; ++w) t.l1[w] = (uint16_t)(s | (l << 8));
-        } else {
-            uint32_t p = (uint32_t)(code[s] >> (l - kL1Bits));
-            long_max[p] = std::max(long_max[p], l);
-        }
-    }
-    // level 2: each long prefix gets a sub-table indexed by the next w2 bits,
-    // w2 = min(8, deepest code under it - 11), shrunk (deepest prefix first)
-    // until all sub-tables fit kL2Size entries
-    uint32_t w2[kL1Size];
-    uint32_t total = 0;
-    for (int p = 0; p < kL1Size; ++p) {
-        w2[p] = long_max[p] ? std::min<uint32_t>(kL2MaxBits, long_max[p] - kL1Bits) : 0;
-        total += long_max[p] ? (1u << w2[p]) : 0;
-    }
-    while (total > (uint32_t)kL2Size) {
-        int best = -1;
-        for (int p = 0; p < kL1Size; ++p)
-            if (long_max[p] && w2[p] > 1 && (best < 0 || w2[p] >= w2[best])) best = p;
-        if (best < 0) break;   // cannot happen: at most 256 long prefixes x 2 entries
-        total -= 1u << (w2[best] - 1);
-        w2[best]--;
-    }
-    uint32_t base = 0;
-    for (int p = 0; p < kL1Size; ++p) {
-        if (!long_max[p]) continue;
-        t.l1[p] = (uint16_t)(kL1Long | ((w2[p] - 1) << 12) | base);
-        for (uint32_t i = 0; i < (1u << w2[p]); ++i) t.l2[base + i] = 0;   // deeper code
-        for (int s = 0; s < 256; ++s) {
-            uint32_t l = len[s];
-            if (l <= (uint32_t)kL1Bits || (uint32_t)(code[s] >> (l - kL1Bits)) != (uint32_t)p) continue;
-            uint32_t rest = l - kL1Bits;
-            if (rest > w2[p]) continue;
-            uint32_t tail = (uint32_t)code[s] & ((1u << rest) - 1);
-            uint32_t lo = tail << (w2[p] - rest), hi = lo + (1u << (w2[p] - rest));
-            for (uint32_t i = lo; i < hi; ++i) t.l2[base + i] = (uint16_t)(s | (l << 8));
-        }
-        base += 1u << w2[p];
+        if (l == 0 || l > (uint32_t)kHuffBits) continue;
+        uint32_t lo = (uint32_t)code[s] << (kHuffBits - l), hi = lo + (1u << (kHuffBits - l));
+        for (uint32_t w = lo; w < hi; ++w) t.hl1[w] = (uint16_t)(s | (l << 8));
     }
 
     uint8_t desc[257];

@@ -4,7 +4,8 @@
 // index, so one lane decodes one sub-chunk serially and a wave64 decodes 64
 // consecutive sub-chunks side by side.  Their compressed bits form one
 // contiguous span of the payload (about 14 KiB at 16384-symbol chunks), which
-// the wave first copies into its own LDS region with coalesced 16-byte loads.
+// the wave first copies into its own LDS region (16 KiB, 15 KiB for Huffman)
+// with coalesced 16-byte loads.
 // The decode loop then reads only LDS: a 32-bit window at any bit position is
 // one two-word LDS read plus a funnel shift and serves two codes of up to 16
 // bits each.  (A global load inside the loop would stall on the output
@@ -14,10 +15,10 @@
 //            (no memory access on the dependency chain); the top 11 bits index
 //            a 2048-entry LDS table that yields the byte or flags an unused
 //            suffix.
-//   Huffman  the top 11 bits index an LDS table: codes of up to 11 bits
-//            resolve there; longer codes point to a per-prefix second-level
-//            LDS table of up to 8 more bits; deeper codes (rare) are found by
-//            comparing a 40-bit window against the canonical code limits.
+//   Huffman  the top 13 bits index a 16 KiB LDS table that yields the byte
+//            and the length of every code of up to 13 bits; longer codes
+//            (rare) are found by comparing a 40-bit window against the
+//            canonical code limits.
 //   EG       count leading zeros z; the code is 2z + k + 1 bits; rank -> byte
 //            through a 256-entry LDS table.
 // After its last symbol a lane checks that it stopped exactly where the index
@@ -30,31 +31,34 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kSpanBytes = 16384;               // LDS staging per wave
-constexpr uint32_t kSpanRegion = kSpanBytes + 32;    // + a leading zero block and a trailing block
 constexpr uint32_t kGuardBytes = 1536;               // > 256 codes x 40 bits of overrun
 
 // Bits of a lane's sub-chunk staged in LDS.  The wave's span is copied to
-// words 1.. of its region (word 0 is a zero guard), and x = 31 + the bit
-// position in the span, so the word holding the bit before the read position
-// is x >> 5 >= 0 and a 32-bit window never needs a special case.  Positions
-// only move forward from a validated start by at most 40 bits a code, and the
-// region is followed by guard words, so reads stay inside the allocation even
-// for corrupt streams.
+// words 4.. of its region (words 0-3 are zero, word 3 is the guard before
+// the span).  x is the absolute LDS bit address of the guard word's start
+// plus 31 plus the span bit position, so the word holding the bit before the
+// read position is x >> 5 and a 32-bit window never needs a special case.
+// Positions only move forward from a validated start by at most 40 bits a
+// code, and the region is followed by guard words, so reads stay inside the
+// allocation even for corrupt streams.
 struct SpanBits {
     static constexpr bool kStaged = true;
-    const uint32_t *words;   // region word 0 (the guard)
-    uint32_t x;
+    uint32_t x;      // absolute LDS bit address of the position, plus 31
+    uint32_t base;   // absolute LDS bit address of the span's first bit
 
+    typedef __attribute__((address_space(3))) const uint32_t lds_word;
     __device__ __forceinline__ uint32_t at(uint32_t xx) const {
-        const uint32_t *w = words + (xx >> 5);
+        // word address from the bit address by a shift and a mask (no base
+        // to add); the two words hold the bit before the position and the
+        // 31 bits after it
+        lds_word *w = (lds_word *)(size_t)((xx >> 3) & ~3u);
         return __builtin_amdgcn_alignbit(w[0], w[1], ~xx);
     }
     __device__ __forceinline__ uint32_t win() const { return at(x); }
     __device__ __forceinline__ uint64_t win64() const { return ((uint64_t)at(x) << 32) | at(x + 32u); }
     __device__ __forceinline__ void adv(uint32_t l) { x += l; }
     __device__ __forceinline__ void prepare() {}
-    __device__ __forceinline__ uint64_t bit() const { return x - 31u; }
+    __device__ __forceinline__ uint64_t bit() const { return x + 1u - base; }   // span-relative position
 };
 
 // Bits of a lane's sub-chunk read straight from global memory (spans that
@@ -109,11 +113,11 @@ struct GlobalBits {
     __device__ __forceinline__ uint64_t bit() const { return (base0 + nxt) * 32 - nb; }
 };
 
-// Huffman code longer than the two table levels: canonical limit search on
-// a 40-bit left-justified window.  Returns symbol | length << 8.
+// Huffman code longer than the decode table's 13 bits (rare): canonical
+// limit search on a 40-bit left-justified window.  Returns symbol | length << 8.
 __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DevTables *tab) {
     const uint64_t w40 = window >> (64 - EC_MAX_CODE_LEN);
-    uint32_t l = kL1Bits + 1;
+    uint32_t l = kHuffBits + 1;
     const uint32_t mx = tab->max_len;
     while (l < mx && w40 >= tab->limit[l]) ++l;
     const uint64_t code = w40 >> (EC_MAX_CODE_LEN - l);
@@ -121,72 +125,62 @@ __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DevTables *tab
     return tab->sym[idx & 255] | (l << 8);
 }
 
-// Huffman lookup for a window whose first-level entry e marks a long code:
-// second-level table, then (rare) the canonical limit search on 64 bits
-// taken at the source's current position.
-template <class Src>
-__device__ __forceinline__ uint32_t huff_long(uint32_t w, uint32_t e, const uint16_t *l2, const Src &S,
-                                              const DevTables *tab) {
-    const uint32_t w2 = ((e >> 12) & 7u) + 1u;
-    e = l2[(e & 0x7ffu) + ((w << kL1Bits) >> (32u - w2))];
-    if ((e >> 8) == 0) e = huff_deep(S.win64(), tab);
-    return e;
-}
-
 // Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
 // run) from source S into dst; returns the bits of the QLC / EG "not a
 // codeword" flags (bit 8 and up).
 template <int CODEC, int PAIRS, class Src>
 __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *dst, const uint16_t *l1,
-                                               const uint16_t *l2, const uint8_t *symtab, const DevTables *tab,
-                                               uint32_t lens, uint32_t k_eg) {
+                                               const uint8_t *symtab, const DevTables *tab, uint32_t lens,
+                                               uint32_t k_eg) {
     uint32_t bad = 0;
-    // symbol | length << 8 of the code that starts the window w
-    auto sym_at = [&](uint32_t w) __attribute__((always_inline)) -> uint32_t {
+    // The code that starts window w: its table entry (symbol in byte 0; for
+    // QLC bit 8 flags an unused suffix) and its length.  QLC takes the length
+    // from the 3-bit prefix through the packed constant, off the memory
+    // dependency chain; Huffman and EG entries carry it in bits 8 and up.
+    struct Code {
+        uint32_t e, len;
+    };
+    auto code_at = [&](uint32_t w) __attribute__((always_inline)) -> Code {
         if (CODEC == EC_CODEC_QLC) {
-            const uint32_t e = l1[w >> 21];
-            bad |= e;
-            return (e & 0xffu) | (((lens >> ((w >> 29) << 2)) & 15u) << 8);
+            return Code{l1[w >> 21], (lens >> ((w >> 29) << 2)) & 15u};
         } else if (CODEC == EC_CODEC_HUFFMAN) {
-            uint32_t e = l1[w >> 21];
-            if (e & kL1Long) e = huff_long(w, e, l2, S, tab);
-            return e;
+            uint32_t e = l1[w >> (32 - kHuffBits)];
+            if (e < 256u) e = huff_deep(S.win64(), tab);
+            return Code{e, e >> 8};
         } else {
             const uint32_t zr = __clz(w);
             const uint32_t z = zr < 8u ? zr : 8u;   // more zeros: not a codeword
             const uint32_t l = 2 * z + k_eg + 1;
             const uint32_t rank = (w >> (32 - l)) - (1u << k_eg);
             bad |= rank | (zr > 8u ? kQlcInvalid : 0u);
-            return symtab[rank & 255u] | (l << 8);
+            return Code{symtab[rank & 255u], l};
         }
     };
     auto one = [&]() __attribute__((always_inline)) -> uint32_t {
-        const uint32_t e = sym_at(S.win());
-        S.adv(e >> 8);
-        return e & 0xffu;
+        const Code c = code_at(S.win());
+        if (CODEC == EC_CODEC_QLC) bad |= c.e;
+        S.adv(c.len);
+        return c.e & 0xffu;
     };
     // two codes from one window when both fit in it; returns byte0 | byte1 << 8
     auto two = [&]() __attribute__((always_inline)) -> uint32_t {
         const uint32_t w = S.win();
-        const uint32_t e1 = sym_at(w);
-        const uint32_t n1 = e1 >> 8;
-        uint32_t e2;
+        const Code c1 = code_at(w);
+        Code c2;
         if (CODEC == EC_CODEC_HUFFMAN) {
-            // the second code comes from the same window when the first left
-            // at least 11 bits and the second is a first-level code
-            S.adv(n1);
-            const uint32_t w2 = n1 <= 21u ? w << n1 : S.win();
-            e2 = l1[w2 >> 21];
-            if (e2 & kL1Long) {
-                const uint32_t wf = S.win();
-                e2 = huff_long(wf, l1[wf >> 21], l2, S, tab);
-            }
-            S.adv(e2 >> 8);
+            // the second code's table index comes from the same window when
+            // the first code left at least 13 bits of it
+            S.adv(c1.len);
+            const uint32_t w2 = c1.len <= 32u - kHuffBits ? w << c1.len : S.win();
+            c2.e = l1[w2 >> (32 - kHuffBits)];
+            if (c2.e < 256u) c2.e = huff_deep(S.win64(), tab);
+            S.adv(c2.e >> 8);
         } else {
-            e2 = sym_at(w << n1);
-            S.adv(n1 + (e2 >> 8));
+            c2 = code_at(w << c1.len);
+            S.adv(c1.len + c2.len);
+            if (CODEC == EC_CODEC_QLC) bad |= c1.e | c2.e;
         }
-        return __builtin_amdgcn_perm(e2, e1, 0x0c0c0400u);   // byte 0 of e1, byte 0 of e2
+        return __builtin_amdgcn_perm(c2.e, c1.e, 0x0c0c0400u);   // byte 0 of c1.e, byte 0 of c2.e
     };
     // eight codes -> two output words
     auto eight = [&](uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {
@@ -238,20 +232,24 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
 
 template <int CODEC, int PAIRS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
+    // Staging per wave: 16 KiB, or 15 KiB next to the 16 KiB Huffman table,
+    // so that two workgroups still fit in a CU's 160 KiB of LDS.
+    constexpr uint32_t kSpan = CODEC == EC_CODEC_HUFFMAN ? 15360 : 16384;
+    constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
+                                   : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
+                                                               : 1;
     // tables first, so that their addresses fit the LDS instructions' offset field
     struct Smem {
-        uint4 l1v[CODEC == EC_CODEC_EXP_GOLOMB ? 1 : kL1Size * 2 / 16];
-        uint4 l2v[CODEC == EC_CODEC_HUFFMAN ? kL2Size * 2 / 16 : 1];
+        uint4 tabv[kTableVec];
         uint8_t symtab[256];
         uint64_t po, pb;
         uint32_t ok, nch, spc;
         uint32_t pad_;
-        uint4 spans[kWaves][kSpanRegion / 16];
+        uint4 spans[kWaves][(kSpan + 32) / 16];
         uint4 guard[kGuardBytes / 16];
     };
     __shared__ Smem sm;
-    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.l1v);
-    const uint16_t *l2 = reinterpret_cast<const uint16_t *>(sm.l2v);
+    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.tabv);
     uint8_t *symtab = sm.symtab;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t seg = blockIdx.y;
@@ -259,8 +257,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
     uint32_t *status = a.status ? a.status + seg : nullptr;
 
-    if (CODEC != EC_CODEC_EXP_GOLOMB) sm.l1v[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
-    if (CODEC == EC_CODEC_HUFFMAN) sm.l2v[tid] = reinterpret_cast<const uint4 *>(tab->l2)[tid];
+    if (CODEC == EC_CODEC_QLC) sm.tabv[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
+    if (CODEC == EC_CODEC_HUFFMAN) {
+#pragma unroll
+        for (int k = 0; k < (int)kTableVec / kThreads; ++k)
+            sm.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
+    }
     if (CODEC == EC_CODEC_EXP_GOLOMB) symtab[tid] = tab->sym[tid];
 
     if (tid == 0) {
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     const uint32_t g_last = (g0 + 63 < a.blocks_per_seg ? g0 + 63 : a.blocks_per_seg - 1);
     const uint64_t span_lo = chunk_off[g0 / spc] & ~15ull;
     const uint64_t span_hi = chunk_off[g_last / spc + 1];
-    bool fits = span_lo <= span_hi && span_hi <= pb && span_hi - span_lo <= kSpanBytes;
+    bool fits = span_lo <= span_hi && span_hi <= pb && span_hi - span_lo <= kSpan;
     fits = fits && __ballot(ok && (co0 < span_lo || co1 > span_hi)) == 0;
 
     const uint64_t first_sym = (uint64_t)g * kSub;
@@ -351,16 +353,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (ok) {
             SpanBits S;
-            S.words = reinterpret_cast<const uint32_t *>(region) + 3;   // the guard word before the span
-            S.x = (uint32_t)((co0 - span_lo) * 8 + e_start) + 31u;
-            bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, l2, symtab, tab, lens, k_eg);
+            // word 3 of the region is the guard word right before the span
+            S.base = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint4 *)region * 8 + 4 * 32;
+            S.x = S.base + (uint32_t)((co0 - span_lo) * 8 + e_start) - 1u;
+            bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, symtab, tab, lens, k_eg);
             end_pos = S.bit();
             want_pos = (co0 - span_lo) * 8 + e_end;
         }
     } else if (ok) {
         GlobalBits S;
         S.init(reinterpret_cast<const uint32_t *>(payload), pb >> 2, co0 * 8 + e_start);
-        bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, l2, symtab, tab, lens, k_eg);
+        bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, symtab, tab, lens, k_eg);
         end_pos = S.bit();
         want_pos = co0 * 8 + e_end;
     }

@@ -16,27 +16,25 @@ constexpr uint32_t kSub = 256;           // symbols per sub-chunk
 constexpr uint32_t kMinChunk = 256;
 constexpr uint32_t kMaxChunk = 65536;
 
-constexpr int kL1Bits = 11;              // first-level decode table index width
+constexpr int kL1Bits = 11;              // QLC decode table index width (codes <= 11 bits)
 constexpr int kL1Size = 1 << kL1Bits;
-constexpr int kL2Size = 2048;            // second-level decode table entries (Huffman)
-constexpr int kL2MaxBits = 8;            // bits indexed by one second-level sub-table
+constexpr int kHuffBits = 13;            // Huffman decode table index width
+constexpr int kHuffSize = 1 << kHuffBits;
 constexpr int kNarrowMaxLen = 26;        // codes up to this length use 32-bit encode entries (6-bit length field)
 
 // Decode table entry formats (uint16):
-//  QLC level 1   : bits 0-7 symbol, bit 8 set = suffix is not a codeword
-//  Huffman L1    : bit 15 clear -> bits 0-7 symbol, bits 8-11 code length (1..11)
-//                  bit 15 set   -> long prefix: bits 0-10 base index into l2,
-//                                  bits 12-14 (sub-table width - 1)
-//  Huffman L2    : bits 0-7 symbol, bits 8-12 code length (12..19); 0 length = deeper code
+//  QLC (11-bit index)     : bits 0-7 symbol, bit 8 set = suffix is not a codeword
+//  Huffman (13-bit index) : bits 0-7 symbol, bits 8-12 code length (1..13);
+//                           0 = the code is longer than 13 bits (canonical
+//                           limit search)
 constexpr uint16_t kQlcInvalid = 0x100;
-constexpr uint16_t kL1Long = 0x8000;
 
 // Everything a kernel needs about one codebook, uploaded as one blob.
 struct alignas(16) DevTables {
     uint64_t enc64[256];      // code << (64 - len) | len: left-aligned code, any length <= 40
     uint32_t enc32[256];      // code << (32 - len) | len, when max_len <= 26 (0 otherwise)
-    uint16_t l1[kL1Size];     // decode level 1
-    uint16_t l2[kL2Size];     // decode level 2 (Huffman)
+    uint16_t l1[kL1Size];     // QLC decode table
+    uint16_t hl1[kHuffSize];  // Huffman decode table
     uint64_t limit[48];       // Huffman: 40-bit left-justified end of codes of length l
     uint64_t first_code[48];  // Huffman: canonical first code of length l
     uint32_t first_idx[48];   // Huffman: position of that code in sorted_sym
