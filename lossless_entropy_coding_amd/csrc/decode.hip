@@ -230,11 +230,98 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
     return bad;
 }
 
+// Index entries of one lane's sub-chunk and of its wave's span, as loaded
+// from the stream (resolved later, so that the loads can be in flight while
+// the wave decodes an earlier task).
+struct IndexRaw {
+    uint64_t co0, co1;        // the lane's chunk: byte offsets of its start and end in the payload
+    uint64_t slo, shi;        // the wave's span: first chunk's start, last chunk's end
+    uint32_t e_start, e_end;  // the lane's sub-chunk: start and end bit in its chunk
+};
+
+// A wave's task: 64 consecutive sub-chunks of one stream, one per lane.
+struct Plan {
+    uint64_t co0, span_lo;
+    uint32_t e_start, e_end, cnt, nblk;
+    uint64_t first_sym;
+    bool active, ok, fits;
+};
+
+// Stream fields the tasks of a segment share (validated once per segment).
+struct StreamInfo {
+    const uint8_t *stream;
+    uint64_t po, pb;
+    uint32_t nch, spc;
+};
+
+__device__ __forceinline__ IndexRaw issue_index(const DecodeArgs &a, const StreamInfo &si, uint32_t g0,
+                                                uint32_t lane) {
+    const uint64_t *chunk_off = reinterpret_cast<const uint64_t *>(si.stream + kHeaderBytes);
+    const uint32_t *sub_end = reinterpret_cast<const uint32_t *>(si.stream + kHeaderBytes + 8ull * (si.nch + 1));
+    const uint32_t g = g0 + lane;
+    const uint32_t gl = g < a.blocks_per_seg ? g : a.blocks_per_seg - 1;
+    const uint32_t c = gl / si.spc, j = gl - c * si.spc;
+    const uint32_t g_last = g0 + 63 < a.blocks_per_seg ? g0 + 63 : a.blocks_per_seg - 1;
+    IndexRaw r;
+    r.co0 = chunk_off[c];
+    r.co1 = chunk_off[c + 1];
+    r.e_end = sub_end[(uint64_t)c * si.spc + j];
+    r.e_start = j ? sub_end[(uint64_t)c * si.spc + j - 1] : 0u;
+    r.slo = chunk_off[g0 / si.spc];
+    r.shi = chunk_off[g_last / si.spc + 1];
+    return r;
+}
+
+// Checks the lane's index entries (flags a corrupt index) and decides
+// whether the wave's span fits its LDS region.
+template <uint32_t kSpan>
+__device__ __forceinline__ Plan resolve(const DecodeArgs &a, const StreamInfo &si, const IndexRaw &r, uint32_t g0,
+                                        uint32_t lane, uint32_t *status) {
+    Plan p;
+    const uint32_t g = g0 + lane;
+    p.active = g < a.blocks_per_seg;
+    p.ok = p.active && r.co0 <= r.co1 && r.co1 <= si.pb && !(r.co0 & 15) &&
+           (uint64_t)r.e_end <= (r.co1 - r.co0) * 8 && r.e_start <= r.e_end;
+    if (p.active && !p.ok) or_status(status, EC_S_CORRUPT);
+    p.span_lo = r.slo & ~15ull;
+    const uint64_t span_hi = r.shi;
+    bool fits = p.span_lo <= span_hi && span_hi <= si.pb && span_hi - p.span_lo <= kSpan;
+    p.fits = fits && __ballot(p.ok && (r.co0 < p.span_lo || r.co1 > span_hi)) == 0;
+    p.nblk = p.fits ? (uint32_t)((span_hi - p.span_lo + 15) >> 4) : 0u;
+    p.co0 = r.co0;
+    p.e_start = r.e_start;
+    p.e_end = r.e_end;
+    p.first_sym = (uint64_t)g * kSub;
+    p.cnt = !p.active ? 0u : (a.seg_n - p.first_sym < kSub ? (uint32_t)(a.seg_n - p.first_sym) : (uint32_t)kSub);
+    return p;
+}
+
+// The wave's span as 16-byte blocks, lane + 64 k, loaded into registers
+// (indexes clamped to the span, so every load stays inside it).
+template <int K>
+__device__ __forceinline__ void issue_span(const StreamInfo &si, const Plan &p, uint32_t lane, uint4 (&v)[K]) {
+    if (!p.fits || p.nblk == 0) return;
+    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + (p.span_lo >> 4);
+    const uint32_t last = p.nblk - 1;
+    static_for<0, K>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        v[k] = src[min(lane + 64u * k, last)];
+    });
+}
+
+// Persistent workgroups: workgroup b takes tasks b, b + G, ... (G = grid);
+// a task is 256 consecutive sub-chunks of one stream, 64 per wave.  For QLC
+// the index entries of the wave's task after next and the compressed span of
+// its next task are loaded while it decodes the current one.
 template <int CODEC, int PAIRS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     // Staging per wave: 16 KiB, or 15 KiB next to the 16 KiB Huffman table,
     // so that two workgroups still fit in a CU's 160 KiB of LDS.
     constexpr uint32_t kSpan = CODEC == EC_CODEC_HUFFMAN ? 15360 : 16384;
+    constexpr int kSpanVec = kSpan / 16 / 64;   // 16-byte blocks per lane
+    // Keeping the next span in registers costs 64 VGPRs: QLC's decode loop
+    // has them to spare, the Huffman and EG loops do not.
+    constexpr bool kPrefetch = CODEC == EC_CODEC_QLC;
     constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
                                    : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
                                                                : 1;
@@ -252,129 +339,189 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.tabv);
     uint8_t *symtab = sm.symtab;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t seg = blockIdx.y;
-    const DevTables *tab = seg_tables<DecodeArgs>(seg);
-    const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
-    uint32_t *status = a.status ? a.status + seg : nullptr;
+    const uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads > 0 ? (a.blocks_per_seg + kThreads - 1) / kThreads
+                                                                           : 1u;
+    const uint32_t n_tasks = gx * a.n_seg;
+    uint4 *region = sm.spans[wave];
+    // word 3 of the region is the guard word right before the span
+    const uint32_t region_base = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint4 *)region * 8 + 4 * 32;
 
-    if (CODEC == EC_CODEC_QLC) sm.tabv[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
-    if (CODEC == EC_CODEC_HUFFMAN) {
+    uint32_t cur_seg = ~0u;
+    StreamInfo si = {};
+    const DevTables *tab = nullptr;
+    uint32_t *status = nullptr;
+    bool have_cur = false, have_next_raw = false;
+    Plan cur = {};
+    IndexRaw next_raw = {};
+    uint4 span_regs[kPrefetch ? kSpanVec : 1];
 #pragma unroll
-        for (int k = 0; k < (int)kTableVec / kThreads; ++k)
-            sm.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
-    }
-    if (CODEC == EC_CODEC_EXP_GOLOMB) symtab[tid] = tab->sym[tid];
+    for (int k = 0; k < (kPrefetch ? kSpanVec : 1); ++k) span_regs[k] = make_uint4(0, 0, 0, 0);
 
-    if (tid == 0) {
-        const uint64_t *h = reinterpret_cast<const uint64_t *>(stream);
-        const uint64_t h0 = h[0], n = h[1], h2 = h[2], po = h[3], pb = h[4], id = h[5];
-        const uint32_t magic = (uint32_t)h0, version = (uint32_t)(h0 >> 32) & 0xffffu;
-        const uint32_t codec = (uint32_t)(h0 >> 48) & 0xffu, flags = (uint32_t)(h0 >> 56);
-        const uint32_t C = (uint32_t)h2, nch = (uint32_t)(h2 >> 32);
-        uint32_t bits = 0;
-        if (magic != kMagic || version != kVersion || (flags & ~1u)) {
-            bits = EC_S_BAD_HEADER;
-        } else if (codec != tab->codec || id != tab->codebook_id) {
-            bits = EC_S_CODEBOOK_MISMATCH;
-        } else if (n != a.seg_n || C == 0 || (C % kSub) || C > kMaxChunk ||
-                   (uint64_t)nch != (n + C - 1) / C) {
-            bits = EC_S_BAD_HEADER;
+    for (uint32_t t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+        const uint32_t seg = t / gx, bx = t - seg * gx;
+        if (seg != cur_seg) {
+            __syncthreads();   // the previous segment's tables are no longer read
+            tab = seg_tables<DecodeArgs>(seg);
+            if (CODEC == EC_CODEC_QLC) sm.tabv[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
+            if (CODEC == EC_CODEC_HUFFMAN) {
+#pragma unroll
+                for (int k = 0; k < (int)kTableVec / kThreads; ++k)
+                    sm.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
+            }
+            if (CODEC == EC_CODEC_EXP_GOLOMB) symtab[tid] = tab->sym[tid];
+            const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
+            status = a.status ? a.status + seg : nullptr;
+            if (tid == 0) {
+                const uint64_t *h = reinterpret_cast<const uint64_t *>(stream);
+                const uint64_t h0 = h[0], n = h[1], h2 = h[2], po = h[3], pb = h[4], id = h[5];
+                const uint32_t magic = (uint32_t)h0, version = (uint32_t)(h0 >> 32) & 0xffffu;
+                const uint32_t codec = (uint32_t)(h0 >> 48) & 0xffu, flags = (uint32_t)(h0 >> 56);
+                const uint32_t C = (uint32_t)h2, nch = (uint32_t)(h2 >> 32);
+                uint32_t bits = 0;
+                if (magic != kMagic || version != kVersion || (flags & ~1u)) {
+                    bits = EC_S_BAD_HEADER;
+                } else if (codec != tab->codec || id != tab->codebook_id) {
+                    bits = EC_S_CODEBOOK_MISMATCH;
+                } else if (n != a.seg_n || C == 0 || (C % kSub) || C > kMaxChunk ||
+                           (uint64_t)nch != (n + C - 1) / C) {
+                    bits = EC_S_BAD_HEADER;
+                } else {
+                    uint64_t end =
+                        kHeaderBytes + 8ull * (nch + 1) + 4ull * nch * (C / kSub) + ((flags & 1) ? 256 : 0);
+                    end = (end + 255) / 256 * 256;
+                    if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
+                        bits = EC_S_BAD_HEADER;
+                }
+                sm.ok = bits == 0;
+                if (bits && bx == 0) or_status(status, bits);
+                sm.nch = nch;
+                sm.spc = C / kSub;
+                sm.po = po;
+                sm.pb = pb;
+            }
+            __syncthreads();
+            cur_seg = seg;
+            si.stream = stream;
+            si.po = sm.po;
+            si.pb = sm.pb;
+            si.nch = sm.nch;
+            si.spc = sm.spc;
+            have_cur = have_next_raw = false;
+        }
+        if (!sm.ok) continue;   // uniform over the workgroup
+
+        const uint32_t g0 = bx * kThreads + wave * 64;   // the wave's first sub-chunk
+        const bool wave_busy = g0 < a.blocks_per_seg;
+        // the wave's next task, if it is in the same stream
+        const uint32_t t1 = t + gridDim.x;
+        const bool next_same = t1 < n_tasks && t1 / gx == seg;
+        const uint32_t g0n = (t1 - seg * gx) * kThreads + wave * 64;
+        const bool next_busy = next_same && g0n < a.blocks_per_seg;
+
+        if (wave_busy) {
+            if (!have_cur) {   // nothing prefetched: load this task's index and span now
+                const IndexRaw r = issue_index(a, si, g0, lane);
+                cur = resolve<kSpan>(a, si, r, g0, lane, status);
+                if constexpr (kPrefetch) issue_span<kSpanVec>(si, cur, lane, span_regs);
+            }
+            if (kPrefetch && next_busy && !have_next_raw) next_raw = issue_index(a, si, g0n, lane);
+            // stage the span: region block 0 is zero (its last word is the
+            // guard before the span), the span follows from block 1, and a
+            // zero block closes it
+            if (cur.fits) {
+                if constexpr (kPrefetch) {
+                    static_for<0, kSpanVec>([&](auto kc) __attribute__((always_inline)) {
+                        constexpr int k = decltype(kc)::value;
+                        if (lane + 64u * k < cur.nblk) region[1 + lane + 64 * k] = span_regs[k];
+                    });
+                } else {
+                    // coalesced copy, four 1 KiB loads in flight per pass
+                    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + (cur.span_lo >> 4);
+                    const uint32_t nblk = cur.nblk;
+                    for (uint32_t i = lane; i < nblk; i += 256) {
+                        const uint32_t last = nblk - 1;
+                        const uint4 v0 = src[min(i, last)], v1 = src[min(i + 64, last)];
+                        const uint4 v2 = src[min(i + 128, last)], v3 = src[min(i + 192, last)];
+                        region[1 + i] = v0;
+                        if (i + 64 < nblk) region[1 + i + 64] = v1;
+                        if (i + 128 < nblk) region[1 + i + 128] = v2;
+                        if (i + 192 < nblk) region[1 + i + 192] = v3;
+                    }
+                }
+                if (lane == 0) region[0] = make_uint4(0u, 0u, 0u, 0u);
+                if (lane == 1) region[1 + cur.nblk] = make_uint4(0u, 0u, 0u, 0u);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const Plan p = cur;
+            // prefetch: the next task's span, and the index entries of the one after
+            if (kPrefetch && next_busy) {
+                cur = resolve<kSpan>(a, si, next_raw, g0n, lane, status);
+                if constexpr (kPrefetch) issue_span<kSpanVec>(si, cur, lane, span_regs);
+                have_cur = true;
+                const uint32_t t2 = t1 + gridDim.x;
+                const uint32_t g0nn = (t2 - seg * gx) * kThreads + wave * 64;
+                have_next_raw = t2 < n_tasks && t2 / gx == seg && g0nn < a.blocks_per_seg;
+                if (have_next_raw) next_raw = issue_index(a, si, g0nn, lane);
+            } else {
+                have_cur = have_next_raw = false;
+            }
+
+            uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + p.first_sym;
+            const uint32_t lens = tab->qlc_lens;
+            const uint32_t k_eg = (uint32_t)tab->eg_k;
+            uint32_t bad = 0;
+            uint64_t end_pos = 0, want_pos = 0;
+            if (p.fits) {
+                if (p.ok) {
+                    SpanBits S;
+                    S.base = region_base;
+                    S.x = S.base + (uint32_t)((p.co0 - p.span_lo) * 8 + p.e_start) - 1u;
+                    bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, tab, lens, k_eg);
+                    end_pos = S.bit();
+                    want_pos = (p.co0 - p.span_lo) * 8 + p.e_end;
+                }
+            } else if (p.ok) {
+                GlobalBits S;
+                S.init(reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb >> 2, p.co0 * 8 + p.e_start);
+                bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, tab, lens, k_eg);
+                end_pos = S.bit();
+                want_pos = p.co0 * 8 + p.e_end;
+            }
+            if (p.ok && ((bad & ~0xffu) || end_pos != want_pos)) or_status(status, EC_S_CORRUPT);
+            // the region is rewritten at the next task: all lanes' reads first
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         } else {
-            uint64_t end = kHeaderBytes + 8ull * (nch + 1) + 4ull * nch * (C / kSub) + ((flags & 1) ? 256 : 0);
-            end = (end + 255) / 256 * 256;
-            if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
-                bits = EC_S_BAD_HEADER;
+            have_cur = have_next_raw = false;
         }
-        sm.ok = bits == 0;
-        if (bits && blockIdx.x == 0) or_status(status, bits);
-        sm.nch = nch;
-        sm.spc = C / kSub;
-        sm.po = po;
-        sm.pb = pb;
     }
-    __syncthreads();
-    if (!sm.ok) return;
+}
 
-    // this lane's run and its place in the index
-    const uint32_t g0 = blockIdx.x * kThreads + wave * 64;   // the wave's first run
-    if (g0 >= a.blocks_per_seg) return;                      // whole wave idle
-    const uint32_t g = g0 + lane;
-    const bool active = g < a.blocks_per_seg;
-    const uint32_t spc = sm.spc;
-    const uint64_t pb = sm.pb;
-    const uint64_t *chunk_off = reinterpret_cast<const uint64_t *>(stream + kHeaderBytes);
-    const uint32_t *sub_end = reinterpret_cast<const uint32_t *>(stream + kHeaderBytes + 8ull * (sm.nch + 1));
-    const uint32_t gl = active ? g : a.blocks_per_seg - 1;
-    const uint32_t c = gl / spc, j = gl - c * spc;
-    const uint64_t co0 = chunk_off[c], co1 = chunk_off[c + 1];
-    const uint32_t e_end = sub_end[(uint64_t)c * spc + j];
-    const uint32_t e_start = j ? sub_end[(uint64_t)c * spc + j - 1] : 0u;
-    const bool ok = active && co0 <= co1 && co1 <= pb && !(co0 & 15) && (uint64_t)e_end <= (co1 - co0) * 8 &&
-                    e_start <= e_end;
-    if (active && !ok) or_status(status, EC_S_CORRUPT);
-
-    // the wave's span: from the first lane's chunk start to the last lane's chunk end
-    const uint32_t g_last = (g0 + 63 < a.blocks_per_seg ? g0 + 63 : a.blocks_per_seg - 1);
-    const uint64_t span_lo = chunk_off[g0 / spc] & ~15ull;
-    const uint64_t span_hi = chunk_off[g_last / spc + 1];
-    bool fits = span_lo <= span_hi && span_hi <= pb && span_hi - span_lo <= kSpan;
-    fits = fits && __ballot(ok && (co0 < span_lo || co1 > span_hi)) == 0;
-
-    const uint64_t first_sym = (uint64_t)g * kSub;
-    const uint32_t cnt = !active ? 0u
-                         : (a.seg_n - first_sym < kSub ? (uint32_t)(a.seg_n - first_sym) : (uint32_t)kSub);
-    uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + first_sym;
-    const uint32_t lens = tab->qlc_lens;
-    const uint32_t k_eg = (uint32_t)tab->eg_k;
-    const uint4 *payload = reinterpret_cast<const uint4 *>(stream + sm.po);
-    uint32_t bad = 0;
-    uint64_t end_pos = 0, want_pos = 0;
-
-    if (fits) {
-        // coalesced copy of the span into this wave's LDS region: region
-        // block 0 is zero (its last word is the guard before the span), the
-        // span follows from block 1, and a zero block closes it
-        uint4 *region = sm.spans[wave];
-        const uint32_t nblk = (uint32_t)((span_hi - span_lo + 15) >> 4);
-        const uint4 *src = payload + (span_lo >> 4);
-        for (uint32_t i = lane; i < nblk; i += 256) {   // four 1 KiB loads in flight per pass
-            const uint32_t last = nblk - 1;
-            const uint4 v0 = src[min(i, last)], v1 = src[min(i + 64, last)];
-            const uint4 v2 = src[min(i + 128, last)], v3 = src[min(i + 192, last)];
-            region[1 + i] = v0;
-            if (i + 64 < nblk) region[1 + i + 64] = v1;
-            if (i + 128 < nblk) region[1 + i + 128] = v2;
-            if (i + 192 < nblk) region[1 + i + 192] = v3;
-        }
-        if (lane == 0) region[0] = make_uint4(0u, 0u, 0u, 0u);
-        if (lane == 1) region[1 + nblk] = make_uint4(0u, 0u, 0u, 0u);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (ok) {
-            SpanBits S;
-            // word 3 of the region is the guard word right before the span
-            S.base = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint4 *)region * 8 + 4 * 32;
-            S.x = S.base + (uint32_t)((co0 - span_lo) * 8 + e_start) - 1u;
-            bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, symtab, tab, lens, k_eg);
-            end_pos = S.bit();
-            want_pos = (co0 - span_lo) * 8 + e_end;
-        }
-    } else if (ok) {
-        GlobalBits S;
-        S.init(reinterpret_cast<const uint32_t *>(payload), pb >> 2, co0 * 8 + e_start);
-        bad = decode_run<CODEC, PAIRS>(S, cnt, dst, l1, symtab, tab, lens, k_eg);
-        end_pos = S.bit();
-        want_pos = co0 * 8 + e_end;
-    }
-    if (ok && ((bad & ~0xffu) || end_pos != want_pos)) or_status(status, EC_S_CORRUPT);
+// Workgroups of a persistent launch: as many as can be resident at once,
+// never more than there are tasks.
+template <class K>
+hipError_t decode_grid(K kernel, uint32_t n_tasks, uint32_t *grid) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+    if (e != hipSuccess) return e;
+    const uint64_t g = (uint64_t)(per_cu > 0 ? per_cu : 1) * (uint64_t)(cus > 0 ? cus : 1);
+    *grid = g < n_tasks ? (uint32_t)g : n_tasks;
+    return hipSuccess;
 }
 
 template <int CODEC, int PAIRS>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
     uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads;
     if (gx == 0) gx = 1;   // still validate the header
-    hipLaunchKernelGGL((decode_kernel<CODEC, PAIRS>), dim3(gx, a.n_seg), dim3(kThreads), 0, s, a);
+    uint32_t grid = 0;
+    const hipError_t e = decode_grid(decode_kernel<CODEC, PAIRS>, gx * a.n_seg, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_kernel<CODEC, PAIRS>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
