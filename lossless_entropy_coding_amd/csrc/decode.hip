@@ -113,16 +113,24 @@ struct GlobalBits {
     __device__ __forceinline__ uint64_t bit() const { return (base0 + nxt) * 32 - nb; }
 };
 
-// Huffman code longer than the decode table's 13 bits (rare): canonical
-// limit search on a 40-bit left-justified window.  Returns symbol | length << 8.
-__device__ __noinline__ uint32_t huff_deep(uint64_t window, const DevTables *tab) {
+// Canonical-code tables for Huffman codes longer than the decode table's 13
+// bits, copied to LDS (lengths 14..40).
+struct DeepTables {
+    uint64_t limit[EC_MAX_CODE_LEN - kHuffBits];        // 40-bit left-justified end of the codes of length l
+    uint64_t first_code[EC_MAX_CODE_LEN - kHuffBits];   // canonical first code of length l
+    uint32_t first_idx[EC_MAX_CODE_LEN - kHuffBits];    // its position in the canonical symbol order
+};
+
+// Huffman code longer than 13 bits (rare): canonical limit search on a
+// 40-bit left-justified window.  Returns symbol | length << 8.
+__device__ __noinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt, const uint8_t *sym, uint32_t mx) {
     const uint64_t w40 = window >> (64 - EC_MAX_CODE_LEN);
     uint32_t l = kHuffBits + 1;
-    const uint32_t mx = tab->max_len;
-    while (l < mx && w40 >= tab->limit[l]) ++l;
+    while (l < mx && w40 >= dt->limit[l - kHuffBits - 1]) ++l;
+    const uint32_t i = l - kHuffBits - 1;
     const uint64_t code = w40 >> (EC_MAX_CODE_LEN - l);
-    const uint32_t idx = tab->first_idx[l] + (uint32_t)(code - tab->first_code[l]);
-    return tab->sym[idx & 255] | (l << 8);
+    const uint32_t idx = dt->first_idx[i] + (uint32_t)(code - dt->first_code[i]);
+    return sym[idx & 255] | (l << 8);
 }
 
 // Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
@@ -130,8 +138,8 @@ __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DevTables *tab
 // codeword" flags (bit 8 and up).
 template <int CODEC, int PAIRS, class Src>
 __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *dst, const uint16_t *l1,
-                                               const uint8_t *symtab, const DevTables *tab, uint32_t lens,
-                                               uint32_t k_eg) {
+                                               const uint8_t *symtab, const DeepTables *dt, uint32_t max_len,
+                                               uint32_t lens, uint32_t k_eg) {
     uint32_t bad = 0;
     // The code that starts window w: its table entry (symbol in byte 0; for
     // QLC bit 8 flags an unused suffix) and its length.  QLC takes the length
@@ -145,7 +153,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             return Code{l1[w >> 21], (lens >> ((w >> 29) << 2)) & 15u};
         } else if (CODEC == EC_CODEC_HUFFMAN) {
             uint32_t e = l1[w >> (32 - kHuffBits)];
-            if (e < 256u) e = huff_deep(S.win64(), tab);
+            if (e < 256u) e = huff_deep(S.win64(), dt, symtab, max_len);
             return Code{e, e >> 8};
         } else {
             const uint32_t zr = __clz(w);
@@ -173,7 +181,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             S.adv(c1.len);
             const uint32_t w2 = c1.len <= 32u - kHuffBits ? w << c1.len : S.win();
             c2.e = l1[w2 >> (32 - kHuffBits)];
-            if (c2.e < 256u) c2.e = huff_deep(S.win64(), tab);
+            if (c2.e < 256u) c2.e = huff_deep(S.win64(), dt, symtab, max_len);
             S.adv(c2.e >> 8);
         } else {
             c2 = code_at(w << c1.len);
@@ -328,7 +336,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     // tables first, so that their addresses fit the LDS instructions' offset field
     struct Smem {
         uint4 tabv[kTableVec];
-        uint8_t symtab[256];
+        uint8_t symtab[256];       // EG: rank -> byte; Huffman: canonical order -> byte
+        DeepTables deep[1];        // Huffman only
         uint64_t po, pb;
         uint32_t ok, nch, spc;
         uint32_t pad_;
@@ -368,7 +377,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                 for (int k = 0; k < (int)kTableVec / kThreads; ++k)
                     sm.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
             }
-            if (CODEC == EC_CODEC_EXP_GOLOMB) symtab[tid] = tab->sym[tid];
+            if (CODEC != EC_CODEC_QLC) symtab[tid] = tab->sym[tid];
+            if constexpr (CODEC == EC_CODEC_HUFFMAN) {
+                constexpr uint32_t kDeep = EC_MAX_CODE_LEN - kHuffBits;
+                if (tid < kDeep) {
+                    sm.deep[0].limit[tid] = tab->limit[kHuffBits + 1 + tid];
+                    sm.deep[0].first_code[tid] = tab->first_code[kHuffBits + 1 + tid];
+                    sm.deep[0].first_idx[tid] = tab->first_idx[kHuffBits + 1 + tid];
+                }
+            }
             const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
             status = a.status ? a.status + seg : nullptr;
             if (tid == 0) {
@@ -478,14 +495,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                     SpanBits S;
                     S.base = region_base;
                     S.x = S.base + (uint32_t)((p.co0 - p.span_lo) * 8 + p.e_start) - 1u;
-                    bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, tab, lens, k_eg);
+                    bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, sm.deep, tab->max_len, lens, k_eg);
                     end_pos = S.bit();
                     want_pos = (p.co0 - p.span_lo) * 8 + p.e_end;
                 }
             } else if (p.ok) {
                 GlobalBits S;
                 S.init(reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb >> 2, p.co0 * 8 + p.e_start);
-                bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, tab, lens, k_eg);
+                bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, sm.deep, tab->max_len, lens, k_eg);
                 end_pos = S.bit();
                 want_pos = p.co0 * 8 + p.e_end;
             }

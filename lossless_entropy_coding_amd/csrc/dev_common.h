@@ -69,6 +69,7 @@ struct EncodeArgs {
     uint32_t sub_at;          // byte offset of sub_end[] in a stream
     uint32_t embed_lengths;
     uint32_t max_len;         // longest code over the launch's codebooks
+    uint32_t stage_bytes;     // LDS stage of the staged packer (set at launch)
     const DevTables *tabs[EC_MAX_BATCH];
 };
 

@@ -261,102 +261,103 @@ __device__ __forceinline__ uint64_t chunk_dst(const EncodeArgs &a, const ChunkPo
     return end > a.out_cap ? ~0ull : (uint64_t)a.payload_offset + off;
 }
 
-// Staged packing, for chunks of up to 4 rows (16384 symbols) of codes up to
-// 26 bits whose packed bits fit in LDS: every 32-bit LUT entry is read once
-// and kept in registers as a left-aligned code (pairs joined when codes are
-// at most 16 bits) with its length byte packed four to a register.
+// Staged packing, for chunks of up to 4 rows (16384 symbols) and codes of up
+// to 26 bits.  Every 32-bit LUT entry (code left-aligned, length in the low
+// 6 bits) is read once; each pair of codes is kept in registers as one
+// left-aligned code with its length byte, four lengths to a register.  A
+// piece with a pair longer than 32 bits (it needs a code of more than 16
+// bits: rare for Huffman codebooks, impossible for QLC) is placed code by
+// code from its bytes instead.  The whole chunk is packed
+// into an LDS stage of at most kStageCap bytes; a chunk that does not fit
+// (codes far longer than the codebook's typical ones) is left to the
+// row-by-row packer, launched after this one when the cap can bind.
 
-enum { kModePairs = 0, kModeSingles = 1 };
+constexpr uint32_t kStageCap = 28 * 1024;   // LDS stage of the staged packer
 
-template <int ROWS, int MODE>
-struct CodeCache {
-    static constexpr int kUnits = MODE == kModePairs ? kPiece / 2 : kPiece;   // codes placed per piece
-    uint32_t c[ROWS][kUnits];          // left-aligned codes
-    uint32_t pk[ROWS][kUnits / 4];     // code lengths, one byte each
+template <int ROWS>
+struct PairCache {
+    uint32_t c[ROWS][kPiece / 2];     // pair codes, left-aligned (exact when the pair has <= 32 bits)
+    uint32_t pk[ROWS][kPiece / 8];    // pair lengths (up to 52), one byte each
 };
 
-// Pass 1 over row r: cache codes and lengths; returns the piece's bit length.
-// All 16 bytes are looked up; bytes past the end of a piece are cleared
-// afterwards by clear_tail.
-template <int MODE, class Cache>
-__device__ __forceinline__ uint32_t cache_row(Cache &cc, int r, const uint4 &v, const uint32_t *lut32) {
-    constexpr int U = Cache::kUnits;
-    uint32_t pk[U / 4];
-#pragma unroll
-    for (int i = 0; i < U / 4; ++i) pk[i] = 0;
-    if (MODE == kModePairs) {
-        static_for<0, U>([&](auto pc) __attribute__((always_inline)) {
-            constexpr int p = decltype(pc)::value;
-            const uint32_t e1 = lut32[byte_k<2 * p>(v)], e2 = lut32[byte_k<2 * p + 1>(v)];
-            // first code's length is at most 16: e1 & 31 is it exactly
-            cc.c[r][p] = (e1 & ~0xffu) | ((e2 & ~0xffu) >> (e1 & 31u));
-            pk[p >> 2] |= ((e1 + e2) & 0xffu) << (8 * (p & 3));
-        });
-    } else {
-        // codes of up to 26 bits: the length sits in the low 6 bits
-        static_for<0, U>([&](auto kc) __attribute__((always_inline)) {
-            constexpr int k = decltype(kc)::value;
-            const uint32_t e = lut32[byte_k<k>(v)];
-            cc.c[r][k] = e & ~63u;
-            pk[k >> 2] |= (e & 63u) << (8 * (k & 3));
-        });
-    }
-    uint32_t len = 0;
-#pragma unroll
-    for (int i = 0; i < U / 4; ++i) {
-        cc.pk[r][i] = pk[i];
-        len = __builtin_amdgcn_sad_u8(pk[i], 0u, len);
-    }
-    return len;
+// Pass 1 over row r: cache the pairs; returns the piece's bit length and
+// sets wide when a pair exceeds 32 bits.  All 16 bytes are looked up; bytes
+// past the end of a piece are cleared afterwards by clear_tail.
+template <int ROWS>
+__device__ __forceinline__ uint32_t cache_row(PairCache<ROWS> &cc, int r, const uint4 &v, const uint32_t *lut32,
+                                              bool &wide) {
+    uint32_t pk[2] = {0, 0}, mx = 0;
+    static_for<0, kPiece / 2>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int p = decltype(pc)::value;
+        const uint32_t e1 = lut32[byte_k<2 * p>(v)], e2 = lut32[byte_k<2 * p + 1>(v)];
+        const uint32_t l12 = (e1 & 63u) + (e2 & 63u);
+        // the first code has at most 26 bits: the shift takes e1's low 5 bits
+        cc.c[r][p] = (e1 & ~63u) | ((e2 & ~63u) >> (e1 & 31u));
+        pk[p >> 2] |= l12 << (8 * (p & 3));
+        mx = max(mx, l12);
+    });
+    cc.pk[r][0] = pk[0];
+    cc.pk[r][1] = pk[1];
+    wide = mx > 32u;
+    return __builtin_amdgcn_sad_u8(pk[0], 0u, __builtin_amdgcn_sad_u8(pk[1], 0u, 0u));
 }
 
 // Drop the symbols at and after byte vb of a piece (vb < 16) from row r's
 // cache; returns the piece's new bit length.
-template <int MODE, class Cache>
-__device__ __forceinline__ uint32_t clear_tail(Cache &cc, int r, const uint4 &v_in, uint32_t vb, const uint32_t *lut32) {
-    constexpr int U = Cache::kUnits;
+template <int ROWS>
+__device__ __forceinline__ uint32_t clear_tail(PairCache<ROWS> &cc, int r, const uint4 &v_in, uint32_t vb,
+                                               const uint32_t *lut32) {
     // Opaque copies: the compiler must not keep pass 1's table entries or
     // addresses alive for this rare path (it recomputes them here instead).
     uint4 v = v_in;
     asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
     asm volatile("" ::: "memory");
-    static_for<0, U>([&](auto uc) __attribute__((always_inline)) {
+    static_for<0, kPiece / 2>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         constexpr uint32_t sh = 8 * (u & 3);
-        if (MODE == kModePairs) {
-            if ((uint32_t)(2 * u + 1) >= vb) {   // the pair keeps at most its first code
-                const uint32_t e1 = (uint32_t)(2 * u) < vb ? lut32[byte_k<2 * u>(v)] : 0u;
-                cc.c[r][u] = e1 & ~0xffu;
-                cc.pk[r][u >> 2] = (cc.pk[r][u >> 2] & ~(0xffu << sh)) | ((e1 & 0xffu) << sh);
-            }
-        } else {
-            if ((uint32_t)u >= vb) {
-                cc.c[r][u] = 0;
-                cc.pk[r][u >> 2] &= ~(0xffu << sh);
-            }
+        if ((uint32_t)(2 * u + 1) >= vb) {   // the pair keeps at most its first code
+            const uint32_t e1 = (uint32_t)(2 * u) < vb ? lut32[byte_k<2 * u>(v)] : 0u;
+            cc.c[r][u] = e1 & ~63u;
+            cc.pk[r][u >> 2] = (cc.pk[r][u >> 2] & ~(0xffu << sh)) | ((e1 & 63u) << sh);
         }
     });
-    uint32_t len = 0;
-#pragma unroll
-    for (int i = 0; i < U / 4; ++i) len = __builtin_amdgcn_sad_u8(cc.pk[r][i], 0u, len);
-    return len;
+    return __builtin_amdgcn_sad_u8(cc.pk[r][0], 0u, __builtin_amdgcn_sad_u8(cc.pk[r][1], 0u, 0u));
 }
 
-// Pass 2 over row r: OR the cached codes into LDS from absolute bit address
-// pos (the buffer's byte address is a multiple of 16, so word boundaries of
-// the buffer and of the absolute address coincide).
-template <class Cache>
-__device__ __forceinline__ void emit_row(const Cache &cc, int r, uint32_t pos) {
-    constexpr int U = Cache::kUnits;
-    static_for<0, U>([&](auto uc) __attribute__((always_inline)) {
-        constexpr int u = decltype(uc)::value;
-        or_code32_at(pos, cc.c[r][u]);
-        pos += (cc.pk[r][u >> 2] >> (8 * (u & 3))) & 0xffu;
-    });
+// Pass 2 over row r: OR the piece's codes into LDS from absolute bit address
+// pos (the stage's byte address is a multiple of 16, so word boundaries of
+// the stage and of the absolute address coincide).  A wide piece is placed
+// code by code from its vb bytes, read again from the input (rare, and
+// cheaper than keeping every piece's bytes in registers).
+template <int ROWS, bool WIDE>
+__device__ __forceinline__ void emit_row(const PairCache<ROWS> &cc, int r, uint32_t pos, bool wide,
+                                         const uint8_t *piece, uint32_t vb, const uint32_t *lut32) {
+    if (!WIDE || !wide) {
+        static_for<0, kPiece / 2>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            or_code32_at(pos, cc.c[r][u]);
+            pos += (cc.pk[r][u >> 2] >> (8 * (u & 3))) & 0xffu;
+        });
+    } else {
+        const uint4 v = *reinterpret_cast<const uint4 *>(piece);
+        static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            const uint32_t e = (uint32_t)k < vb ? lut32[byte_k<k>(v)] : 0u;
+            or_code32_at(pos, e & ~63u);
+            pos += e & 63u;
+        });
+    }
 }
 
-template <int ROWS, int MODE>
-__device__ __forceinline__ void encode_pack_staged(const EncodeArgs &a) {
+// A chunk fits the staged packer when its 16-byte groups plus the spare
+// group the two-word ORs may touch fit the stage.
+__device__ __forceinline__ bool fits_stage(const EncodeArgs &a, uint32_t units) {
+    return units + 1 <= a.stage_bytes / 16;
+}
+
+// WIDE: the codebook has codes of more than 16 bits, so a pair can exceed 32.
+template <int ROWS, bool WIDE>
+__global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const EncodeArgs a) {
     extern __shared__ uint4 stage4[];
     __shared__ uint32_t lut32[256];
     __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
@@ -367,49 +368,40 @@ __device__ __forceinline__ void encode_pack_staged(const EncodeArgs &a) {
     uint32_t vb[ROWS];
     load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
     lut32[tid] = seg_tables<EncodeArgs>(p.seg)->enc32[tid];
-    // zero the chunk buffer (worst-case chunk plus the spare group the
-    // two-word ORs may touch) while the loads are in flight
-    const uint32_t stage_groups = (a.chunk_symbols * a.max_len + 127) / 128 + 1;
-    for (uint32_t i = tid; i < stage_groups; i += kThreads) stage4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
-    CodeCache<ROWS, MODE> cc;
+    PairCache<ROWS> cc;
     uint32_t plen[ROWS];
+    bool wide[ROWS];
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        plen[r] = cache_row<MODE>(cc, r, v[r], lut32);
+        plen[r] = cache_row<ROWS>(cc, r, v[r], lut32, wide[r]);
     });
     if (p.cn != (uint32_t)(ROWS * kRowSyms)) {   // the segment's last chunk: drop missing symbols
         static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
-            if (vb[r] < (uint32_t)kPiece) plen[r] = clear_tail<MODE>(cc, r, v[r], vb[r], lut32);
+            if (vb[r] < (uint32_t)kPiece) plen[r] = clear_tail<ROWS>(cc, r, v[r], vb[r], lut32);
         });
     }
     uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
     const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
     const uint32_t units = (chunk_bits + 127) >> 7;
+    const uint64_t dst_at = chunk_dst(a, p, units);
+    // uniform over the workgroup: chunks that do not fit are packed by the
+    // row-by-row kernel that follows
+    if (dst_at == ~0ull || !fits_stage(a, units)) return;
 
+    for (uint32_t i = tid; i < units + 1; i += kThreads) stage4[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
     const uint32_t base_bit = lds_addr(stage4) * 8;
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        emit_row(cc, r, base_bit + excl[r]);
+        emit_row<ROWS, WIDE>(cc, r, base_bit + excl[r], wide[r], p.src + (uint32_t)(r * kThreads + tid) * kPiece,
+                             vb[r], lut32);
     });
-    const uint64_t dst_at = chunk_dst(a, p, units);
     __syncthreads();
-    if (dst_at == ~0ull) return;
     uint4 *dst = reinterpret_cast<uint4 *>(p.out + dst_at);
     for (uint32_t i = tid; i < units; i += kThreads) dst[i] = stage4[i];
-}
-
-// Pair mode keeps 40 cached registers per thread: held to 128 VGPRs so that
-// four workgroups fit on a CU.  Single-code mode is bounded by its LDS stage.
-template <int ROWS>
-__global__ __launch_bounds__(kThreads, 4) void encode_pack_pairs_kernel(const EncodeArgs a) {
-    encode_pack_staged<ROWS, kModePairs>(a);
-}
-template <int ROWS>
-__global__ __launch_bounds__(kThreads) void encode_pack_singles_kernel(const EncodeArgs a) {
-    encode_pack_staged<ROWS, kModeSingles>(a);
 }
 
 // Row-by-row packing, any chunk size and code length up to 40 bits: each
@@ -422,6 +414,8 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
     __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // after the staged packer: only the chunks it left
+    if (a.stage_bytes && fits_stage(a, a.sizes[blockIdx.x])) return;
     const ChunkPos p = chunk_pos(a, blockIdx.x);
     uint4 v[ROWS];
     uint32_t vb[ROWS];
@@ -478,29 +472,33 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
 // ---------------------------------------------------------------- launches
 
 template <int ROWS>
-hipError_t launch_chunks(const EncodeArgs &a, uint32_t n_chunks, uint32_t stage, bool staged, hipStream_t s) {
+hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t s) {
+    EncodeArgs a = a_in;
     hipLaunchKernelGGL((encode_sizes_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), 0, s, a);
     hipLaunchKernelGGL(encode_offsets_kernel, dim3(a.n_seg), dim3(kScanThreads), 0, s, a);
-    bool done = false;
+    // row buffer of the row-by-row packer: one row's bits plus the carried
+    // word, the final padding and the spare words the three-word ORs may touch
+    const uint32_t rows_lds = (kRowSyms * a.max_len / 32 + 8) * 4;
+    bool all_staged = false;
+    a.stage_bytes = 0;
     if constexpr (ROWS <= 4) {
-        if (staged) {
-            if (a.max_len <= 16)
-                hipLaunchKernelGGL((encode_pack_pairs_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), stage, s, a);
+        if (a.max_len <= (uint32_t)kNarrowMaxLen) {
+            // stage: the worst-case chunk plus a spare group, capped
+            const uint32_t worst = ((a.chunk_symbols * a.max_len + 127) / 128 + 1) * 16;
+            a.stage_bytes = worst < kStageCap ? worst : kStageCap;
+            all_staged = worst <= kStageCap;
+            if (a.max_len > 16)
+                hipLaunchKernelGGL((encode_pack_staged_kernel<ROWS, true>), dim3(n_chunks), dim3(kThreads),
+                                   a.stage_bytes, s, a);
             else
-                hipLaunchKernelGGL((encode_pack_singles_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), stage, s, a);
-            done = true;
+                hipLaunchKernelGGL((encode_pack_staged_kernel<ROWS, false>), dim3(n_chunks), dim3(kThreads),
+                                   a.stage_bytes, s, a);
         }
     }
-    if (!done) {
-        // row buffer: one row's bits plus the carried word, the final
-        // padding and the spare words the three-word ORs may touch
-        const uint32_t lds = (kRowSyms * a.max_len / 32 + 8) * 4;
-        hipLaunchKernelGGL((encode_pack_rows_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), lds, s, a);
-    }
+    if (!all_staged)
+        hipLaunchKernelGGL((encode_pack_rows_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), rows_lds, s, a);
     return hipGetLastError();
 }
-
-constexpr uint32_t kStageBudget = 60 * 1024;   // dynamic LDS of the staged packer
 
 }  // namespace
 
@@ -511,13 +509,11 @@ hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
         return hipGetLastError();
     }
     const uint32_t rows = (a.chunk_symbols + kRowSyms - 1) / kRowSyms;
-    const uint32_t stage = ((a.chunk_symbols * a.max_len + 127) / 128 + 1) * 16;
-    const bool staged = rows <= 4 && a.max_len <= (uint32_t)kNarrowMaxLen && stage <= kStageBudget;
-    if (rows <= 1) return launch_chunks<1>(a, n_chunks, stage, staged, s);
-    if (rows <= 2) return launch_chunks<2>(a, n_chunks, stage, staged, s);
-    if (rows <= 4) return launch_chunks<4>(a, n_chunks, stage, staged, s);
-    if (rows <= 8) return launch_chunks<8>(a, n_chunks, stage, false, s);
-    return launch_chunks<16>(a, n_chunks, stage, false, s);
+    if (rows <= 1) return launch_chunks<1>(a, n_chunks, s);
+    if (rows <= 2) return launch_chunks<2>(a, n_chunks, s);
+    if (rows <= 4) return launch_chunks<4>(a, n_chunks, s);
+    if (rows <= 8) return launch_chunks<8>(a, n_chunks, s);
+    return launch_chunks<16>(a, n_chunks, s);
 }
 
 }  // namespace ec

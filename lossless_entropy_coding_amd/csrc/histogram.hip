@@ -158,20 +158,39 @@ __device__ float kl_phi(float d) {
     return (1.f + d) * log1pf(d) - d;
 }
 
+// Sum of a 64-bit value over the 256 threads of a workgroup: DPP-free wave
+// reduction with cross-lane adds, then the four wave totals through LDS.
+__device__ __forceinline__ uint64_t wg_sum_u64(uint64_t v, uint64_t *w4) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((threadIdx.x & 63) == 0) w4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return w4[0] + w4[1] + w4[2] + w4[3];
+}
+__device__ __forceinline__ float wg_sum_f32(float v, float *w4) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((threadIdx.x & 63) == 0) w4[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (w4[0] + w4[1]) + (w4[2] + w4[3]);
+}
+
 // One workgroup per row: D(P_row || Q) = sum_b Q_b phi(P_b / Q_b - 1) / ln 2,
 // which equals sum P log2(P / Q) because both distributions sum to one.
 // d = (p Nq - q Np) / (q Np) comes from exact integer products.
 __global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict__ pc, uint32_t n_seg,
                                                      const uint64_t *__restrict__ qc, uint32_t q_add,
                                                      float *__restrict__ kl) {
-    __shared__ uint64_t scratch[256];
-    __shared__ float fs[256];
+    __shared__ uint64_t w_np[4], w_nq[4];
+    __shared__ float w_t[4];
+    __shared__ int any_inf;
     const uint32_t b = threadIdx.x;
     const uint32_t row = blockIdx.x;
+    if (b == 0) any_inf = 0;
     const uint64_t p = pc[(uint64_t)row * 256 + b];
     const uint64_t q = qc[b] + q_add;
-    const uint64_t np = block_sum_u64(p, scratch);
-    const uint64_t nq = block_sum_u64(q, scratch);
+    const uint64_t np = wg_sum_u64(p, w_np);
+    const uint64_t nq = wg_sum_u64(q, w_nq);
     float term;
     bool inf = false;
     if (np == 0) {
@@ -193,16 +212,9 @@ __global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict_
         }
         term = ((float)q / (float)nq) * kl_phi(d);
     }
-    fs[b] = term;
-    __shared__ int any_inf;
-    if (b == 0) any_inf = 0;
-    __syncthreads();
     if (inf) any_inf = 1;
-    for (uint32_t s = 128; s > 0; s >>= 1) {
-        if (b < s) fs[b] += fs[b + s];
-        __syncthreads();
-    }
-    if (b == 0) kl[row] = any_inf ? __builtin_inff() : fs[0] * 1.4426950408889634f;  // 1 / ln 2
+    const float sum = wg_sum_f32(term, w_t);
+    if (b == 0) kl[row] = any_inf ? __builtin_inff() : sum * 1.4426950408889634f;  // 1 / ln 2
 }
 
 }  // namespace
