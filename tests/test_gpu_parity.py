@@ -129,6 +129,27 @@ def test_deep_huffman_codes(ec, depth):
     assert dstatus == 0 and np.array_equal(y, x)
 
 
+@pytest.mark.parametrize("C", [4096, 16384, 65536])
+@pytest.mark.parametrize("depth", [20, 26, 27])
+def test_chunks_of_mixed_code_length(ec, C, depth):
+    """Chunks of short codes next to chunks of the deepest code: one launch
+    has chunks whose packed bits fit the encoder's LDS stage and chunks that
+    do not, and rows whose code pairs span more than 32 bits."""
+    counts = [int(c) for c in deep_counts(depth)]
+    cb, ocb = ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
+    assert ocb.max_len == depth
+    deepest, shortest = int(np.argmax(ocb.length)), int(np.argmin(ocb.length))
+    rng = np.random.default_rng(C + depth)
+    parts = [np.full(C, shortest), np.full(C, deepest), rng.integers(0, 256, C),
+             np.where(rng.random(C) < 0.5, deepest, shortest), np.full(C // 2 + 37, deepest)]
+    x = np.concatenate(parts).astype(np.uint8)
+    want = st.encode_stream(x, ocb, C)
+    got, status = _gpu_encode(ec, cb, x, C)
+    assert status == 0 and got == want
+    y, dstatus = _gpu_decode(ec, cb, want, x.size)
+    assert dstatus == 0 and np.array_equal(y, x)
+
+
 def test_encode_is_deterministic(ec):
     counts = _calib_counts()
     cb, _ = _pair(ec, "huffman", counts)
