@@ -1,13 +1,16 @@
 // Byte histogram and the PMF statistics kernels.
 //
 // Histogram, two launches:
-//   1. histogram_kernel: each workgroup counts a contiguous slice of one
-//      segment into LDS bins privatised per wave and per lane group (so the
-//      skewed e4m3 distributions, where a few bytes dominate, do not
-//      serialise the LDS atomics), then stores its 256 partial counts with
-//      plain stores;
+//   1. histogram_kernel: the workgroups of a segment sweep it together in
+//      rounds of 32 KiB per workgroup, counting into LDS counters; each then
+//      stores its 256 partial counts with plain stores.  Every wave owns 16 columns of 256 counters; lane l adds
+//      into column l & 15, so the counter of byte b is word 16 b + (l & 15):
+//      whatever bytes the 32 lanes of one LDS pass hold, at most two of them
+//      share a bank (random addresses into one shared table, and the skewed
+//      e4m3 distributions where a few bytes dominate, cost several times
+//      more);
 //   2. histogram_reduce_kernel: sums the partial rows of each segment into
-//      the 64-bit counts, a slice of 16 bins per workgroup.
+//      the 64-bit counts, one wave per bin.
 // No global atomics: same-address atomics from many workgroups serialise at
 // the memory side.
 #include "dev_common.h"
@@ -17,22 +20,23 @@ namespace ec {
 namespace {
 
 constexpr int kHistThreads = 256;
-constexpr int kHistCopies = 8;                 // LDS copies per wave (lane & 7)
-constexpr int kHistStride = 257;               // words per copy: copies of one bin fall in different banks
-constexpr int kHistVecPerThread = 16;          // 16-byte loads per thread per block (64 KiB per block)
-constexpr int kReduceBins = 2;                 // bins per reduce workgroup
-constexpr int kReduceGroups = 256 / kReduceBins;
+constexpr int kHistCols = 16;                          // counter columns per wave (lane & 15)
+constexpr int kHistWaveWords = 256 * kHistCols;        // 16 KiB of counters per wave
+constexpr int kHistRoundVec = 8;                       // 16-byte loads in flight per thread per round
+constexpr uint64_t kHistRound = (uint64_t)kHistRoundVec * kHistThreads;   // vectors per workgroup round
+constexpr int kHistRoundsPerBlock = 4;                 // target rounds per workgroup (128 KiB)
 
 __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
                                                                  uint64_t seg_n, uint64_t in_stride,
-                                                                 uint64_t vec_per_block,
                                                                  uint32_t *__restrict__ partial) {
-    constexpr int kCopies = kHistThreads / 64 * kHistCopies;
-    __shared__ uint32_t bins[kCopies * kHistStride];
-    const uint32_t tid = threadIdx.x;
-    uint32_t *mine = bins + ((tid >> 6) * kHistCopies + (tid & (kHistCopies - 1))) * kHistStride;
-    for (uint32_t i = tid; i < kCopies * kHistStride; i += kHistThreads) bins[i] = 0;
+    constexpr int kWaves = kHistThreads / 64;
+    __shared__ uint4 hv[kWaves * kHistWaveWords / 4];
+    uint32_t *h = reinterpret_cast<uint32_t *>(hv);
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (uint32_t i = tid; i < kWaves * kHistWaveWords / 4; i += kHistThreads) hv[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
+    // a word takes the bytes of 4 lanes of one workgroup: far below 2^32
+    uint32_t *mine = h + wave * kHistWaveWords + (lane & (kHistCols - 1));
 
     const uint32_t seg = blockIdx.y;
     const uint8_t *base = in + (uint64_t)seg * in_stride;
@@ -42,67 +46,78 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
     const uint8_t *vbase = base + head;
     const uint64_t n_vec = (seg_n - head) / 16;
     const uint64_t tail = (seg_n - head) % 16;
-    const uint64_t v0 = (uint64_t)blockIdx.x * vec_per_block;
-    const uint64_t v1 = v0 + vec_per_block < n_vec ? v0 + vec_per_block : n_vec;
     const uint4 *vp = reinterpret_cast<const uint4 *>(vbase);
     auto count = [&](const uint4 &q) __attribute__((always_inline)) {
         const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            atomicAdd(&mine[w[k] & 0xff], 1u);
-            atomicAdd(&mine[(w[k] >> 8) & 0xff], 1u);
-            atomicAdd(&mine[(w[k] >> 16) & 0xff], 1u);
-            atomicAdd(&mine[w[k] >> 24], 1u);
+            atomicAdd(&mine[(w[k] & 0xff) * kHistCols], 1u);
+            atomicAdd(&mine[((w[k] >> 8) & 0xff) * kHistCols], 1u);
+            atomicAdd(&mine[((w[k] >> 16) & 0xff) * kHistCols], 1u);
+            atomicAdd(&mine[(w[k] >> 24) * kHistCols], 1u);
         }
     };
-    // four vectors in flight per thread
-    uint64_t v = v0 + tid;
-    for (; v + 3 * kHistThreads < v1; v += 4 * kHistThreads) {
-        const uint4 q0 = vp[v], q1 = vp[v + kHistThreads], q2 = vp[v + 2 * kHistThreads], q3 = vp[v + 3 * kHistThreads];
-        count(q0);
-        count(q1);
-        count(q2);
-        count(q3);
+    // grid-stride rounds: at any time the workgroups of a segment read one
+    // contiguous window of it; every load of a round is issued before its
+    // first count, and each count waits for its own load only
+    for (uint64_t r0 = (uint64_t)blockIdx.x * kHistRound; r0 < n_vec; r0 += (uint64_t)gridDim.x * kHistRound) {
+        const uint64_t v = r0 + tid;
+        uint4 q[kHistRoundVec];
+        if (r0 + kHistRound <= n_vec) {
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) q[k] = vp[v + k * kHistThreads];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) count(q[k]);
+        } else {   // the segment's last, partial round
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) {
+                if (v + k * kHistThreads < n_vec) q[k] = vp[v + k * kHistThreads];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) {
+                if (v + k * kHistThreads < n_vec) count(q[k]);
+            }
+        }
     }
-    for (; v < v1; v += kHistThreads) count(vp[v]);
-    if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid]], 1u);
-    if (blockIdx.x == 0 && tid < tail) atomicAdd(&mine[vbase[n_vec * 16 + tid]], 1u);
+    if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid] * kHistCols], 1u);
+    if (blockIdx.x == 0 && tid < tail) atomicAdd(&mine[vbase[n_vec * 16 + tid] * kHistCols], 1u);
     __syncthreads();
 
+    // thread t sums byte t over all columns, starting at column t & 15 so
+    // that the lanes of one access spread over the banks
     uint32_t sum = 0;
 #pragma unroll
-    for (int c = 0; c < kCopies; ++c) sum += bins[c * kHistStride + tid];
-    partial[((uint64_t)seg * gridDim.x + blockIdx.x) * 256 + tid] = sum;
+    for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+        for (int j = 0; j < kHistCols; ++j) sum += h[w * kHistWaveWords + tid * kHistCols + ((j + tid) & (kHistCols - 1))];
+    }
+    partial[((uint64_t)seg * 256 + tid) * gridDim.x + blockIdx.x] = sum;   // bin-major rows
 }
 
-// Workgroup (j, seg) sums bins [2 j, 2 j + 2) of segment seg over its `rows`
-// partial rows: thread t takes bin t % 2 and every 128th row from t / 2
-// (eight loads in flight), then the 128 row groups are added in LDS.
-__global__ __launch_bounds__(256) void histogram_reduce_kernel(const uint32_t *__restrict__ partial, uint32_t rows,
-                                                               uint64_t *__restrict__ counts) {
-    __shared__ uint64_t acc[kReduceGroups][kReduceBins];
-    const uint32_t tid = threadIdx.x, b = tid % kReduceBins, g = tid / kReduceBins;
-    const uint32_t bin = blockIdx.x * kReduceBins + b;
-    const uint32_t *src = partial + (uint64_t)blockIdx.y * rows * 256 + bin;
-    uint64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-    uint32_t r = g;
-    for (; r + 7 * kReduceGroups < rows; r += 8 * kReduceGroups) {
+// Workgroup (bin, seg), one wave: lane l adds the partial counts of rows
+// l, l + 64, ... (contiguous in the bin-major layout, eight loads in
+// flight), then the wave adds its lanes.
+__global__ __launch_bounds__(64) void histogram_reduce_kernel(const uint32_t *__restrict__ partial, uint32_t rows,
+                                                              uint64_t *__restrict__ counts) {
+    const uint32_t l = threadIdx.x;
+    const uint64_t bin = (uint64_t)blockIdx.y * 256 + blockIdx.x;
+    const uint32_t *src = partial + bin * rows;
+    uint64_t s0 = 0, s1 = 0;
+    uint32_t r = l;
+    for (; r + 7 * 64 < rows; r += 8 * 64) {
         uint32_t x[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = src[(uint64_t)(r + k * kReduceGroups) * 256];
-        s0 += (uint64_t)x[0] + x[1];
-        s1 += (uint64_t)x[2] + x[3];
-        s2 += (uint64_t)x[4] + x[5];
-        s3 += (uint64_t)x[6] + x[7];
+        for (int k = 0; k < 8; ++k) x[k] = src[r + k * 64];
+        s0 += ((uint64_t)x[0] + x[1]) + ((uint64_t)x[2] + x[3]);
+        s1 += ((uint64_t)x[4] + x[5]) + ((uint64_t)x[6] + x[7]);
     }
-    for (; r < rows; r += kReduceGroups) s0 += src[(uint64_t)r * 256];
-    acc[g][b] = s0 + s1 + s2 + s3;
-    __syncthreads();
-    for (uint32_t h = kReduceGroups / 2; h > 0; h >>= 1) {
-        if (g < h) acc[g][b] += acc[g + h][b];
-        __syncthreads();
-    }
-    if (g == 0) counts[(uint64_t)blockIdx.y * 256 + bin] = acc[0][b];
+    for (; r < rows; r += 64) s0 += src[r];
+    uint64_t v = s0 + s1;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if (l == 0) counts[bin] = v;
 }
 
 // ------------------------------------------------------------ PMF average
@@ -219,12 +234,12 @@ __global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict_
 
 }  // namespace
 
-// Workgroups per segment: one per 4096 16-byte vectors, at most 65536 rows
-// of partial counts over all segments (but at least one per segment).
+// Workgroups per segment: one per kHistRoundsPerBlock rounds of the
+// segment, at most 65536 rows of partial counts over all segments (but at
+// least one per segment).
 uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
-    const uint64_t n_vec = seg_n / 16;
-    const uint64_t per_block = (uint64_t)kHistThreads * kHistVecPerThread;
-    uint64_t blocks = (n_vec + per_block - 1) / per_block;
+    const uint64_t rounds = (seg_n / 16 + kHistRound - 1) / kHistRound;
+    uint64_t blocks = (rounds + kHistRoundsPerBlock - 1) / kHistRoundsPerBlock;
     const uint64_t cap = n_seg < 65536 ? 65536 / n_seg : 1;
     if (blocks > cap) blocks = cap;
     return blocks ? (uint32_t)blocks : 1u;
@@ -233,12 +248,9 @@ uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
 hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
                             uint64_t *counts, uint32_t *partial, hipStream_t s) {
     const uint32_t blocks = histogram_blocks(seg_n, n_seg);
-    const uint64_t n_vec = seg_n / 16;
-    const uint64_t per_block = (n_vec + blocks - 1) / blocks;
     hipLaunchKernelGGL(histogram_kernel, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n, in_stride,
-                       per_block, partial);
-    hipLaunchKernelGGL(histogram_reduce_kernel, dim3(256 / kReduceBins, n_seg), dim3(256), 0, s, partial, blocks,
-                       counts);
+                       partial);
+    hipLaunchKernelGGL(histogram_reduce_kernel, dim3(256, n_seg), dim3(64), 0, s, partial, blocks, counts);
     return hipGetLastError();
 }
 
