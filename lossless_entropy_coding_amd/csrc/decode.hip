@@ -2,15 +2,17 @@
 //
 // Every 256-symbol sub-chunk starts at a bit offset recorded in the stream
 // index, so one lane decodes one sub-chunk serially and a wave64 decodes 64
-// consecutive sub-chunks side by side.  Their compressed bits form one
-// contiguous span of the payload (about 14 KiB at 16384-symbol chunks), which
-// the wave first copies into its own LDS region (16 KiB, 15 KiB for Huffman)
-// with coalesced 16-byte loads.
-// The decode loop then reads only LDS: a 32-bit window at any bit position is
-// one two-word LDS read plus a funnel shift and serves two codes of up to 16
-// bits each.  (A global load inside the loop would stall on the output
-// stores too: one counter tracks both.)  A span larger than the LDS region
-// (data that barely compresses) is decoded straight from global memory.
+// sub-chunks side by side.  Each lane first copies the 16-byte blocks that
+// hold its sub-chunk from the payload into its own column of the wave's LDS
+// region: word k of lane l's bits goes to row k, column l.  A 32-bit window
+// at any bit position is then one two-row LDS read (rows k and k + 1 of the
+// lane's column) plus a funnel shift, and the 64 lanes of a read always hit
+// 64 different banks, whatever their positions: a contiguous copy of the
+// compressed span would have the lanes read at scattered addresses, which
+// costs several times more in bank conflicts.  (A global load inside the
+// decode loop would stall on the output stores too: one counter tracks both.)
+// A sub-chunk too long for the region (data that barely compresses) is
+// decoded straight from global memory.
 //   QLC      the 3-bit prefix gives the code length through a packed constant
 //            (no memory access on the dependency chain); the top 11 bits index
 //            a 2048-entry LDS table that yields the byte or flags an unused
@@ -29,36 +31,43 @@ namespace ec {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                        // one workgroup per CU shares one copy of the tables
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kGuardBytes = 1536;               // > 256 codes x 40 bits of overrun
+constexpr uint32_t kLdsBytes = 160 * 1024;
+constexpr uint32_t kRowBytes = 64 * 4;               // one word per lane
+// Rows past the last region that a lane may read: a position is clamped to
+// its region at the start of every 8 codes, which then move it by at most
+// 8 x 40 bits (10 rows), and a window or the Huffman bit buffer reads up to
+// five rows further.
+constexpr uint32_t kGuardRows = 16;
 
-// Bits of a lane's sub-chunk staged in LDS.  The wave's span is copied to
-// words 4.. of its region (words 0-3 are zero, word 3 is the guard before
-// the span).  x is the absolute LDS bit address of the guard word's start
-// plus 31 plus the span bit position, so the word holding the bit before the
-// read position is x >> 5 and a 32-bit window never needs a special case.
-// Positions only move forward from a validated start by at most 40 bits a
-// code, and the region is followed by guard words, so reads stay inside the
-// allocation even for corrupt streams.
-struct SpanBits {
+// Bits of a lane's sub-chunk staged in its LDS column.  Row r of the wave's
+// region holds word r - 1 of every lane's bits (row 0 is never written: a
+// window at a word boundary reads it and shifts it out).  Y is the position
+// plus 31 plus the region's row offset in bits (its LDS byte address / 8), so
+// the row holding the bit before the position is Y >> 5 and its LDS byte
+// address is (Y >> 5) * 256 + 4 * lane: no base to add, and a 32-bit window
+// never needs a special case.  A valid sub-chunk never leaves its region;
+// for corrupt streams prepare() clamps the position to the region's last row
+// every 8 codes, so reads stay inside the allocation (rows past a lane's data
+// hold other data or guard rows) and the end check flags the stream.
+struct ColBits {
     static constexpr bool kStaged = true;
-    uint32_t x;      // absolute LDS bit address of the position, plus 31
-    uint32_t base;   // absolute LDS bit address of the span's first bit
+    uint32_t Y;      // see above
+    uint32_t col;    // 4 * lane
+    uint32_t base;   // Y of the lane's bit 0
+    uint32_t ylim;   // largest Y in the region's last row
 
     typedef __attribute__((address_space(3))) const uint32_t lds_word;
-    __device__ __forceinline__ uint32_t at(uint32_t xx) const {
-        // word address from the bit address by a shift and a mask (no base
-        // to add); the two words hold the bit before the position and the
-        // 31 bits after it
-        lds_word *w = (lds_word *)(size_t)((xx >> 3) & ~3u);
-        return __builtin_amdgcn_alignbit(w[0], w[1], ~xx);
+    __device__ __forceinline__ uint32_t at(uint32_t yy) const {
+        lds_word *w = (lds_word *)(size_t)(((yy >> 5) << 8) | col);
+        return __builtin_amdgcn_alignbit(w[0], w[64], ~yy);
     }
-    __device__ __forceinline__ uint32_t win() const { return at(x); }
-    __device__ __forceinline__ uint64_t win64() const { return ((uint64_t)at(x) << 32) | at(x + 32u); }
-    __device__ __forceinline__ void adv(uint32_t l) { x += l; }
-    __device__ __forceinline__ void prepare() {}
-    __device__ __forceinline__ uint64_t bit() const { return x + 1u - base; }   // span-relative position
+    __device__ __forceinline__ uint32_t win() const { return at(Y); }
+    __device__ __forceinline__ uint64_t win64() const { return ((uint64_t)at(Y) << 32) | at(Y + 32u); }
+    __device__ __forceinline__ void adv(uint32_t l) { Y += l; }
+    __device__ __forceinline__ void prepare() { Y = min(Y, ylim); }
+    __device__ __forceinline__ uint64_t bit() const { return Y - base; }   // lane-relative position
 };
 
 // Bits of a lane's sub-chunk read straight from global memory (spans that
@@ -133,10 +142,17 @@ __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt
     return sym[idx & 255] | (l << 8);
 }
 
+// Status bits from a rare path, behind a call: the decode loop then has a
+// fixed number of memory operations, and the compiler counts the loads in
+// flight exactly instead of waiting for every store.
+__device__ __noinline__ void flag(uint32_t *status, uint32_t bits) { or_status(status, bits); }
+
 // Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
 // run) from source S into dst; returns the bits of the QLC / EG "not a
-// codeword" flags (bit 8 and up).
-template <int CODEC, int PAIRS, class Src>
+// codeword" flags (bit 8 and up).  FULL > 0: a whole run from an LDS column
+// (the common case), in code with a fixed number of stores, so that the
+// compiler can count the memory operations in flight across it.
+template <int CODEC, int PAIRS, int FULL, class Src>
 __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *dst, const uint16_t *l1,
                                                const uint8_t *symtab, const DeepTables *dt, uint32_t max_len,
                                                uint32_t lens, uint32_t k_eg) {
@@ -173,16 +189,26 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
     // two codes from one window when both fit in it; returns byte0 | byte1 << 8
     auto two = [&]() __attribute__((always_inline)) -> uint32_t {
         const uint32_t w = S.win();
-        const Code c1 = code_at(w);
-        Code c2;
+        Code c1, c2;
+        if (CODEC != EC_CODEC_HUFFMAN) c1 = code_at(w);
         if (CODEC == EC_CODEC_HUFFMAN) {
-            // the second code's table index comes from the same window when
-            // the first code left at least 13 bits of it
-            S.adv(c1.len);
-            const uint32_t w2 = c1.len <= 32u - kHuffBits ? w << c1.len : S.win();
-            c2.e = l1[w2 >> (32 - kHuffBits)];
-            if (c2.e < 256u) c2.e = huff_deep(S.win64(), dt, symtab, max_len);
-            S.adv(c2.e >> 8);
+            // Both table reads from the one window: a code the table covers
+            // has at most 13 bits, so 19 bits of the window follow it.  A
+            // longer code (rare) sends the lanes that hold one to the
+            // canonical search and a fresh window for the second code.
+            uint32_t e1 = l1[w >> (32 - kHuffBits)];
+            uint32_t e2 = l1[(w << (e1 >> 8)) >> (32 - kHuffBits)];
+            if (min(e1, e2) < 256u) {
+                if (e1 < 256u) e1 = huff_deep(S.win64(), dt, symtab, max_len);
+                S.adv(e1 >> 8);
+                e2 = l1[S.win() >> (32 - kHuffBits)];
+                if (e2 < 256u) e2 = huff_deep(S.win64(), dt, symtab, max_len);
+                S.adv(e2 >> 8);
+            } else {
+                S.adv((e1 >> 8) + (e2 >> 8));
+            }
+            c1.e = e1;
+            c2.e = e2;
         } else {
             c2 = code_at(w << c1.len);
             S.adv(c1.len + c2.len);
@@ -206,11 +232,22 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
         }
     };
 
-    if (cnt == kSub && Src::kStaged) {
+    if constexpr (FULL == 2) {
+        // a loop of 16 codes a pass: the Huffman pair step carries the rare
+        // long code path, and the whole run unrolled would not fit the
+        // instruction cache
+        for (int i = 0; i < kSub / 16; ++i) {
+            uint32_t o[4];
+            eight(o[0], o[1]);
+            eight(o[2], o[3]);
+            *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    } else if constexpr (FULL == 1) {
         // 128 decoded bytes are collected in registers and written as one
         // whole cache line: 16-byte stores to 64 lanes' separate lines leave
         // partial lines in L2 that get written back more than once
-        for (int half = 0; half < 2; ++half) {
+        static_for<0, 2>([&](auto hf) __attribute__((always_inline)) {
+            constexpr int half = decltype(hf)::value;
             uint32_t o[32];
             static_for<0, 16>([&](auto hc) __attribute__((always_inline)) {
                 constexpr int h = decltype(hc)::value;
@@ -224,7 +261,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
                 constexpr int i = decltype(ic)::value;
                 line[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
             });
-        }
+        });
     } else if (cnt == kSub) {
         for (int i = 0; i < kSub / 16; ++i) {
             uint32_t o[4];
@@ -233,26 +270,32 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     } else {
-        for (uint32_t k = 0; k < cnt; ++k) dst[k] = (uint8_t)one();
+        for (uint32_t k = 0; k < cnt; ++k) {
+            S.prepare();
+            dst[k] = (uint8_t)one();
+        }
     }
     return bad;
 }
 
-// Index entries of one lane's sub-chunk and of its wave's span, as loaded
-// from the stream (resolved later, so that the loads can be in flight while
-// the wave decodes an earlier task).
-struct IndexRaw {
-    uint64_t co0, co1;        // the lane's chunk: byte offsets of its start and end in the payload
-    uint64_t slo, shi;        // the wave's span: first chunk's start, last chunk's end
-    uint32_t e_start, e_end;  // the lane's sub-chunk: start and end bit in its chunk
+// A lane's sub-chunk: its bits [sb, eb) in the payload and its symbols,
+// the 16-byte payload blocks that hold them, and the wave's largest block
+// count.
+struct LaneTask {
+    uint64_t sb, eb;
+    uint64_t first_sym;
+    uint64_t blk0;      // first block
+    uint32_t nv;        // blocks (0: nothing to decode)
+    uint32_t nv_max;    // over the wave
+    uint32_t cnt;       // symbols (0: no sub-chunk)
+    bool ok;            // index entries valid
 };
 
-// A wave's task: 64 consecutive sub-chunks of one stream, one per lane.
-struct Plan {
-    uint64_t co0, span_lo;
-    uint32_t e_start, e_end, cnt, nblk;
-    uint64_t first_sym;
-    bool active, ok, fits;
+// Index entries of a lane's sub-chunk as loaded (resolved later, so that the
+// loads are in flight while the wave decodes an earlier task).
+struct IndexRaw {
+    uint64_t co0, co1;        // the lane's chunk: byte offsets of its start and end in the payload
+    uint32_t e_start, e_end;  // the lane's sub-chunk: start and end bit in its chunk
 };
 
 // Stream fields the tasks of a segment share (validated once per segment).
@@ -262,132 +305,186 @@ struct StreamInfo {
     uint32_t nch, spc;
 };
 
-__device__ __forceinline__ IndexRaw issue_index(const DecodeArgs &a, const StreamInfo &si, uint32_t g0,
-                                                uint32_t lane) {
+__device__ __forceinline__ IndexRaw issue_index(const DecodeArgs &a, const StreamInfo &si, uint32_t g) {
     const uint64_t *chunk_off = reinterpret_cast<const uint64_t *>(si.stream + kHeaderBytes);
     const uint32_t *sub_end = reinterpret_cast<const uint32_t *>(si.stream + kHeaderBytes + 8ull * (si.nch + 1));
-    const uint32_t g = g0 + lane;
     const uint32_t gl = g < a.blocks_per_seg ? g : a.blocks_per_seg - 1;
     const uint32_t c = gl / si.spc, j = gl - c * si.spc;
-    const uint32_t g_last = g0 + 63 < a.blocks_per_seg ? g0 + 63 : a.blocks_per_seg - 1;
     IndexRaw r;
     r.co0 = chunk_off[c];
     r.co1 = chunk_off[c + 1];
     r.e_end = sub_end[(uint64_t)c * si.spc + j];
     r.e_start = j ? sub_end[(uint64_t)c * si.spc + j - 1] : 0u;
-    r.slo = chunk_off[g0 / si.spc];
-    r.shi = chunk_off[g_last / si.spc + 1];
     return r;
 }
 
-// Checks the lane's index entries (flags a corrupt index) and decides
-// whether the wave's span fits its LDS region.
-template <uint32_t kSpan>
-__device__ __forceinline__ Plan resolve(const DecodeArgs &a, const StreamInfo &si, const IndexRaw &r, uint32_t g0,
-                                        uint32_t lane, uint32_t *status) {
-    Plan p;
-    const uint32_t g = g0 + lane;
-    p.active = g < a.blocks_per_seg;
-    p.ok = p.active && r.co0 <= r.co1 && r.co1 <= si.pb && !(r.co0 & 15) &&
-           (uint64_t)r.e_end <= (r.co1 - r.co0) * 8 && r.e_start <= r.e_end;
-    if (p.active && !p.ok) or_status(status, EC_S_CORRUPT);
-    p.span_lo = r.slo & ~15ull;
-    const uint64_t span_hi = r.shi;
-    bool fits = p.span_lo <= span_hi && span_hi <= si.pb && span_hi - p.span_lo <= kSpan;
-    p.fits = fits && __ballot(p.ok && (r.co0 < p.span_lo || r.co1 > span_hi)) == 0;
-    p.nblk = p.fits ? (uint32_t)((span_hi - p.span_lo + 15) >> 4) : 0u;
-    p.co0 = r.co0;
-    p.e_start = r.e_start;
-    p.e_end = r.e_end;
-    p.first_sym = (uint64_t)g * kSub;
-    p.cnt = !p.active ? 0u : (a.seg_n - p.first_sym < kSub ? (uint32_t)(a.seg_n - p.first_sym) : (uint32_t)kSub);
-    return p;
+// Checks the index entries of sub-chunk g (flags a corrupt index).
+__device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInfo &si, const IndexRaw &r, uint32_t g,
+                                            uint32_t *status) {
+    const bool active = g < a.blocks_per_seg;
+    LaneTask t;
+    t.ok = active && r.co0 <= r.co1 && r.co1 <= si.pb && !(r.co0 & 15) && (uint64_t)r.e_end <= (r.co1 - r.co0) * 8 &&
+           r.e_start <= r.e_end;
+    if (active && !t.ok) flag(status, EC_S_CORRUPT);
+    t.sb = r.co0 * 8 + r.e_start;
+    t.eb = r.co0 * 8 + r.e_end;
+    t.first_sym = (uint64_t)g * kSub;
+    t.cnt = !active ? 0u : (a.seg_n - t.first_sym < kSub ? (uint32_t)(a.seg_n - t.first_sym) : (uint32_t)kSub);
+    const bool live = t.ok && t.cnt > 0 && t.eb > t.sb;
+    t.blk0 = live ? t.sb >> 7 : 0;
+    t.nv = live ? (uint32_t)(((t.eb - 1) >> 7) - t.blk0 + 1) : 0u;
+    uint32_t m = t.nv;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
+    t.nv_max = m;
+    return t;
 }
 
-// The wave's span as 16-byte blocks, lane + 64 k, loaded into registers
-// (indexes clamped to the span, so every load stays inside it).
+// The first K blocks of a lane's sub-chunk, loaded into registers (indexes
+// clamped to the lane's last block, or to the payload's first block for
+// lanes with nothing to decode, so every load stays inside the payload).
 template <int K>
-__device__ __forceinline__ void issue_span(const StreamInfo &si, const Plan &p, uint32_t lane, uint4 (&v)[K]) {
-    if (!p.fits || p.nblk == 0) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + (p.span_lo >> 4);
-    const uint32_t last = p.nblk - 1;
+__device__ __forceinline__ void issue_blocks(const StreamInfo &si, const LaneTask &t, uint4 (&v)[K]) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + t.blk0;
+    const uint32_t last = t.nv ? t.nv - 1 : 0u;
     static_for<0, K>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
-        v[k] = src[min(lane + 64u * k, last)];
+        v[k] = src[min((uint32_t)k, last)];
     });
 }
 
+// Blocks first .. nv_max - 1 of the lanes' sub-chunks (those not
+// prefetched) into their LDS columns; a rare path, behind a call.
+__device__ __noinline__ void stage_rest(uint32_t col_word0, const uint4 *src, uint32_t nv, uint32_t first,
+                                        uint32_t nv_max) {
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    for (uint32_t j = first; j < nv_max; j += 4) {   // four loads in flight per lane
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (j + k < nv) v[k] = src[j + k];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (j + k < nv) {
+                lds_u32 *w = (lds_u32 *)(size_t)(col_word0 + (4 * (j + k)) * kRowBytes);
+                w[0] = v[k].x;
+                w[64] = v[k].y;
+                w[128] = v[k].z;
+                w[192] = v[k].w;
+            }
+        }
+    }
+}
+
+// Everything but a whole staged run, behind a call: a segment's last,
+// shorter run; runs of a wave whose longest sub-chunk does not fit its LDS
+// region (read straight from global memory); sub-chunks without bits.
+template <int CODEC, int PAIRS>
+__device__ __noinline__ void decode_rest(const LaneTask &L, bool fits, uint32_t region, uint32_t ylim, uint32_t lane,
+                                         const uint32_t *payload, uint64_t pb, uint8_t *dst, const uint16_t *l1,
+                                         const uint8_t *symtab, const DeepTables *dt, uint32_t max_len, uint32_t lens,
+                                         uint32_t k_eg, uint32_t *status) {
+    uint32_t bad = 0;
+    uint64_t end_pos = 1, want_pos = 0;
+    if (L.nv == 0) {
+        // symbols but no bits: corrupt
+    } else if (fits) {
+        ColBits S;
+        S.col = 4 * lane;
+        S.base = region / 8 + 31;
+        S.Y = S.base + (uint32_t)(L.sb - L.blk0 * 128);
+        S.ylim = ylim;
+        bad = decode_run<CODEC, PAIRS, 0>(S, L.cnt, dst, l1, symtab, dt, max_len, lens, k_eg);
+        end_pos = S.bit();
+        want_pos = L.eb - L.blk0 * 128;
+    } else {
+        GlobalBits S;
+        S.init(payload, pb >> 2, L.sb);
+        bad = decode_run<CODEC, PAIRS, 0>(S, L.cnt, dst, l1, symtab, dt, max_len, lens, k_eg);
+        end_pos = S.bit();
+        want_pos = L.eb;
+    }
+    if ((bad & ~0xffu) || end_pos != want_pos) or_status(status, EC_S_CORRUPT);
+}
+
 // Persistent workgroups: workgroup b takes tasks b, b + G, ... (G = grid);
-// a task is 256 consecutive sub-chunks of one stream, 64 per wave.  For QLC
-// the index entries of the wave's task after next and the compressed span of
-// its next task are loaded while it decodes the current one.
+// a task is 512 consecutive sub-chunks of one stream, 64 per wave.
 template <int CODEC, int PAIRS>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
-    // Staging per wave: 16 KiB, or 15 KiB next to the 16 KiB Huffman table,
-    // so that two workgroups still fit in a CU's 160 KiB of LDS.
-    constexpr uint32_t kSpan = CODEC == EC_CODEC_HUFFMAN ? 15360 : 16384;
-    constexpr int kSpanVec = kSpan / 16 / 64;   // 16-byte blocks per lane
-    // Keeping the next span in registers costs 64 VGPRs: QLC's decode loop
-    // has them to spare, the Huffman and EG loops do not.
-    constexpr bool kPrefetch = CODEC == EC_CODEC_QLC;
     constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
                                    : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
                                                                : 1;
-    // tables first, so that their addresses fit the LDS instructions' offset field
-    struct Smem {
-        uint4 tabv[kTableVec];
+    struct Head {
+        uint4 tabv[kTableVec];     // QLC / Huffman decode table
         uint8_t symtab[256];       // EG: rank -> byte; Huffman: canonical order -> byte
         DeepTables deep[1];        // Huffman only
         uint64_t po, pb;
-        uint32_t ok, nch, spc;
-        uint32_t pad_;
-        uint4 spans[kWaves][(kSpan + 32) / 16];
-        uint4 guard[kGuardBytes / 16];
+        uint32_t ok, nch, spc, pad_;
     };
+    // the rest of the CU's LDS: one region of kRows rows per wave, then guard rows
+    constexpr uint32_t kHeadBytes = (sizeof(Head) + kRowBytes - 1) / kRowBytes * kRowBytes;
+    constexpr uint32_t kRows = (kLdsBytes - kHeadBytes - kGuardRows * kRowBytes) / (kWaves * kRowBytes);
+    struct Smem {
+        Head h;
+        alignas(256) uint32_t cols[kWaves][kRows * 64];
+        uint32_t guard[kGuardRows * 64];
+    };
+    static_assert(sizeof(Smem) <= kLdsBytes, "LDS budget");
     __shared__ Smem sm;
-    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.tabv);
-    uint8_t *symtab = sm.symtab;
+    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.h.tabv);
+    uint8_t *symtab = sm.h.symtab;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads > 0 ? (a.blocks_per_seg + kThreads - 1) / kThreads
                                                                            : 1u;
     const uint32_t n_tasks = gx * a.n_seg;
-    uint4 *region = sm.spans[wave];
-    // word 3 of the region is the guard word right before the span
-    const uint32_t region_base = (uint32_t)(size_t)(__attribute__((address_space(3))) const uint4 *)region * 8 + 4 * 32;
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    const uint32_t region = (uint32_t)(size_t)(lds_u32 *)sm.cols[wave];   // 256-byte aligned
+    lds_u32 *my_col = (lds_u32 *)(size_t)(region + 4 * lane);
 
+    // Blocks of the next task that a lane loads into registers while it
+    // decodes the current one: 16 (a whole sub-chunk at 16384-symbol chunks)
+    // next to the QLC and Huffman loops, 4 next to the EG loop.
+    constexpr int kPre = CODEC == EC_CODEC_EXP_GOLOMB ? 4 : 16;
     uint32_t cur_seg = ~0u;
     StreamInfo si = {};
     const DevTables *tab = nullptr;
     uint32_t *status = nullptr;
+    // codebook constants, read once per segment: a global load in the loop
+    // would wait for the prefetch loads issued before it
+    uint32_t seg_lens = 0, seg_max_len = 0, seg_k_eg = 0;
     bool have_cur = false, have_next_raw = false;
-    Plan cur = {};
+    LaneTask cur = {};
     IndexRaw next_raw = {};
-    uint4 span_regs[kPrefetch ? kSpanVec : 1];
+    uint4 pre[kPre];
 #pragma unroll
-    for (int k = 0; k < (kPrefetch ? kSpanVec : 1); ++k) span_regs[k] = make_uint4(0, 0, 0, 0);
+    for (int k = 0; k < kPre; ++k) pre[k] = make_uint4(0u, 0u, 0u, 0u);
 
     for (uint32_t t = blockIdx.x; t < n_tasks; t += gridDim.x) {
         const uint32_t seg = t / gx, bx = t - seg * gx;
         if (seg != cur_seg) {
             __syncthreads();   // the previous segment's tables are no longer read
             tab = seg_tables<DecodeArgs>(seg);
-            if (CODEC == EC_CODEC_QLC) sm.tabv[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
+            if (CODEC == EC_CODEC_QLC && tid < kTableVec) sm.h.tabv[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
             if (CODEC == EC_CODEC_HUFFMAN) {
 #pragma unroll
                 for (int k = 0; k < (int)kTableVec / kThreads; ++k)
-                    sm.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
+                    sm.h.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
             }
-            if (CODEC != EC_CODEC_QLC) symtab[tid] = tab->sym[tid];
+            if (CODEC != EC_CODEC_QLC && tid < 256) symtab[tid] = tab->sym[tid];
             if constexpr (CODEC == EC_CODEC_HUFFMAN) {
                 constexpr uint32_t kDeep = EC_MAX_CODE_LEN - kHuffBits;
                 if (tid < kDeep) {
-                    sm.deep[0].limit[tid] = tab->limit[kHuffBits + 1 + tid];
-                    sm.deep[0].first_code[tid] = tab->first_code[kHuffBits + 1 + tid];
-                    sm.deep[0].first_idx[tid] = tab->first_idx[kHuffBits + 1 + tid];
+                    sm.h.deep[0].limit[tid] = tab->limit[kHuffBits + 1 + tid];
+                    sm.h.deep[0].first_code[tid] = tab->first_code[kHuffBits + 1 + tid];
+                    sm.h.deep[0].first_idx[tid] = tab->first_idx[kHuffBits + 1 + tid];
                 }
             }
             const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
             status = a.status ? a.status + seg : nullptr;
+            seg_lens = tab->qlc_lens;
+            seg_max_len = tab->max_len;
+            seg_k_eg = (uint32_t)tab->eg_k;
             if (tid == 0) {
                 const uint64_t *h = reinterpret_cast<const uint64_t *>(stream);
                 const uint64_t h0 = h[0], n = h[1], h2 = h[2], po = h[3], pb = h[4], id = h[5];
@@ -409,111 +506,101 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                     if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
                         bits = EC_S_BAD_HEADER;
                 }
-                sm.ok = bits == 0;
-                if (bits && bx == 0) or_status(status, bits);
-                sm.nch = nch;
-                sm.spc = C / kSub;
-                sm.po = po;
-                sm.pb = pb;
+                sm.h.ok = bits == 0;
+                if (bits && bx == 0) flag(status, bits);
+                sm.h.nch = nch;
+                sm.h.spc = C / kSub;
+                sm.h.po = po;
+                sm.h.pb = pb;
             }
             __syncthreads();
             cur_seg = seg;
             si.stream = stream;
-            si.po = sm.po;
-            si.pb = sm.pb;
-            si.nch = sm.nch;
-            si.spc = sm.spc;
+            si.po = sm.h.po;
+            si.pb = sm.h.pb;
+            si.nch = sm.h.nch;
+            si.spc = sm.h.spc;
             have_cur = have_next_raw = false;
         }
-        if (!sm.ok) continue;   // uniform over the workgroup
+        if (!sm.h.ok) continue;   // uniform over the workgroup
 
         const uint32_t g0 = bx * kThreads + wave * 64;   // the wave's first sub-chunk
-        const bool wave_busy = g0 < a.blocks_per_seg;
         // the wave's next task, if it is in the same stream
         const uint32_t t1 = t + gridDim.x;
         const bool next_same = t1 < n_tasks && t1 / gx == seg;
         const uint32_t g0n = (t1 - seg * gx) * kThreads + wave * 64;
         const bool next_busy = next_same && g0n < a.blocks_per_seg;
+        if (g0 >= a.blocks_per_seg) {   // uniform over the wave
+            have_cur = have_next_raw = false;
+            continue;
+        }
+        if (!have_cur) {   // nothing prefetched: this task's index and blocks now
+            cur = resolve(a, si, issue_index(a, si, g0 + lane), g0 + lane, status);
+            issue_blocks<kPre>(si, cur, pre);
+        }
+        if (next_busy && !have_next_raw) next_raw = issue_index(a, si, g0n + lane);
+        const LaneTask L = cur;
+        const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
 
-        if (wave_busy) {
-            if (!have_cur) {   // nothing prefetched: load this task's index and span now
-                const IndexRaw r = issue_index(a, si, g0, lane);
-                cur = resolve<kSpan>(a, si, r, g0, lane, status);
-                if constexpr (kPrefetch) issue_span<kSpanVec>(si, cur, lane, span_regs);
-            }
-            if (kPrefetch && next_busy && !have_next_raw) next_raw = issue_index(a, si, g0n, lane);
-            // stage the span: region block 0 is zero (its last word is the
-            // guard before the span), the span follows from block 1, and a
-            // zero block closes it
-            if (cur.fits) {
-                if constexpr (kPrefetch) {
-                    static_for<0, kSpanVec>([&](auto kc) __attribute__((always_inline)) {
-                        constexpr int k = decltype(kc)::value;
-                        if (lane + 64u * k < cur.nblk) region[1 + lane + 64 * k] = span_regs[k];
-                    });
-                } else {
-                    // coalesced copy, four 1 KiB loads in flight per pass
-                    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + (cur.span_lo >> 4);
-                    const uint32_t nblk = cur.nblk;
-                    for (uint32_t i = lane; i < nblk; i += 256) {
-                        const uint32_t last = nblk - 1;
-                        const uint4 v0 = src[min(i, last)], v1 = src[min(i + 64, last)];
-                        const uint4 v2 = src[min(i + 128, last)], v3 = src[min(i + 192, last)];
-                        region[1 + i] = v0;
-                        if (i + 64 < nblk) region[1 + i + 64] = v1;
-                        if (i + 128 < nblk) region[1 + i + 128] = v2;
-                        if (i + 192 < nblk) region[1 + i + 192] = v3;
-                    }
+        // stage the lane's blocks in its column if the wave's longest
+        // sub-chunk fits the region: the prefetched ones from registers, any
+        // further ones loaded now
+        const bool fits = 1 + 4 * L.nv_max <= kRows;
+        if (fits) {
+            static_for<0, kPre>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                if ((uint32_t)k < L.nv) {
+                    lds_u32 *w = my_col + (1 + 4 * k) * 64;   // rows 1 + 4 k ...
+                    w[0] = pre[k].x;
+                    w[64] = pre[k].y;
+                    w[128] = pre[k].z;
+                    w[192] = pre[k].w;
                 }
-                if (lane == 0) region[0] = make_uint4(0u, 0u, 0u, 0u);
-                if (lane == 1) region[1 + cur.nblk] = make_uint4(0u, 0u, 0u, 0u);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const Plan p = cur;
-            // prefetch: the next task's span, and the index entries of the one after
-            if (kPrefetch && next_busy) {
-                cur = resolve<kSpan>(a, si, next_raw, g0n, lane, status);
-                if constexpr (kPrefetch) issue_span<kSpanVec>(si, cur, lane, span_regs);
-                have_cur = true;
-                const uint32_t t2 = t1 + gridDim.x;
-                const uint32_t g0nn = (t2 - seg * gx) * kThreads + wave * 64;
-                have_next_raw = t2 < n_tasks && t2 / gx == seg && g0nn < a.blocks_per_seg;
-                if (have_next_raw) next_raw = issue_index(a, si, g0nn, lane);
-            } else {
-                have_cur = have_next_raw = false;
-            }
+            });
+            if (L.nv_max > (uint32_t)kPre)
+                stage_rest(region + kRowBytes + 4 * lane, reinterpret_cast<const uint4 *>(si.stream + si.po) + L.blk0,
+                           L.nv, kPre, L.nv_max);
+            // each lane reads only its own column: program order suffices
+            asm volatile("" ::: "memory");
+        }
 
-            uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + p.first_sym;
-            const uint32_t lens = tab->qlc_lens;
-            const uint32_t k_eg = (uint32_t)tab->eg_k;
-            uint32_t bad = 0;
-            uint64_t end_pos = 0, want_pos = 0;
-            if (p.fits) {
-                if (p.ok) {
-                    SpanBits S;
-                    S.base = region_base;
-                    S.x = S.base + (uint32_t)((p.co0 - p.span_lo) * 8 + p.e_start) - 1u;
-                    bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, sm.deep, tab->max_len, lens, k_eg);
-                    end_pos = S.bit();
-                    want_pos = (p.co0 - p.span_lo) * 8 + p.e_end;
-                }
-            } else if (p.ok) {
-                GlobalBits S;
-                S.init(reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb >> 2, p.co0 * 8 + p.e_start);
-                bad = decode_run<CODEC, PAIRS>(S, p.cnt, dst, l1, symtab, sm.deep, tab->max_len, lens, k_eg);
-                end_pos = S.bit();
-                want_pos = p.co0 * 8 + p.e_end;
-            }
-            if (p.ok && ((bad & ~0xffu) || end_pos != want_pos)) or_status(status, EC_S_CORRUPT);
-            // the region is rewritten at the next task: all lanes' reads first
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // prefetch: the next task's blocks, and the index entries of the one after
+        if (next_busy) {
+            cur = resolve(a, si, next_raw, g0n + lane, status);
+            issue_blocks<kPre>(si, cur, pre);
+            have_cur = true;
+            const uint32_t t2 = t1 + gridDim.x;
+            const uint32_t g0nn = (t2 - seg * gx) * kThreads + wave * 64;
+            have_next_raw = t2 < n_tasks && t2 / gx == seg && g0nn < a.blocks_per_seg;
+            if (have_next_raw) next_raw = issue_index(a, si, g0nn + lane);
         } else {
             have_cur = have_next_raw = false;
         }
+
+        uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + L.first_sym;
+        const uint32_t ylim = region / 8 + kRows * 32 - 1;
+        const bool full = live && fits && L.cnt == kSub && L.nv > 0;
+        bool corrupt = false;
+        if (full) {   // the common case: a whole run from the lane's column
+            const uint32_t p0 = (uint32_t)(L.sb - L.blk0 * 128), want = (uint32_t)(L.eb - L.blk0 * 128);
+            ColBits S;
+            S.col = 4 * lane;
+            S.base = region / 8 + 31;
+            S.Y = S.base + p0;
+            S.ylim = ylim;
+            constexpr int kFull = CODEC == EC_CODEC_HUFFMAN ? 2 : 1;
+            const uint32_t bad = decode_run<CODEC, PAIRS, kFull>(S, kSub, dst, l1, symtab, sm.h.deep, seg_max_len,
+                                                                 seg_lens, seg_k_eg);
+            corrupt = (bad & ~0xffu) || S.bit() != want;
+        }
+        if (__ballot(live && !full))
+            if (live && !full)
+                decode_rest<CODEC, PAIRS>(L, fits, region, ylim, lane, reinterpret_cast<const uint32_t *>(si.stream + si.po),
+                                          si.pb, dst, l1, symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg,
+                                          status);
+        if (corrupt) flag(status, EC_S_CORRUPT);
+        // the column is rewritten at the next task, after this lane's reads
+        asm volatile("" ::: "memory");
     }
 }
 
