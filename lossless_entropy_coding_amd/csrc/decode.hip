@@ -37,9 +37,13 @@ constexpr uint32_t kLdsBytes = 160 * 1024;
 constexpr uint32_t kRowBytes = 64 * 4;               // one word per lane
 // Rows past the last region that a lane may read: a position is clamped to
 // its region at the start of every 8 codes, which then move it by at most
-// 8 x 40 bits (10 rows), and a window or the Huffman bit buffer reads up to
-// five rows further.
-constexpr uint32_t kGuardRows = 16;
+// 8 codes of the longest length the codec can read (QLC 11 bits, EG 25,
+// Huffman 40), and a window reads up to two rows further.
+template <int CODEC>
+constexpr uint32_t guard_rows() {
+    constexpr uint32_t kMaxCode = CODEC == EC_CODEC_QLC ? 11 : CODEC == EC_CODEC_HUFFMAN ? EC_MAX_CODE_LEN : 25;
+    return (8 * kMaxCode + 31) / 32 + 3;
+}
 
 // Bits of a lane's sub-chunk staged in its LDS column.  Row r of the wave's
 // region holds word r - 1 of every lane's bits (row 0 is never written: a
@@ -233,9 +237,9 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
     };
 
     if constexpr (FULL == 2) {
-        // a loop of 16 codes a pass: the Huffman pair step carries the rare
-        // long code path, and the whole run unrolled would not fit the
-        // instruction cache
+        // a loop of 16 codes a pass (Huffman, EG): the whole run unrolled
+        // would not fit the instruction cache next to the Huffman pair
+        // step's rare long code path, and the EG loop would spill
         for (int i = 0; i < kSub / 16; ++i) {
             uint32_t o[4];
             eight(o[0], o[1]);
@@ -415,10 +419,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
                                    : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
                                                                : 1;
+    constexpr bool kSym = CODEC != EC_CODEC_QLC;
+    constexpr bool kHasDeep = CODEC == EC_CODEC_HUFFMAN;
+    constexpr uint32_t kGuardRows = guard_rows<CODEC>();
     struct Head {
         uint4 tabv[kTableVec];     // QLC / Huffman decode table
-        uint8_t symtab[256];       // EG: rank -> byte; Huffman: canonical order -> byte
-        DeepTables deep[1];        // Huffman only
+        uint8_t symtab[kSym ? 256 : 4];       // EG: rank -> byte; Huffman: canonical order -> byte
+        DeepTables deep[kHasDeep ? 1 : 0];    // Huffman only
         uint64_t po, pb;
         uint32_t ok, nch, spc, pad_;
     };
@@ -443,9 +450,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     lds_u32 *my_col = (lds_u32 *)(size_t)(region + 4 * lane);
 
     // Blocks of the next task that a lane loads into registers while it
-    // decodes the current one: 16 (a whole sub-chunk at 16384-symbol chunks)
-    // next to the QLC and Huffman loops, 4 next to the EG loop.
-    constexpr int kPre = CODEC == EC_CODEC_EXP_GOLOMB ? 4 : 16;
+    // decodes the current one (a whole sub-chunk at 16384-symbol chunks of
+    // codes averaging under 8 bits).
+    constexpr int kPre = 16;
     uint32_t cur_seg = ~0u;
     StreamInfo si = {};
     const DevTables *tab = nullptr;
@@ -471,7 +478,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                 for (int k = 0; k < (int)kTableVec / kThreads; ++k)
                     sm.h.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
             }
-            if (CODEC != EC_CODEC_QLC && tid < 256) symtab[tid] = tab->sym[tid];
+            if constexpr (kSym) {
+                if (tid < 256) symtab[tid] = tab->sym[tid];
+            }
             if constexpr (CODEC == EC_CODEC_HUFFMAN) {
                 constexpr uint32_t kDeep = EC_MAX_CODE_LEN - kHuffBits;
                 if (tid < kDeep) {
@@ -588,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
             S.base = region / 8 + 31;
             S.Y = S.base + p0;
             S.ylim = ylim;
-            constexpr int kFull = CODEC == EC_CODEC_HUFFMAN ? 2 : 1;
+            constexpr int kFull = CODEC == EC_CODEC_QLC ? 1 : 2;
             const uint32_t bad = decode_run<CODEC, PAIRS, kFull>(S, kSub, dst, l1, symtab, sm.h.deep, seg_max_len,
                                                                  seg_lens, seg_k_eg);
             corrupt = (bad & ~0xffu) || S.bit() != want;
