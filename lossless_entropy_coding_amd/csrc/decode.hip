@@ -237,15 +237,38 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
     };
 
     if constexpr (FULL == 2) {
-        // a loop of 16 codes a pass (Huffman, EG): the whole run unrolled
-        // would not fit the instruction cache next to the Huffman pair
-        // step's rare long code path, and the EG loop would spill
-        for (int i = 0; i < kSub / 16; ++i) {
-            uint32_t o[4];
-            eight(o[0], o[1]);
-            eight(o[2], o[3]);
-            *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
+        // A loop of 16 codes a pass (Huffman, EG): the whole run unrolled
+        // would not fit the instruction cache next to the Huffman pair step's
+        // rare long code path, and the EG loop would spill.  The words of a
+        // half run still gather in registers (placed by the uniform pass
+        // counter) and leave as one whole 128-byte line per lane: 16-byte
+        // stores to 64 lanes' separate lines leave partial lines in L2 that
+        // get written back several times.
+        static_for<0, 2>([&](auto hf) __attribute__((always_inline)) {
+            constexpr int half = decltype(hf)::value;
+            uint32_t o[32];
+#pragma nounroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t w0, w1, w2, w3;
+                eight(w0, w1);
+                eight(w2, w3);
+                // a uniform branch per pass keeps o in registers
+                static_for<0, 8>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int j = decltype(jc)::value;
+                    if (i == j) {
+                        o[4 * j] = w0;
+                        o[4 * j + 1] = w1;
+                        o[4 * j + 2] = w2;
+                        o[4 * j + 3] = w3;
+                    }
+                });
+            }
+            uint4 *line = reinterpret_cast<uint4 *>(dst + 128 * half);
+            static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                line[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+            });
+        });
     } else if constexpr (FULL == 1) {
         // 128 decoded bytes are collected in registers and written as one
         // whole cache line: 16-byte stores to 64 lanes' separate lines leave
