@@ -449,8 +449,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
         uint4 tabv[kTableVec];     // QLC / Huffman decode table
         uint8_t symtab[kSym ? 256 : 4];       // EG: rank -> byte; Huffman: canonical order -> byte
         DeepTables deep[kHasDeep ? 1 : 0];    // Huffman only
-        uint64_t po, pb;
-        uint32_t ok, nch, spc, pad_;
     };
     // the rest of the CU's LDS: one region of kRows rows per wave, then guard rows
     constexpr uint32_t kHeadBytes = (sizeof(Head) + kRowBytes - 1) / kRowBytes * kRowBytes;
@@ -483,9 +481,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     // codebook constants, read once per segment: a global load in the loop
     // would wait for the prefetch loads issued before it
     uint32_t seg_lens = 0, seg_max_len = 0, seg_k_eg = 0;
-    bool have_cur = false, have_next_raw = false;
+    bool have_cur = false, have_next_raw = false, have_first = false, seg_ok = false;
     LaneTask cur = {};
-    IndexRaw next_raw = {};
+    IndexRaw next_raw = {}, first_raw = {};
     uint4 pre[kPre];
 #pragma unroll
     for (int k = 0; k < kPre; ++k) pre[k] = make_uint4(0u, 0u, 0u, 0u);
@@ -495,11 +493,54 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
         if (seg != cur_seg) {
             __syncthreads();   // the previous segment's tables are no longer read
             tab = seg_tables<DecodeArgs>(seg);
-            if (CODEC == EC_CODEC_QLC && tid < kTableVec) sm.h.tabv[tid] = reinterpret_cast<const uint4 *>(tab->l1)[tid];
-            if (CODEC == EC_CODEC_HUFFMAN) {
+            // this thread's share of the decode table, in flight while the
+            // header is checked and the first task's index entries are requested
+            constexpr int kTabPer = (kTableVec + kThreads - 1) / kThreads;
+            uint4 tv[kTabPer];
+            const uint4 *tsrc = reinterpret_cast<const uint4 *>(CODEC == EC_CODEC_HUFFMAN ? tab->hl1 : tab->l1);
 #pragma unroll
-                for (int k = 0; k < (int)kTableVec / kThreads; ++k)
-                    sm.h.tabv[tid + k * kThreads] = reinterpret_cast<const uint4 *>(tab->hl1)[tid + k * kThreads];
+            for (int k = 0; k < kTabPer; ++k) {
+                if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kTableVec) tv[k] = tsrc[tid + k * kThreads];
+            }
+            const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
+            status = a.status ? a.status + seg : nullptr;
+            seg_lens = tab->qlc_lens;
+            seg_max_len = tab->max_len;
+            seg_k_eg = (uint32_t)tab->eg_k;
+            // every wave reads and checks the header itself (no wait on a barrier)
+            const uint64_t *h = reinterpret_cast<const uint64_t *>(stream);
+            const uint64_t h0 = h[0], n = h[1], h2 = h[2], po = h[3], pb = h[4], id = h[5];
+            const uint32_t magic = (uint32_t)h0, version = (uint32_t)(h0 >> 32) & 0xffffu;
+            const uint32_t codec = (uint32_t)(h0 >> 48) & 0xffu, flags = (uint32_t)(h0 >> 56);
+            const uint32_t C = (uint32_t)h2, nch = (uint32_t)(h2 >> 32);
+            uint32_t bits = 0;
+            if (magic != kMagic || version != kVersion || (flags & ~1u)) {
+                bits = EC_S_BAD_HEADER;
+            } else if (codec != tab->codec || id != tab->codebook_id) {
+                bits = EC_S_CODEBOOK_MISMATCH;
+            } else if (n != a.seg_n || C == 0 || (C % kSub) || C > kMaxChunk || (uint64_t)nch != (n + C - 1) / C) {
+                bits = EC_S_BAD_HEADER;
+            } else {
+                uint64_t end = kHeaderBytes + 8ull * (nch + 1) + 4ull * nch * (C / kSub) + ((flags & 1) ? 256 : 0);
+                end = (end + 255) / 256 * 256;
+                if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
+                    bits = EC_S_BAD_HEADER;
+            }
+            if (bits && bx == 0 && tid == 0) flag(status, bits);
+            seg_ok = bits == 0;
+            cur_seg = seg;
+            si.stream = stream;
+            si.po = po;
+            si.pb = pb;
+            si.nch = nch;
+            si.spc = C / kSub;
+            have_cur = have_next_raw = false;
+            const uint32_t g0f = bx * kThreads + wave * 64;
+            have_first = seg_ok && g0f < a.blocks_per_seg;
+            if (have_first) first_raw = issue_index(a, si, g0f + lane);
+#pragma unroll
+            for (int k = 0; k < kTabPer; ++k) {
+                if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kTableVec) sm.h.tabv[tid + k * kThreads] = tv[k];
             }
             if constexpr (kSym) {
                 if (tid < 256) symtab[tid] = tab->sym[tid];
@@ -512,49 +553,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                     sm.h.deep[0].first_idx[tid] = tab->first_idx[kHuffBits + 1 + tid];
                 }
             }
-            const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
-            status = a.status ? a.status + seg : nullptr;
-            seg_lens = tab->qlc_lens;
-            seg_max_len = tab->max_len;
-            seg_k_eg = (uint32_t)tab->eg_k;
-            if (tid == 0) {
-                const uint64_t *h = reinterpret_cast<const uint64_t *>(stream);
-                const uint64_t h0 = h[0], n = h[1], h2 = h[2], po = h[3], pb = h[4], id = h[5];
-                const uint32_t magic = (uint32_t)h0, version = (uint32_t)(h0 >> 32) & 0xffffu;
-                const uint32_t codec = (uint32_t)(h0 >> 48) & 0xffu, flags = (uint32_t)(h0 >> 56);
-                const uint32_t C = (uint32_t)h2, nch = (uint32_t)(h2 >> 32);
-                uint32_t bits = 0;
-                if (magic != kMagic || version != kVersion || (flags & ~1u)) {
-                    bits = EC_S_BAD_HEADER;
-                } else if (codec != tab->codec || id != tab->codebook_id) {
-                    bits = EC_S_CODEBOOK_MISMATCH;
-                } else if (n != a.seg_n || C == 0 || (C % kSub) || C > kMaxChunk ||
-                           (uint64_t)nch != (n + C - 1) / C) {
-                    bits = EC_S_BAD_HEADER;
-                } else {
-                    uint64_t end =
-                        kHeaderBytes + 8ull * (nch + 1) + 4ull * nch * (C / kSub) + ((flags & 1) ? 256 : 0);
-                    end = (end + 255) / 256 * 256;
-                    if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
-                        bits = EC_S_BAD_HEADER;
-                }
-                sm.h.ok = bits == 0;
-                if (bits && bx == 0) flag(status, bits);
-                sm.h.nch = nch;
-                sm.h.spc = C / kSub;
-                sm.h.po = po;
-                sm.h.pb = pb;
-            }
             __syncthreads();
-            cur_seg = seg;
-            si.stream = stream;
-            si.po = sm.h.po;
-            si.pb = sm.h.pb;
-            si.nch = sm.h.nch;
-            si.spc = sm.h.spc;
-            have_cur = have_next_raw = false;
         }
-        if (!sm.h.ok) continue;   // uniform over the workgroup
+        if (!seg_ok) continue;   // uniform over the workgroup
 
         const uint32_t g0 = bx * kThreads + wave * 64;   // the wave's first sub-chunk
         // the wave's next task, if it is in the same stream
@@ -567,9 +568,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
             continue;
         }
         if (!have_cur) {   // nothing prefetched: this task's index and blocks now
-            cur = resolve(a, si, issue_index(a, si, g0 + lane), g0 + lane, status);
+            cur = resolve(a, si, have_first ? first_raw : issue_index(a, si, g0 + lane), g0 + lane, status);
             issue_blocks<kPre>(si, cur, pre);
         }
+        have_first = false;
         if (next_busy && !have_next_raw) next_raw = issue_index(a, si, g0n + lane);
         const LaneTask L = cur;
         const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt

@@ -171,11 +171,29 @@ __global__ __launch_bounds__(kScanThreads) void encode_offsets_kernel(const Enco
     const uint32_t *sz = a.sizes + (uint64_t)seg * n;
     uint64_t *chunk_off = reinterpret_cast<uint64_t *>(out + kHeaderBytes);
 
-    // each thread owns a run of consecutive chunks
+    // Each thread owns a run of consecutive chunks.  Up to four chunks a
+    // thread (up to 4096 chunks a stream) come in one 16-byte load and stay
+    // in registers; longer runs loop.
     const uint32_t per = (n + kScanThreads - 1) / kScanThreads;
     const uint32_t lo = min(n, tid * per), hi = min(n, lo + per);
     uint64_t mine = 0;
-    for (uint32_t i = lo; i < hi; ++i) mine += sz[i];
+    uint32_t s4[4] = {0, 0, 0, 0};
+    const bool quad = per <= 4;
+    if (quad) {
+        if (per == 4 && hi == lo + 4 && !((uintptr_t)(sz + lo) & 15)) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(sz + lo);
+            s4[0] = v.x;
+            s4[1] = v.y;
+            s4[2] = v.z;
+            s4[3] = v.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s4[k] = lo + k < hi ? sz[lo + k] : 0u;
+        }
+        mine = (uint64_t)s4[0] + s4[1] + s4[2] + s4[3];
+    } else {
+        for (uint32_t i = lo; i < hi; ++i) mine += sz[i];
+    }
     uint64_t x = mine;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -191,9 +209,28 @@ __global__ __launch_bounds__(kScanThreads) void encode_offsets_kernel(const Enco
         total += wsum[w];
     }
     uint64_t run = before + x - mine;   // units before chunk lo
-    for (uint32_t i = lo; i < hi; ++i) {
-        chunk_off[i] = run * 16;
-        run += sz[i];
+    if (quad) {
+        uint64_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[k] = run * 16;
+            run += s4[k];
+        }
+        if (per == 4 && hi == lo + 4 && !((uintptr_t)(chunk_off + lo) & 15)) {
+            ulonglong2 *dst = reinterpret_cast<ulonglong2 *>(chunk_off + lo);
+            dst[0] = make_ulonglong2(o[0], o[1]);
+            dst[1] = make_ulonglong2(o[2], o[3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (lo + k < hi) chunk_off[lo + k] = o[k];
+            }
+        }
+    } else {
+        for (uint32_t i = lo; i < hi; ++i) {
+            chunk_off[i] = run * 16;
+            run += sz[i];
+        }
     }
     const uint64_t payload = total * 16;
     const uint64_t end = (uint64_t)a.payload_offset + payload;
