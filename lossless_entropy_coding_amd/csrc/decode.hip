@@ -68,7 +68,11 @@ struct ColBits {
         return __builtin_amdgcn_alignbit(w[0], w[64], ~yy);
     }
     __device__ __forceinline__ uint32_t win() const { return at(Y); }
-    __device__ __forceinline__ uint64_t win64() const { return ((uint64_t)at(Y) << 32) | at(Y + 32u); }
+    __device__ __forceinline__ uint64_t win64() const {   // rows k, k + 1, k + 2 of the column
+        lds_word *w = (lds_word *)(size_t)(((Y >> 5) << 8) | col);
+        const uint32_t d0 = w[0], d1 = w[64], d2 = w[128];
+        return ((uint64_t)__builtin_amdgcn_alignbit(d0, d1, ~Y) << 32) | __builtin_amdgcn_alignbit(d1, d2, ~Y);
+    }
     __device__ __forceinline__ void adv(uint32_t l) { Y += l; }
     __device__ __forceinline__ void prepare() { Y = min(Y, ylim); }
     __device__ __forceinline__ uint64_t bit() const { return Y - base; }   // lane-relative position
@@ -220,10 +224,33 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
         }
         return __builtin_amdgcn_perm(c2.e, c1.e, 0x0c0c0400u);   // byte 0 of c1.e, byte 0 of c2.e
     };
+    // Huffman: four codes from one 64-bit window when all four are covered by
+    // the table (at most 13 bits each, so the second pair's 32-bit window lies
+    // inside the 64 bits); otherwise (rare) the pair step twice.  Returns the
+    // four bytes in order.
+    auto four = [&]() __attribute__((always_inline)) -> uint32_t {
+        const uint64_t W = S.win64();
+        const uint32_t w = (uint32_t)(W >> 32);
+        const uint32_t e1 = l1[w >> (32 - kHuffBits)];
+        const uint32_t e2 = l1[(w << (e1 >> 8)) >> (32 - kHuffBits)];
+        const uint32_t L1 = (e1 >> 8) + (e2 >> 8);
+        const uint32_t v = (uint32_t)((W << L1) >> 32);
+        const uint32_t e3 = l1[v >> (32 - kHuffBits)];
+        const uint32_t e4 = l1[(v << (e3 >> 8)) >> (32 - kHuffBits)];
+        if (min(min(e1, e2), min(e3, e4)) < 256u) {
+            const uint32_t p0 = two(), p1 = two();
+            return p0 | (p1 << 16);
+        }
+        S.adv(L1 + (e3 >> 8) + (e4 >> 8));
+        return __builtin_amdgcn_perm(e2, e1, 0x0c0c0400u) | (__builtin_amdgcn_perm(e4, e3, 0x0c0c0400u) << 16);
+    };
     // eight codes -> two output words
     auto eight = [&](uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {
         S.prepare();
-        if (PAIRS) {
+        if (CODEC == EC_CODEC_HUFFMAN && FULL == 2) {
+            lo = four();
+            hi = four();
+        } else if (PAIRS) {
             const uint32_t p0 = two(), p1 = two(), p2 = two(), p3 = two();
             lo = p0 | (p1 << 16);
             hi = p2 | (p3 << 16);
