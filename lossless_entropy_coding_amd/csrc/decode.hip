@@ -224,13 +224,25 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
         }
         return __builtin_amdgcn_perm(c2.e, c1.e, 0x0c0c0400u);   // byte 0 of c1.e, byte 0 of c2.e
     };
-    // Huffman: four codes from one 64-bit window when all four are covered by
-    // the table (at most 13 bits each, so the second pair's 32-bit window lies
-    // inside the 64 bits); otherwise (rare) the pair step twice.  Returns the
-    // four bytes in order.
+    // Four codes from one 64-bit window: the second pair's 32-bit window lies
+    // inside the 64 bits when a pair has at most 32 bits (QLC: codes of at
+    // most 11 bits; EG in pair mode: at most 16; Huffman: codes the table
+    // covers, at most 13 bits each, else (rare) the pair step twice).
+    // Returns the four bytes in order.
     auto four = [&]() __attribute__((always_inline)) -> uint32_t {
         const uint64_t W = S.win64();
         const uint32_t w = (uint32_t)(W >> 32);
+        if (CODEC != EC_CODEC_HUFFMAN) {
+            const Code c1 = code_at(w);
+            const Code c2 = code_at(w << c1.len);
+            const uint32_t L1 = c1.len + c2.len;
+            const uint32_t v = (uint32_t)((W << L1) >> 32);
+            const Code c3 = code_at(v);
+            const Code c4 = code_at(v << c3.len);
+            S.adv(L1 + c3.len + c4.len);
+            if (CODEC == EC_CODEC_QLC) bad |= c1.e | c2.e | c3.e | c4.e;
+            return __builtin_amdgcn_perm(c2.e, c1.e, 0x0c0c0400u) | (__builtin_amdgcn_perm(c4.e, c3.e, 0x0c0c0400u) << 16);
+        }
         const uint32_t e1 = l1[w >> (32 - kHuffBits)];
         const uint32_t e2 = l1[(w << (e1 >> 8)) >> (32 - kHuffBits)];
         const uint32_t L1 = (e1 >> 8) + (e2 >> 8);
@@ -247,7 +259,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
     // eight codes -> two output words
     auto eight = [&](uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {
         S.prepare();
-        if (CODEC == EC_CODEC_HUFFMAN && FULL == 2) {
+        if (FULL && PAIRS) {
             lo = four();
             hi = four();
         } else if (PAIRS) {
