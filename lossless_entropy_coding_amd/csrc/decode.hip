@@ -165,16 +165,28 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
                                                const uint8_t *symtab, const DeepTables *dt, uint32_t max_len,
                                                uint32_t lens, uint32_t k_eg) {
     uint32_t bad = 0;
+    // QLC code lengths by area, one byte each: areas 0-3 in llo, 4-7 in lhi
+    uint32_t llo = 0, lhi = 0;
+    if (CODEC == EC_CODEC_QLC) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            llo |= ((lens >> (4 * k)) & 15u) << (8 * k);
+            lhi |= ((lens >> (4 * k + 16)) & 15u) << (8 * k);
+        }
+    }
     // The code that starts window w: its table entry (symbol in byte 0; for
     // QLC bit 8 flags an unused suffix) and its length.  QLC takes the length
-    // from the 3-bit prefix through the packed constant, off the memory
-    // dependency chain; Huffman and EG entries carry it in bits 8 and up.
+    // from the 3-bit prefix, off the memory dependency chain: a funnel shift
+    // puts the prefix in byte 0 of a byte-select word whose other bytes
+    // select zero, and a byte permute picks that area's length.  Huffman and
+    // EG entries carry the length in bits 8 and up.
     struct Code {
         uint32_t e, len;
     };
     auto code_at = [&](uint32_t w) __attribute__((always_inline)) -> Code {
         if (CODEC == EC_CODEC_QLC) {
-            return Code{l1[w >> 21], (lens >> ((w >> 29) << 2)) & 15u};
+            const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, w, 29);   // 0x0c0c0c00 | w >> 29
+            return Code{l1[w >> 21], __builtin_amdgcn_perm(lhi, llo, sel)};
         } else if (CODEC == EC_CODEC_HUFFMAN) {
             uint32_t e = l1[w >> (32 - kHuffBits)];
             if (e < 256u) e = huff_deep(S.win64(), dt, symtab, max_len);
