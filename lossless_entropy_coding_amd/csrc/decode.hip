@@ -4,19 +4,19 @@
 // index, so one lane decodes one sub-chunk serially and a wave64 decodes 64
 // sub-chunks side by side.  Each lane first copies the 16-byte blocks that
 // hold its sub-chunk from the payload into its own column of the wave's LDS
-// region: word k of lane l's bits goes to row k, column l.  A 32-bit window
-// at any bit position is then one two-row LDS read (rows k and k + 1 of the
-// lane's column) plus a funnel shift, and the 64 lanes of a read always hit
-// 64 different banks, whatever their positions: a contiguous copy of the
-// compressed span would have the lanes read at scattered addresses, which
-// costs several times more in bank conflicts.  (A global load inside the
+// region: word k of lane l's bits goes to row k, column l.  A 64-bit window
+// at any bit position is then one read of three rows of the lane's column
+// plus two funnel shifts, and the 64 lanes of a read always hit 64 different
+// banks, whatever their positions (a contiguous copy of the compressed span
+// has the lanes read at scattered addresses: about twice the LDS time in bank
+// conflicts).  One window serves four codes.  (A global load inside the
 // decode loop would stall on the output stores too: one counter tracks both.)
 // A sub-chunk too long for the region (data that barely compresses) is
 // decoded straight from global memory.
-//   QLC      the 3-bit prefix gives the code length through a packed constant
-//            (no memory access on the dependency chain); the top 11 bits index
-//            a 2048-entry LDS table that yields the byte or flags an unused
-//            suffix.
+//   QLC      the 3-bit prefix gives the code length through a funnel shift
+//            and a byte permute of the per-area lengths (no memory access on
+//            the dependency chain); the top 11 bits index a 2048-entry LDS
+//            table that yields the byte or flags an unused suffix.
 //   Huffman  the top 13 bits index a 16 KiB LDS table that yields the byte
 //            and the length of every code of up to 13 bits; longer codes
 //            (rare) are found by comparing a 40-bit window against the
@@ -38,7 +38,7 @@ constexpr uint32_t kRowBytes = 64 * 4;               // one word per lane
 // Rows past the last region that a lane may read: a position is clamped to
 // its region at the start of every 8 codes, which then move it by at most
 // 8 codes of the longest length the codec can read (QLC 11 bits, EG 25,
-// Huffman 40), and a window reads up to two rows further.
+// Huffman 40), and a window reads up to three rows from there.
 template <int CODEC>
 constexpr uint32_t guard_rows() {
     constexpr uint32_t kMaxCode = CODEC == EC_CODEC_QLC ? 11 : CODEC == EC_CODEC_HUFFMAN ? EC_MAX_CODE_LEN : 25;
