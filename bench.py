@@ -299,8 +299,10 @@ def run_single(args, ec, torch):
 
 def run_batch(args, ec, torch):
     """64 x 4 MiB shards: single-stage (one fixed avg-PMF Huffman codebook)
-    against three-stage (per-shard histogram, per-shard codebook built on the
-    host, codebook lengths embedded in each stream)."""
+    against three-stage (per-shard histogram, per-shard codebook, codebook
+    lengths embedded in each stream), the codebooks built on the GPU
+    (three_stage) or on the host after a copy of the histograms
+    (three_stage_host)."""
     import synth
     dev = torch.device("cuda:0")
     C = 16384
@@ -314,13 +316,15 @@ def run_batch(args, ec, torch):
     torch.cuda.synchronize()
     counts = [int(c) for c in pooled_d.cpu().numpy()]
     fixed = ec.Codebook.huffman(counts)
-    stride = (ec.max_encoded_bytes(fixed, n, C, True) + 255) // 256 * 256 + 4096
+    stride = max(ec.max_encoded_bytes(fixed, n, C, True), ec.own_max_encoded_bytes(n, C, True))
+    stride = (stride + 255) // 256 * 256 + 4096
     out = torch.empty((S, stride), dtype=torch.uint8, device=dev)
     y = torch.empty((S, n), dtype=torch.uint8, device=dev)
     lens = torch.zeros(S, dtype=torch.int64, device=dev)
     status = torch.zeros(S, dtype=torch.int32, device=dev)
     hist = torch.empty((S, 256), dtype=torch.int64, device=dev)
     kl = torch.empty(S, dtype=torch.float32, device=dev)
+    tables = torch.empty((S, ec.device_codebook_bytes()), dtype=torch.uint8, device=dev)
 
     def single():
         ec.byte_histogram(x_d, out=hist)
@@ -329,15 +333,21 @@ def run_batch(args, ec, torch):
         ec.decode_batch(fixed, out, n, out=y, status=status)
 
     def three():
+        ec.byte_histogram(x_d, out=hist)                                  # frequency analysis
+        ec.build_huffman_device(hist, out=tables, status=status)          # codebook generation
+        ec.encode_batch_device(tables, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
+        ec.decode_batch_device(tables, out, n, out=y, status=status)
+
+    def three_host():
         ec.byte_histogram(x_d, out=hist)
-        h = hist.cpu().numpy()          # frequency analysis -> host
-        cbs = [ec.Codebook.huffman([int(c) for c in row]) for row in h]   # codebook generation
+        h = hist.cpu().numpy()          # histograms -> host
+        cbs = [ec.Codebook.huffman([int(c) for c in row]) for row in h]
         ec.encode_batch(cbs, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
         ec.decode_batch(cbs, out, n, out=y, status=status)
         return cbs
 
     res = {}
-    for name, fn in (("single_stage", single), ("three_stage", three)):
+    for name, fn in (("single_stage", single), ("three_stage", three), ("three_stage_host", three_host)):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()

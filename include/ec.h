@@ -22,10 +22,15 @@
  *     function and released with ec_codebook_free.  Its device tables are
  *     allocated on the current device at its first GPU use and freed with
  *     the handle.
- *   - The encoder keeps a small look-back scratch buffer per device (8 bytes
- *     per chunk), allocated at first use and kept until the process ends.
- *     GPU calls that overlap in time on one device (different streams) share
- *     it and race: order them (one stream, or events).
+ *   - The library keeps two scratch buffers per device, allocated at first
+ *     use, grown by doubling and kept until the process ends: the encoder's
+ *     chunk sizes (4 bytes per chunk of a launch) and the histogram's
+ *     partial counts (1 KiB per partial row).  GPU calls of the same kind
+ *     that overlap in time on one device (different streams) share one and
+ *     race: order them (one stream, or events).
+ *   - Device codebook tables (the *_device functions) live in caller-owned
+ *     device memory: n_seg consecutive tables of ec_device_codebook_bytes()
+ *     bytes each, 16-byte aligned.
  *
  * Errors
  *   - Functions return an ec_error code for argument, allocation and launch
@@ -79,8 +84,9 @@ typedef enum ec_error {
 #define EC_S_CORRUPT 0x2u           /* payload or index does not decode consistently */
 #define EC_S_BAD_HEADER 0x4u        /* magic, version, sizes or layout wrong */
 #define EC_S_CODEBOOK_MISMATCH 0x8u /* stream made with another codebook or codec */
-#define EC_S_INTERNAL 0x10u         /* encoder look-back wait expired (overlapping calls on one
-                                       device); the chunk's payload was not written */
+#define EC_S_BAD_CODEBOOK 0x10u     /* device codebook build: a code would exceed EC_MAX_CODE_LEN
+                                       bits (or a count is 2^55 or more); the table is unusable
+                                       (codec 0) and encodes that use it set this bit too */
 
 typedef enum ec_codec {
     EC_CODEC_QLC = 1,
@@ -119,7 +125,8 @@ int qlc_build_codebook(const uint64_t counts[256], const uint16_t area_size[8],
  *   counts[256]  summed byte counts of the calibration data (for shards of
  *                equal size this is proportional to their average PMF).
  *                Every symbol is weighted counts[s] + 1 so that symbols not
- *                seen in calibration still get a code.
+ *                seen in calibration still get a code.  Counts must be
+ *                below 2^55 (EC_E_INVAL otherwise).
  * The tree merges the two lightest nodes, ties ordered by (weight, leaves
  * before internal nodes, byte value / creation order); codes are canonical
  * in (length, byte) order.  EC_E_UNSUPPORTED if a code exceeds
@@ -233,6 +240,74 @@ int entropy_encode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const ui
 int entropy_decode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in,
                          uint64_t in_stride, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride,
                          uint32_t *d_status, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Device-resident codebooks: the three-stage path without a host round trip
+ * (single-stage Huffman page, abstract: frequency analysis, codebook
+ * generation, encoding with the shard's own codebook, which travels with the
+ * data).  Histogram rows -> huff_build_codebooks_device -> the *_device
+ * encode and decode, all enqueued on one stream.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of one device codebook table (a multiple of 16). */
+uint64_t ec_device_codebook_bytes(void);
+
+/*
+ * Build one Huffman codebook per segment on the GPU from d_counts[s * 256 + b]
+ * (as written by byte_histogram), with exactly the rule and the tables of
+ * huff_build_codebook (weights counts + 1, the same merge order and tie rule,
+ * canonical codes, the same codebook id).
+ *   n_seg     1..65535
+ *   d_tables  n_seg * ec_device_codebook_bytes() bytes, 16-byte aligned;
+ *             overwritten
+ *   d_status  device u32[n_seg], caller-zeroed, or NULL: EC_S_BAD_CODEBOOK
+ *             when the segment's code would need more than EC_MAX_CODE_LEN
+ *             bits or a count is 2^55 or more (its table is then unusable:
+ *             codec 0, all zero).
+ */
+int huff_build_codebooks_device(const uint64_t *d_counts, uint32_t n_seg, void *d_tables, uint32_t *d_status,
+                                hipStream_t stream);
+
+/*
+ * Copy a host-built codebook's table, in the device table format, to host
+ * memory `table` (ec_device_codebook_bytes() bytes).  Uploaded into a device
+ * table array it serves the *_device functions like a device-built one.
+ */
+int ec_codebook_export(const ec_codebook *cb, void *table);
+
+/*
+ * Capacity per stream that always suffices when segment s is coded with a
+ * Huffman codebook built from its own byte histogram (three-stage path):
+ * such a code never spends more than 8 bits a symbol on the segment as a
+ * whole (a Huffman code is no longer than the 8-bit fixed code on its
+ * weights counts + 1, and 256 complete-code lengths sum to at least 2048),
+ * plus at most 16 bytes of padding per chunk.  0 on bad arguments.
+ */
+uint64_t entropy_own_max_encoded_bytes(uint64_t n, uint32_t chunk_symbols, uint32_t embed_lengths);
+
+/*
+ * entropy_encode_batch with the codebooks in device memory: segment s uses
+ * the table at d_tables + s * ec_device_codebook_bytes().  n_seg 1..
+ * EC_MAX_BATCH.  The host does not read the tables, so it cannot size
+ * anything from them: chunks whose table has codes longer than 26 bits are
+ * packed by the general row-by-row packer; a stream longer than out_stride
+ * sets EC_S_CAPACITY (see entropy_own_max_encoded_bytes).  A table marked
+ * unusable sets EC_S_BAD_CODEBOOK.
+ */
+int entropy_encode_batch_device(const void *d_tables, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
+                                uint64_t in_stride, uint32_t chunk_symbols, uint32_t embed_lengths,
+                                uint8_t *d_out, uint64_t out_stride, uint64_t *d_out_len, uint32_t *d_status,
+                                hipStream_t stream);
+
+/*
+ * entropy_decode_batch with the codebooks in device memory (as for
+ * entropy_encode_batch_device); `codec` is the codec of every table
+ * (EC_CODEC_*).  A stream whose header names another codec or codebook id
+ * than its table sets EC_S_CODEBOOK_MISMATCH.
+ */
+int entropy_decode_batch_device(const void *d_tables, uint32_t codec, uint32_t n_seg, const uint8_t *d_in,
+                                uint64_t in_stride, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride,
+                                uint32_t *d_status, hipStream_t stream);
 
 /*
  * Byte histogram of n_seg segments (single-stage Huffman page, method step

@@ -19,13 +19,14 @@ __all__ = [
     "byte_histogram", "pmf_average", "pmf_kl", "huff_code_lengths", "index_bytes",
     "max_encoded_bytes", "QLC_BASE", "QLC_ADAPTED", "CODEC_QLC", "CODEC_HUFFMAN",
     "CODEC_EXP_GOLOMB", "S_CAPACITY", "S_CORRUPT", "S_BAD_HEADER", "S_CODEBOOK_MISMATCH",
-    "S_INTERNAL", "EXPORTS",
+    "S_BAD_CODEBOOK", "EXPORTS", "device_codebook_bytes", "build_huffman_device", "own_max_encoded_bytes",
+    "encode_batch_device", "decode_batch_device",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libec.so")
 
 CODEC_QLC, CODEC_HUFFMAN, CODEC_EXP_GOLOMB = 1, 2, 3
-S_CAPACITY, S_CORRUPT, S_BAD_HEADER, S_CODEBOOK_MISMATCH, S_INTERNAL = 0x1, 0x2, 0x4, 0x8, 0x10
+S_CAPACITY, S_CORRUPT, S_BAD_HEADER, S_CODEBOOK_MISMATCH, S_BAD_CODEBOOK = 0x1, 0x2, 0x4, 0x8, 0x10
 MAX_BATCH = 128
 
 # QLC area layouts (symbols per area, suffix bits per area)
@@ -58,6 +59,12 @@ EXPORTS = {
     "entropy_encode_batch": (_int, [ctypes.POINTER(_vp), _u32, _vp, _u64, _u64, _u32, _u32, _vp, _u64, _vp,
                                     _vp, _vp]),
     "entropy_decode_batch": (_int, [ctypes.POINTER(_vp), _u32, _vp, _u64, _vp, _u64, _u64, _vp, _vp]),
+    "ec_device_codebook_bytes": (_u64, []),
+    "huff_build_codebooks_device": (_int, [_vp, _u32, _vp, _vp, _vp]),
+    "ec_codebook_export": (_int, [_vp, _vp]),
+    "entropy_own_max_encoded_bytes": (_u64, [_u64, _u32, _u32]),
+    "entropy_encode_batch_device": (_int, [_vp, _u32, _vp, _u64, _u64, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
+    "entropy_decode_batch_device": (_int, [_vp, _u32, _u32, _vp, _u64, _vp, _u64, _u64, _vp, _vp]),
     "byte_histogram": (_int, [_vp, _u64, _u32, _u64, _vp, _vp]),
     "pmf_average": (_int, [_vp, _u32, _vp, _vp]),
     "pmf_kl": (_int, [_vp, _u32, _vp, _u32, _vp, _vp]),
@@ -174,6 +181,12 @@ class Codebook:
         return dict(codec=codec.value, max_len=mx.value, codebook_id=cid.value, code_len=list(lens),
                     code=list(code), rank_to_sym=list(r2s), eg_k=k.value)
 
+    def export(self) -> bytes:
+        """The codebook's table in the device table format (ec_codebook_export)."""
+        buf = (ctypes.c_uint8 * device_codebook_bytes())()
+        _check(lib().ec_codebook_export(self._h, buf), "ec_codebook_export")
+        return bytes(buf)
+
     @property
     def codec(self) -> int:
         return self.info()["codec"]
@@ -284,6 +297,76 @@ def decode_batch(cbs, data: torch.Tensor, seg_n: int, out: torch.Tensor | None =
         status = torch.zeros(S, dtype=torch.int32, device=data.device)
     _check(lib().entropy_decode_batch(_handles(cbl), S, _ptr(data), data.stride(0), _ptr(out), seg_n,
                                       out.stride(0), _ptr(status), _stream(stream)), "entropy_decode_batch")
+    return out[:, :seg_n], status
+
+
+def device_codebook_bytes() -> int:
+    return int(lib().ec_device_codebook_bytes())
+
+
+def own_max_encoded_bytes(n: int, chunk_symbols: int, embed_lengths: bool = False) -> int:
+    return int(lib().entropy_own_max_encoded_bytes(n, chunk_symbols, int(embed_lengths)))
+
+
+def _tables_cuda(tables: torch.Tensor, S: int):
+    _u8_cuda(tables, "tables")
+    if tables.numel() < S * device_codebook_bytes():
+        raise ECError("tables must hold %d device codebooks" % S)
+
+
+def build_huffman_device(counts: torch.Tensor, out: torch.Tensor | None = None,
+                         status: torch.Tensor | None = None, stream=None):
+    """huff_build_codebooks_device over the rows of an int64 [S, 256] count
+    tensor.  Returns (tables uint8 [S, device_codebook_bytes()], status int32[S])."""
+    c = counts.view(-1, 256)
+    if c.dtype != torch.int64 or not c.is_cuda or not c.is_contiguous():
+        raise ECError("counts must be a contiguous int64 CUDA tensor of rows of 256")
+    S = c.shape[0]
+    if out is None:
+        out = torch.empty((S, device_codebook_bytes()), dtype=torch.uint8, device=c.device)
+    _tables_cuda(out, S)
+    if status is None:
+        status = torch.zeros(S, dtype=torch.int32, device=c.device)
+    _check(lib().huff_build_codebooks_device(_ptr(c), S, _ptr(out), _ptr(status), _stream(stream)),
+           "huff_build_codebooks_device")
+    return out, status
+
+
+def encode_batch_device(tables: torch.Tensor, x: torch.Tensor, chunk_symbols: int, embed_lengths: bool = False,
+                        out: torch.Tensor | None = None, out_len: torch.Tensor | None = None,
+                        status: torch.Tensor | None = None, stream=None):
+    """entropy_encode_batch_device over the rows of a 2-D uint8 tensor with
+    row s's codebook table at tables[s].  Without `out`, streams get the
+    own-histogram capacity (entropy_own_max_encoded_bytes)."""
+    _u8_cuda(x, "x")
+    S, seg_n = x.shape
+    _tables_cuda(tables, S)
+    if out is None:
+        stride = (own_max_encoded_bytes(seg_n, chunk_symbols, embed_lengths) + 255) // 256 * 256
+        out = torch.empty((S, stride), dtype=torch.uint8, device=x.device)
+    if out_len is None:
+        out_len = torch.zeros(S, dtype=torch.int64, device=x.device)
+    if status is None:
+        status = torch.zeros(S, dtype=torch.int32, device=x.device)
+    _check(lib().entropy_encode_batch_device(_ptr(tables), S, _ptr(x), seg_n, x.stride(0), chunk_symbols,
+                                             int(embed_lengths), _ptr(out), out.stride(0), _ptr(out_len),
+                                             _ptr(status), _stream(stream)), "entropy_encode_batch_device")
+    return out, out_len, status
+
+
+def decode_batch_device(tables: torch.Tensor, data: torch.Tensor, seg_n: int, codec: int = CODEC_HUFFMAN,
+                        out: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
+    """entropy_decode_batch_device of the rows of a 2-D uint8 tensor of streams."""
+    _u8_cuda(data, "data")
+    S = data.shape[0]
+    _tables_cuda(tables, S)
+    if out is None:
+        out = torch.empty((S, (max(seg_n, 1) + 15) // 16 * 16), dtype=torch.uint8, device=data.device)
+    if status is None:
+        status = torch.zeros(S, dtype=torch.int32, device=data.device)
+    _check(lib().entropy_decode_batch_device(_ptr(tables), int(codec), S, _ptr(data), data.stride(0), _ptr(out),
+                                             seg_n, out.stride(0), _ptr(status), _stream(stream)),
+           "entropy_decode_batch_device")
     return out[:, :seg_n], status
 
 

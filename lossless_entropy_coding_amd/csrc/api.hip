@@ -101,11 +101,24 @@ uint64_t max_payload(uint64_t n, uint32_t C, uint32_t max_len) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? EC_OK : EC_E_HIP; }
 
-int encode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
+// Where a launch's codebook tables come from: library handles (uploaded on
+// first use, their sizes known to the host) or a caller-owned device array of
+// tables the host never reads.
+struct TableSrc {
+    const ec_codebook *const *cbs;
+    const uint8_t *dev;
+};
+
+const DevTables *dev_table(const uint8_t *base, uint32_t i) {
+    return reinterpret_cast<const DevTables *>(base + (uint64_t)i * sizeof(DevTables));
+}
+
+int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
                 uint64_t in_stride, uint32_t C, uint32_t embed, uint8_t *d_out, uint64_t out_stride,
                 uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t s) {
-    if (!cbs || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_out || !d_out_len || !chunk_ok(C)) return EC_E_INVAL;
-    if (seg_n > kMaxSegSymbols || (seg_n && !d_in)) return EC_E_INVAL;
+    if ((!ts.cbs && !ts.dev) || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_out || !d_out_len || !chunk_ok(C))
+        return EC_E_INVAL;
+    if (seg_n > kMaxSegSymbols || (seg_n && !d_in) || !aligned16(ts.dev)) return EC_E_INVAL;
     if (!aligned16(d_in) || !aligned16(d_out)) return EC_E_INVAL;
     if (n_seg > 1 && (in_stride % 16 || out_stride % 16 || in_stride < seg_n || out_stride < out_cap))
         return EC_E_INVAL;
@@ -117,11 +130,20 @@ int encode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_
     memset(&a, 0, sizeof(a));
     uint32_t max_len = 1;
     for (uint32_t i = 0; i < n_seg; ++i) {
-        if (!cbs[i]) return EC_E_INVAL;
-        int rc = device_tables(cbs[i], &a.tabs[i]);
+        if (ts.dev) {
+            a.tabs[i] = dev_table(ts.dev, i);
+            continue;
+        }
+        const ec_codebook *cb = ts.cbs[i];
+        if (!cb) return EC_E_INVAL;
+        int rc = device_tables(cb, &a.tabs[i]);
         if (rc) return rc;
-        max_len = cbs[i]->host.max_len > max_len ? cbs[i]->host.max_len : max_len;
-        if (embed && cbs[i]->host.codec != EC_CODEC_HUFFMAN) return EC_E_INVAL;
+        max_len = cb->host.max_len > max_len ? cb->host.max_len : max_len;
+        if (embed && cb->host.codec != EC_CODEC_HUFFMAN) return EC_E_INVAL;
+    }
+    if (ts.dev) {
+        max_len = EC_MAX_CODE_LEN;
+        a.tables_unread = 1;
     }
     a.in = d_in;
     a.in_stride = in_stride;
@@ -147,21 +169,30 @@ int encode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_
     return hip_rc(launch_encode(a, s));
 }
 
-int decode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t in_stride,
+// codec: the tables' codec when they come from device memory (ts.dev).
+int decode_impl(TableSrc ts, uint32_t codec, uint32_t n_seg, const uint8_t *d_in, uint64_t in_stride,
                 uint64_t in_len, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride, uint32_t *d_status,
                 hipStream_t s) {
-    if (!cbs || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_in || in_len < kHeaderBytes) return EC_E_INVAL;
-    if (seg_n > kMaxSegSymbols || (seg_n && !d_out)) return EC_E_INVAL;
+    if ((!ts.cbs && !ts.dev) || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_in || in_len < kHeaderBytes)
+        return EC_E_INVAL;
+    if (seg_n > kMaxSegSymbols || (seg_n && !d_out) || !aligned16(ts.dev)) return EC_E_INVAL;
     if (!aligned16(d_in) || !aligned16(d_out)) return EC_E_INVAL;
     if (n_seg > 1 && (in_stride % 16 || out_stride % 16 || in_stride < in_len || out_stride < seg_n))
         return EC_E_INVAL;
     DecodeArgs a;
     memset(&a, 0, sizeof(a));
-    const uint32_t codec = cbs[0] ? cbs[0]->host.codec : 0;
-    for (uint32_t i = 0; i < n_seg; ++i) {
-        if (!cbs[i] || cbs[i]->host.codec != codec) return EC_E_INVAL;
-        int rc = device_tables(cbs[i], &a.tabs[i]);
-        if (rc) return rc;
+    uint32_t max_len = EC_MAX_CODE_LEN;
+    if (ts.dev) {
+        if (codec < EC_CODEC_QLC || codec > EC_CODEC_EXP_GOLOMB) return EC_E_INVAL;
+        for (uint32_t i = 0; i < n_seg; ++i) a.tabs[i] = dev_table(ts.dev, i);
+    } else {
+        codec = ts.cbs[0] ? ts.cbs[0]->host.codec : 0;
+        for (uint32_t i = 0; i < n_seg; ++i) {
+            if (!ts.cbs[i] || ts.cbs[i]->host.codec != codec) return EC_E_INVAL;
+            int rc = device_tables(ts.cbs[i], &a.tabs[i]);
+            if (rc) return rc;
+        }
+        max_len = ts.cbs[0]->host.max_len;
     }
     a.in = d_in;
     a.in_stride = in_stride;
@@ -172,7 +203,7 @@ int decode_impl(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_
     a.status = d_status;
     a.n_seg = n_seg;
     a.blocks_per_seg = (uint32_t)((seg_n + kSub - 1) / kSub);
-    return hip_rc(launch_decode(a, codec, cbs[0]->host.max_len, s));
+    return hip_rc(launch_decode(a, codec, max_len, s));
 }
 
 }  // namespace
@@ -196,7 +227,7 @@ const char *ec_error_string(int code) {
 
 const char *ec_status_string(uint32_t st) {
     if (st == 0) return "ok";
-    if (st & EC_S_INTERNAL) return "internal: encoder look-back wait expired";
+    if (st & EC_S_BAD_CODEBOOK) return "device-built codebook unusable (code longer than EC_MAX_CODE_LEN)";
     if (st & EC_S_BAD_HEADER) return "bad stream header";
     if (st & EC_S_CODEBOOK_MISMATCH) return "stream made with another codebook";
     if (st & EC_S_CORRUPT) return "corrupt stream";
@@ -213,7 +244,7 @@ int huff_build_codebook(const uint64_t counts[256], ec_codebook **out) {
     if (!counts || !out) return EC_E_INVAL;
     uint64_t w[256];
     for (int s = 0; s < 256; ++s) {
-        if (counts[s] == UINT64_MAX) return EC_E_INVAL;
+        if (counts[s] >= (1ull << 55)) return EC_E_INVAL;   // node weights must not overflow
         w[s] = counts[s] + 1;
     }
     uint8_t len[256];
@@ -279,26 +310,67 @@ uint64_t entropy_max_encoded_bytes(const ec_codebook *cb, uint64_t n, uint32_t c
 int entropy_encode(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols, uint8_t *d_out,
                    uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream) {
     const ec_codebook *cbs[1] = {cb};
-    return encode_impl(cbs, 1, d_in, n, 0, chunk_symbols, 0, d_out, 0, out_cap, d_out_len, d_status, stream);
+    return encode_impl(TableSrc{cbs, nullptr}, 1, d_in, n, 0, chunk_symbols, 0, d_out, 0, out_cap, d_out_len,
+                       d_status, stream);
 }
 
 int entropy_decode(const ec_codebook *cb, const uint8_t *d_in, uint64_t in_len, uint8_t *d_out, uint64_t n,
                    uint32_t *d_status, hipStream_t stream) {
     const ec_codebook *cbs[1] = {cb};
-    return decode_impl(cbs, 1, d_in, 0, in_len, d_out, n, 0, d_status, stream);
+    return decode_impl(TableSrc{cbs, nullptr}, 0, 1, d_in, 0, in_len, d_out, n, 0, d_status, stream);
 }
 
 int entropy_encode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
                          uint64_t in_stride, uint32_t chunk_symbols, uint32_t embed_lengths, uint8_t *d_out,
                          uint64_t out_stride, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream) {
-    return encode_impl(cbs, n_seg, d_in, seg_n, in_stride, chunk_symbols, embed_lengths, d_out, out_stride,
-                       out_stride, d_out_len, d_status, stream);
+    if (!cbs) return EC_E_INVAL;
+    return encode_impl(TableSrc{cbs, nullptr}, n_seg, d_in, seg_n, in_stride, chunk_symbols, embed_lengths, d_out,
+                       out_stride, out_stride, d_out_len, d_status, stream);
 }
 
 int entropy_decode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t in_stride,
                          uint8_t *d_out, uint64_t seg_n, uint64_t out_stride, uint32_t *d_status,
                          hipStream_t stream) {
-    return decode_impl(cbs, n_seg, d_in, in_stride, in_stride, d_out, seg_n, out_stride, d_status, stream);
+    if (!cbs) return EC_E_INVAL;
+    return decode_impl(TableSrc{cbs, nullptr}, 0, n_seg, d_in, in_stride, in_stride, d_out, seg_n, out_stride,
+                       d_status, stream);
+}
+
+uint64_t ec_device_codebook_bytes(void) { return sizeof(DevTables); }
+
+int huff_build_codebooks_device(const uint64_t *d_counts, uint32_t n_seg, void *d_tables, uint32_t *d_status,
+                                hipStream_t stream) {
+    if (!d_counts || !d_tables || n_seg == 0 || n_seg > 65535 || !aligned16(d_tables)) return EC_E_INVAL;
+    return hip_rc(launch_huff_build(d_counts, n_seg, static_cast<DevTables *>(d_tables), d_status, stream));
+}
+
+int ec_codebook_export(const ec_codebook *cb, void *table) {
+    if (!cb || !table) return EC_E_INVAL;
+    memcpy(table, &cb->host, sizeof(DevTables));
+    return EC_OK;
+}
+
+uint64_t entropy_own_max_encoded_bytes(uint64_t n, uint32_t chunk_symbols, uint32_t embed_lengths) {
+    if (!chunk_ok(chunk_symbols) || n > kMaxSegSymbols) return 0;
+    const Layout l = layout(n, chunk_symbols, embed_lengths);
+    return l.payload_offset + n + 16 * l.n_chunks;
+}
+
+int entropy_encode_batch_device(const void *d_tables, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
+                                uint64_t in_stride, uint32_t chunk_symbols, uint32_t embed_lengths,
+                                uint8_t *d_out, uint64_t out_stride, uint64_t *d_out_len, uint32_t *d_status,
+                                hipStream_t stream) {
+    if (!d_tables) return EC_E_INVAL;
+    return encode_impl(TableSrc{nullptr, static_cast<const uint8_t *>(d_tables)}, n_seg, d_in, seg_n, in_stride,
+                       chunk_symbols, embed_lengths, d_out, out_stride, out_stride, d_out_len, d_status, stream);
+}
+
+int entropy_decode_batch_device(const void *d_tables, uint32_t codec, uint32_t n_seg, const uint8_t *d_in,
+                                uint64_t in_stride, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride,
+                                uint32_t *d_status, hipStream_t stream) {
+    if (!d_tables) return EC_E_INVAL;
+    return decode_impl(TableSrc{nullptr, static_cast<const uint8_t *>(d_tables)}, codec, n_seg, d_in, in_stride,
+                       in_stride, d_out, seg_n, out_stride, d_status, stream);
 }
 
 int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride, uint64_t *d_counts,

@@ -1,0 +1,265 @@
+// Per-shard Huffman codebooks built on the GPU: the codebook-generation stage
+// of the three-stage design ("Single-Stage Huffman Encoder for ML
+// Compression", abstract: frequency analysis, codebook generation and
+// transmission, encoding), so that a batch of shards goes from histogram rows
+// to encoded streams without a trip through host memory.
+//
+// One workgroup of 256 threads builds the tables of one shard, bit for bit
+// the tables the host builder makes from the same counts:
+//   1. weights counts[b] + 1; the leaves in stable order of weight (the rank
+//      of (weight, byte) among all 256, counted by every thread for its byte);
+//   2. the two-queue merge (leaves in sorted order, merged nodes in creation
+//      order; the lighter front is taken, the leaf on a tie), run by one wave
+//      with uniform scalar control flow, the four candidate fronts of a step
+//      read from LDS together;
+//   3. every node's depth by pointer jumping over the parent links (nine
+//      rounds cover the deepest possible tree of 256 leaves);
+//   4. canonical codes: the number of codes of each length, the first code
+//      and first canonical position of each length, each byte's position in
+//      (length, byte) order;
+//   5. the tables: left-aligned encode entries, the 13-bit decode table (a
+//      window's code length is one more than the number of 13-bit limits at
+//      or below it), the 40-bit canonical limits, the canonical symbol order,
+//      the code lengths and the FNV-1a codebook id.
+// A code longer than EC_MAX_CODE_LEN bits, or a count of 2^55 or more, makes
+// the shard's table unusable (codec 0, all entries zero) and sets
+// EC_S_BAD_CODEBOOK in its status word.
+#include "dev_common.h"
+
+namespace ec {
+
+namespace {
+
+constexpr int kBuildThreads = 256;
+constexpr uint32_t kNodes = 511;                 // 256 leaves + 255 merged nodes
+constexpr uint32_t kRoot = 510;
+constexpr uint64_t kHeavy = ~0ull;               // weight of an empty queue front
+constexpr uint64_t kMaxCount = 1ull << 55;       // larger counts could overflow the 64-bit node weights
+
+struct BuildSmem {
+    uint64_t w[256];          // weight by byte; later the code length by byte, as a 64-bit key
+    uint64_t sw[256 + 2];     // leaf weights in sorted order (+2 heavy sentinels)
+    uint64_t iw[256 + 2];     // merged-node weights in creation order
+    uint64_t fcode[48];       // first canonical code of each length
+    uint32_t fidx[48];        // first canonical position of each length
+    uint32_t blc[64];         // codes of each length
+    uint32_t lim13[16];       // end of the codes of length l as 13-bit windows
+    uint16_t par[512];        // parent of node v (leaf at sorted position p: v = p; merged node k: 256 + k)
+    uint16_t anc[512];        // pointer-jumping ancestor
+    uint16_t dep[512];        // distance from v to anc[v]
+    uint8_t sidx[256];        // byte at sorted position
+    uint8_t len[256];         // code length by byte
+    uint8_t symc[256];        // byte at canonical position
+    uint32_t bad, max_len;
+};
+
+// Rank of (key[s], s) among the 256 pairs (key[j], j) in lexicographic
+// order: the number of pairs below it.  Every thread counts for its own s
+// over the same broadcast LDS reads.
+__device__ __forceinline__ uint32_t rank256(const uint64_t *key, uint64_t ks, uint32_t s) {
+    uint32_t r = 0;
+#pragma unroll 8
+    for (uint32_t j = 0; j < 256; ++j) {
+        const uint64_t kj = key[j];
+        r += (kj < ks || (kj == ks && j < s)) ? 1u : 0u;
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return (uint64_t)hi << 32 | lo;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void huff_build_kernel(const uint64_t *counts, DevTables *tabs,
+                                                                   uint32_t *status) {
+    __shared__ BuildSmem sm;
+    const uint32_t tid = threadIdx.x, wave = tid >> 6;
+    const uint32_t seg = blockIdx.x;
+    DevTables *t = tabs + seg;
+
+    // 1. weights and the stable sort of the leaves
+    const uint64_t c = counts[(uint64_t)seg * 256 + tid];
+    const uint64_t ws = c + 1;
+    if (tid == 0) {
+        sm.bad = 0;
+        sm.max_len = 0;
+    }
+    if (tid < 64) sm.blc[tid] = 0;
+    sm.w[tid] = ws;
+    __syncthreads();
+    if (c >= kMaxCount) sm.bad = 1;
+    const uint32_t r = rank256(sm.w, ws, tid);
+    sm.sw[r] = ws;
+    sm.sidx[r] = (uint8_t)tid;
+    if (tid < 2) {
+        sm.sw[256 + tid] = kHeavy;
+        sm.iw[256 + tid] = kHeavy;
+    }
+    __syncthreads();
+
+    // 2. two-queue merge, one wave; li / qh / qt and the fronts are uniform.
+    // A step takes two nodes, so the two leading entries of each queue are
+    // all it can need: they are read together at the start of the step.
+    // Every take finds a node in one of the queues (a step starts with at
+    // least two), so li <= 256 and qh < qt whatever the weights.
+    if (wave == 0) {
+        uint32_t li = 0, qh = 0, qt = 0;
+        for (uint32_t k = 0; k < 255; ++k) {
+            uint64_t l0 = uniform64(sm.sw[li]), l1 = uniform64(sm.sw[li + 1]);
+            uint64_t q0 = qh < qt ? uniform64(sm.iw[qh]) : kHeavy;
+            uint64_t q1 = qh + 1 < qt ? uniform64(sm.iw[qh + 1]) : kHeavy;
+            uint32_t id[2];
+            uint64_t wt[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (li < 256 && l0 <= q0) {   // the leaf on a tie
+                    id[m] = li++;
+                    wt[m] = l0;
+                    l0 = l1;
+                } else {
+                    id[m] = 256 + qh++;
+                    wt[m] = q0;
+                    q0 = q1;
+                }
+            }
+            const uint64_t sum = wt[0] + wt[1];
+            if (tid == 0) {
+                sm.iw[qt] = sum;
+                sm.par[id[0]] = (uint16_t)(256 + qt);
+                sm.par[id[1]] = (uint16_t)(256 + qt);
+            }
+            ++qt;
+        }
+        if (tid == 0) sm.par[kRoot] = (uint16_t)kRoot;
+    }
+    __syncthreads();
+
+    // 3. depths by pointer jumping: dep[v] = distance from v to anc[v]
+    const uint32_t v0 = tid, v1 = tid + 256;
+    sm.anc[v0] = sm.par[v0];
+    sm.dep[v0] = 1;
+    if (v1 < kNodes) {
+        sm.anc[v1] = sm.par[v1];
+        sm.dep[v1] = v1 == kRoot ? 0 : 1;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int round = 0; round < 9; ++round) {
+        const uint32_t a0 = sm.anc[v0];
+        const uint32_t d0 = sm.dep[a0], aa0 = sm.anc[a0];
+        uint32_t a1 = 0, d1 = 0, aa1 = 0;
+        if (v1 < kNodes) {
+            a1 = sm.anc[v1];
+            d1 = sm.dep[a1];
+            aa1 = sm.anc[a1];
+        }
+        __syncthreads();
+        sm.dep[v0] = (uint16_t)(sm.dep[v0] + d0);
+        sm.anc[v0] = (uint16_t)aa0;
+        if (v1 < kNodes) {
+            sm.dep[v1] = (uint16_t)(sm.dep[v1] + d1);
+            sm.anc[v1] = (uint16_t)aa1;
+        }
+        __syncthreads();
+    }
+    // leaf at sorted position tid: its byte's code length
+    const uint32_t d = sm.dep[tid];
+    const uint32_t byte = sm.sidx[tid];
+    sm.len[byte] = (uint8_t)(d < 255 ? d : 255);
+    if (d > (uint32_t)EC_MAX_CODE_LEN) sm.bad = 1;
+    else atomicAdd(&sm.blc[d], 1u);
+    atomicMax(&sm.max_len, d);
+    __syncthreads();
+
+    const bool bad = sm.bad != 0;
+    if (bad) {
+        // unusable table: all zero, codec 0
+        uint4 *p = reinterpret_cast<uint4 *>(t);
+        for (uint32_t i = tid; i < sizeof(DevTables) / 16; i += kBuildThreads) p[i] = make_uint4(0, 0, 0, 0);
+        if (tid == 0) or_status(status ? status + seg : nullptr, EC_S_BAD_CODEBOOK);
+        return;
+    }
+
+    // 4. canonical codes.  first_code[l] = sum_{j<l} blc[j] << (l - j) and
+    // first_idx[l] = sum_{j<l} blc[j] (the recurrence c_l = (c_{l-1} +
+    // blc[l-1]) << 1 unrolled).
+    if (tid < 48) {
+        uint64_t fc = 0;
+        uint32_t fi = 0;
+        if (tid >= 1 && tid <= (uint32_t)EC_MAX_CODE_LEN) {
+            for (uint32_t j = 1; j < tid; ++j) {
+                fc += (uint64_t)sm.blc[j] << (tid - j);
+                fi += sm.blc[j];
+            }
+        }
+        sm.fcode[tid] = fc;
+        sm.fidx[tid] = fi;
+    }
+    const uint32_t my_len = sm.len[tid];
+    sm.w[tid] = my_len;   // (length, byte) keys for the canonical order
+    __syncthreads();
+    if (tid >= 1 && tid <= (uint32_t)kHuffBits)
+        sm.lim13[tid] = (uint32_t)((sm.fcode[tid] + sm.blc[tid]) << (kHuffBits - tid));
+    const uint32_t pos = rank256(sm.w, my_len, tid);
+    sm.symc[pos] = (uint8_t)tid;
+    const uint64_t code = sm.fcode[my_len] + (pos - sm.fidx[my_len]);
+    const uint32_t max_len = sm.max_len;
+    __syncthreads();
+
+    // 5. tables
+    t->enc64[tid] = (code << (64 - my_len)) | my_len;
+    t->enc32[tid] = max_len <= (uint32_t)kNarrowMaxLen ? ((uint32_t)code << (32 - my_len)) | my_len : 0u;
+    t->sym[tid] = sm.symc[tid];
+    t->code_len[tid] = (uint8_t)my_len;
+    for (uint32_t i = tid; i < (uint32_t)kL1Size; i += kBuildThreads) t->l1[i] = 0;
+    if (tid < 48) {
+        const bool in = tid >= 1 && tid <= (uint32_t)EC_MAX_CODE_LEN;
+        t->limit[tid] = in ? (sm.fcode[tid] + sm.blc[tid]) << (EC_MAX_CODE_LEN - tid) : 0ull;
+        t->first_code[tid] = in ? sm.fcode[tid] : 0ull;
+        t->first_idx[tid] = in ? sm.fidx[tid] : 0u;
+    }
+    if (wave == 0) {
+        // codebook id: FNV-1a 64 over the codec byte and the 256 code lengths
+        if (tid == 0) {
+            uint64_t h = 0xcbf29ce484222325ull;
+            h = (h ^ (uint64_t)EC_CODEC_HUFFMAN) * 0x100000001b3ull;
+            for (uint32_t s = 0; s < 256; ++s) h = (h ^ (uint64_t)sm.len[s]) * 0x100000001b3ull;
+            t->codebook_id = h;
+            t->codec = EC_CODEC_HUFFMAN;
+            t->max_len = max_len;
+            t->qlc_lens = 0;
+            t->eg_k = -1;
+            t->pad[0] = 0;
+            t->pad[1] = 0;
+        }
+    } else {
+        // 13-bit decode table: window w starts a code of length
+        // l = 1 + #{l' <= 13 : lim13[l'] <= w}; none when l > 13
+        uint32_t lim[kHuffBits + 1];
+#pragma unroll
+        for (int l = 1; l <= kHuffBits; ++l) lim[l] = sm.lim13[l];
+        for (uint32_t w = tid - 64; w < (uint32_t)kHuffSize; w += kBuildThreads - 64) {
+            uint32_t l = 1;
+#pragma unroll
+            for (int j = 1; j <= kHuffBits; ++j) l += lim[j] <= w ? 1u : 0u;
+            uint16_t e = 0;
+            if (l <= (uint32_t)kHuffBits) {
+                const uint32_t idx = sm.fidx[l] + (uint32_t)((w >> (kHuffBits - l)) - sm.fcode[l]);
+                e = (uint16_t)(sm.symc[idx & 255u] | (l << 8));
+            }
+            t->hl1[w] = e;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_huff_build(const uint64_t *counts, uint32_t n_seg, DevTables *tabs, uint32_t *status,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(huff_build_kernel, dim3(n_seg), dim3(kBuildThreads), 0, s, counts, tabs, status);
+    return hipGetLastError();
+}
+
+}  // namespace ec

@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
             uint32_t bits = 0;
             if (magic != kMagic || version != kVersion || (flags & ~1u)) {
                 bits = EC_S_BAD_HEADER;
-            } else if (codec != tab->codec || id != tab->codebook_id) {
+            } else if (codec != (uint32_t)CODEC || codec != tab->codec || id != tab->codebook_id) {
                 bits = EC_S_CODEBOOK_MISMATCH;
             } else if (n != a.seg_n || C == 0 || (C % kSub) || C > kMaxChunk || (uint64_t)nch != (n + C - 1) / C) {
                 bits = EC_S_BAD_HEADER;

@@ -70,6 +70,8 @@ struct EncodeArgs {
     uint32_t embed_lengths;
     uint32_t max_len;         // longest code over the launch's codebooks
     uint32_t stage_bytes;     // LDS stage of the staged packer (set at launch)
+    uint32_t tables_unread;   // 1: the host never read the tables (device-built); the packers check
+                              // each chunk's table for codes longer than kNarrowMaxLen themselves
     const DevTables *tabs[EC_MAX_BATCH];
 };
 
@@ -92,6 +94,8 @@ hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t max_len, 
 uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg);
 hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
                             uint64_t *counts, uint32_t *partial, hipStream_t s);
+hipError_t launch_huff_build(const uint64_t *counts, uint32_t n_seg, DevTables *tabs, uint32_t *status,
+                             hipStream_t s);
 hipError_t launch_pmf_average(const uint64_t *counts, uint32_t n_seg, float *pmf, hipStream_t s);
 hipError_t launch_pmf_kl(const uint64_t *p, uint32_t n_seg, const uint64_t *q, uint32_t q_add,
                          float *kl, hipStream_t s);

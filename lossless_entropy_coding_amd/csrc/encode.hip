@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kScanThreads) void encode_offsets_kernel(const Enco
         h[7] = 0;
         a.out_len[seg] = end;
         if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
+        if (tab->codec == 0) or_status(a.status ? a.status + seg : nullptr, EC_S_BAD_CODEBOOK);
     }
     const uint32_t index_end = a.sub_at + 4u * n * (a.chunk_symbols / kSub);
     uint32_t pad_from = index_end;
@@ -401,6 +402,9 @@ __global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const E
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const ChunkPos p = chunk_pos(a, blockIdx.x);
+    // a table the host never saw may have codes too long for the 32-bit
+    // entries (then all zero): its chunks go to the row-by-row packer
+    if (a.tables_unread && seg_tables<EncodeArgs>(p.seg)->max_len > (uint32_t)kNarrowMaxLen) return;
     uint4 v[ROWS];
     uint32_t vb[ROWS];
     load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
@@ -451,9 +455,11 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
     __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // after the staged packer: only the chunks it left
-    if (a.stage_bytes && fits_stage(a, a.sizes[blockIdx.x])) return;
     const ChunkPos p = chunk_pos(a, blockIdx.x);
+    // after the staged packer: only the chunks it left
+    if (a.stage_bytes && fits_stage(a, a.sizes[blockIdx.x]) &&
+        !(a.tables_unread && seg_tables<EncodeArgs>(p.seg)->max_len > (uint32_t)kNarrowMaxLen))
+        return;
     uint4 v[ROWS];
     uint32_t vb[ROWS];
     load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
@@ -518,13 +524,16 @@ hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t 
     const uint32_t rows_lds = (kRowSyms * a.max_len / 32 + 8) * 4;
     bool all_staged = false;
     a.stage_bytes = 0;
+    // tables the host never read: staged packing for the chunks whose table
+    // has 32-bit entries, sized for the longest such code
+    const uint32_t narrow_len = a.tables_unread ? (uint32_t)kNarrowMaxLen : a.max_len;
     if constexpr (ROWS <= 4) {
-        if (a.max_len <= (uint32_t)kNarrowMaxLen) {
+        if (narrow_len <= (uint32_t)kNarrowMaxLen) {
             // stage: the worst-case chunk plus a spare group, capped
-            const uint32_t worst = ((a.chunk_symbols * a.max_len + 127) / 128 + 1) * 16;
+            const uint32_t worst = ((a.chunk_symbols * narrow_len + 127) / 128 + 1) * 16;
             a.stage_bytes = worst < kStageCap ? worst : kStageCap;
-            all_staged = worst <= kStageCap;
-            if (a.max_len > 16)
+            all_staged = worst <= kStageCap && !a.tables_unread;
+            if (narrow_len > 16)
                 hipLaunchKernelGGL((encode_pack_staged_kernel<ROWS, true>), dim3(n_chunks), dim3(kThreads),
                                    a.stage_bytes, s, a);
             else

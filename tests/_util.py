@@ -19,3 +19,25 @@ def deep_counts(depth: int) -> np.ndarray:
     for i in range(m):
         counts[i] = fib[i] * 256 - 1
     return counts
+
+
+# Device codebook table layout (DevTables in csrc/ec_internal.h): byte
+# offsets of the fields these tests read.
+TABLE_BYTES = 25056
+T_ENC64, T_HL1, T_LIMIT, T_SYM, T_CODE_LEN, T_ID = 0, 7168, 23552, 24512, 24768, 25024
+
+
+def parse_table(b: bytes) -> dict:
+    """Fields of a device codebook table (Huffman) as Python values."""
+    enc64 = np.frombuffer(b, np.uint64, 256, T_ENC64)
+    code_len = list(np.frombuffer(b, np.uint8, 256, T_CODE_LEN))
+    codec, max_len = np.frombuffer(b, np.uint32, 2, T_ID + 8)
+    return dict(
+        code_len=[int(v) for v in code_len],
+        code=[int(e) >> (64 - int(l)) if l else 0 for e, l in zip(enc64, code_len)],
+        enc_len=[int(e) & 0xFF for e in enc64],
+        hl1=np.frombuffer(b, np.uint16, 8192, T_HL1),
+        limit=[int(v) for v in np.frombuffer(b, np.uint64, 48, T_LIMIT)],
+        sym=list(np.frombuffer(b, np.uint8, 256, T_SYM)),
+        codebook_id=int(np.frombuffer(b, np.uint64, 1, T_ID)[0]),
+        codec=int(codec), max_len=int(max_len))

@@ -6,7 +6,8 @@ Every stream is compared byte for byte with the oracle's (the oracle's C
 encoder finishes a 64 MiB shard in a few seconds); the decoded bytes must
 equal the input and the histograms must equal the oracle's.  The 256 MiB
 multi-shard batch checks every shard's histogram and round trip and a
-sample of 8 shards' streams (both codebook paths) against the oracle.
+sample of 8 shards' streams against the oracle, for the fixed codebook and
+for per-shard codebooks built on the host and on the GPU.
 """
 
 import functools
@@ -93,9 +94,10 @@ def test_full_size_stream_matches_oracle(ec, workload, codec):
     assert torch.equal(y, x_d)
 
 
-@pytest.mark.parametrize("per_shard", [False, True])
-def test_full_size_batch_matches_oracle(ec, per_shard):
-    print("case batch per_shard=%s" % per_shard, flush=True)
+@pytest.mark.parametrize("mode", ["fixed", "per_shard_host", "per_shard_device"])
+def test_full_size_batch_matches_oracle(ec, mode):
+    print("case batch %s" % mode, flush=True)
+    per_shard = mode != "fixed"
     x, counts = _workload("batch")
     S, n = 64, 1 << 22
     x = x.reshape(S, n)
@@ -109,18 +111,25 @@ def test_full_size_batch_matches_oracle(ec, per_shard):
         assert np.array_equal(h[i].astype(np.uint64), stats.histogram(x[i])), i
     if per_shard:
         rows = [[int(c) for c in r] for r in h]
-        cbs = [ec.Codebook.huffman(r) for r in rows]
     else:
         rows = [counts] * S
-        cbs = ec.Codebook.huffman(counts)
-    worst = max(ec.max_encoded_bytes(c, n, C, True) for c in (cbs if per_shard else [cbs]))
-    stride = (worst + 255) // 256 * 256 + 4096
-    out = torch.empty((S, stride), dtype=torch.uint8, device=DEV)
     y = torch.empty((S, n), dtype=torch.uint8, device=DEV)
     lens = torch.zeros(S, dtype=torch.int64, device=DEV)
     status = torch.zeros(S, dtype=torch.int32, device=DEV)
-    ec.encode_batch(cbs, x_d, C, embed_lengths=per_shard, out=out, out_len=lens, status=status)
-    ec.decode_batch(cbs, out, n, out=y, status=status)
+    if mode == "per_shard_device":
+        # the bench's three-stage step: histogram rows -> device codebooks
+        stride = (ec.own_max_encoded_bytes(n, C, True) + 255) // 256 * 256 + 4096
+        out = torch.empty((S, stride), dtype=torch.uint8, device=DEV)
+        tables, _ = ec.build_huffman_device(hist, status=status)
+        ec.encode_batch_device(tables, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
+        ec.decode_batch_device(tables, out, n, out=y, status=status)
+    else:
+        cbs = [ec.Codebook.huffman(r) for r in rows] if per_shard else ec.Codebook.huffman(counts)
+        worst = max(ec.max_encoded_bytes(c, n, C, True) for c in (cbs if per_shard else [cbs]))
+        stride = (worst + 255) // 256 * 256 + 4096
+        out = torch.empty((S, stride), dtype=torch.uint8, device=DEV)
+        ec.encode_batch(cbs, x_d, C, embed_lengths=per_shard, out=out, out_len=lens, status=status)
+        ec.decode_batch(cbs, out, n, out=y, status=status)
     torch.cuda.synchronize()
     assert not status.cpu().numpy().any()
     assert torch.equal(y, x_d)

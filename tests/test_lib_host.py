@@ -11,7 +11,7 @@ import pytest
 
 from oracle import codebooks as cbm
 
-from _util import deep_counts
+from _util import TABLE_BYTES, deep_counts, parse_table
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -151,3 +151,63 @@ def test_index_and_max_sizes(ec):
     assert ec.index_bytes(100, 300) == 0          # not a multiple of 256
     cb = ec.Codebook.qlc([1] * 256)
     assert ec.max_encoded_bytes(cb, 1 << 20, 4096) == st.layout(1 << 20, 4096)[3] + 256 * (4096 * 11 // 8)
+
+
+def expected_hl1(ora) -> np.ndarray:
+    """13-bit decode table from the oracle's codes, by brute force: window w
+    holds s | len << 8 when it starts with s's code of at most 13 bits."""
+    w = np.arange(8192, dtype=np.int64)
+    out = np.zeros(8192, dtype=np.uint16)
+    for s in range(256):
+        L = ora.length[s]
+        if L <= 13:
+            out[(w >> (13 - L)) == ora.code[s]] = s | (L << 8)
+    return out
+
+
+@pytest.mark.parametrize("which", ["r0", "r1", "ties", "d20", "d27", "d40", "uniform"])
+def test_exported_table_matches_oracle(ec, which):
+    """The device table format of a Huffman codebook (what the GPU builder
+    must also produce, byte for byte): encode entries, the 13-bit decode
+    table, the 40-bit limits (windows below limit[l] start with a code of
+    at most l bits: a Kraft partial sum), the canonical order and the id."""
+    if which.startswith("d"):
+        counts = [int(c) for c in deep_counts(int(which[1:]))]
+    elif which == "uniform":
+        counts = [0] * 256
+    else:
+        counts = _counts({"r0": 0, "r1": 1, "ties": 3}[which], zeros=40, ties=which == "ties")
+    ora = cbm.huffman_codebook(counts)
+    b = ec.Codebook.huffman(counts).export()
+    assert len(b) == ec.device_codebook_bytes() == TABLE_BYTES
+    t = parse_table(b)
+    assert t["code_len"] == ora.length and t["enc_len"] == ora.length
+    assert t["code"] == ora.code
+    assert t["codebook_id"] == ora.codebook_id and t["codec"] == cbm.HUFFMAN and t["max_len"] == ora.max_len
+    assert np.array_equal(t["hl1"], expected_hl1(ora))
+    for L in range(1, 41):
+        assert t["limit"][L] == sum(1 << (40 - l) for l in ora.length if l <= L), L
+    assert t["sym"] == sorted(range(256), key=lambda s: (ora.length[s], s))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_own_histogram_bound(ec, seed):
+    """A Huffman code built from a segment's own histogram spends at most 8
+    bits a symbol on it, so index + n + 16 bytes per chunk always holds the
+    stream (checked on skewed, chunk-wise varying data with the oracle)."""
+    from oracle import stats
+    from oracle import stream as st
+    rng = np.random.default_rng(seed)
+    C = 4096
+    n = 20 * C + 1234 * seed
+    # chunks of very different statistics: the code is short on average but
+    # some chunks cost far more than 8 bits a symbol
+    x = np.where(rng.random(n) < 0.9, rng.integers(0, 3, n), rng.integers(0, 256, n)).astype(np.uint8)
+    x[: 2 * C] = rng.integers(0, 256, 2 * C).astype(np.uint8)
+    counts = [int(c) for c in stats.histogram(x)]
+    ora = cbm.huffman_codebook(counts)
+    assert cbm.coded_bits(counts, ora.length) <= 8 * n
+    bound = ec.own_max_encoded_bytes(n, C, True)
+    nch = (n + C - 1) // C
+    assert bound == st.layout(n, C, True)[3] + n + 16 * nch
+    assert len(st.encode_stream(x, ora, C, embed_lengths=True)) <= bound
