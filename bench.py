@@ -325,6 +325,7 @@ def run_batch(args, ec, torch):
     hist = torch.empty((S, 256), dtype=torch.int64, device=dev)
     kl = torch.empty(S, dtype=torch.float32, device=dev)
     tables = torch.empty((S, ec.device_codebook_bytes()), dtype=torch.uint8, device=dev)
+    rtables = torch.empty_like(tables)
 
     def single():
         ec.byte_histogram(x_d, out=hist)
@@ -336,7 +337,9 @@ def run_batch(args, ec, torch):
         ec.byte_histogram(x_d, out=hist)                                  # frequency analysis
         ec.build_huffman_device(hist, out=tables, status=status)          # codebook generation
         ec.encode_batch_device(tables, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
-        ec.decode_batch_device(tables, out, n, out=y, status=status)
+        # the receiver rebuilds each codebook from the lengths its stream carries
+        ec.huffman_tables_from_streams(out, out=rtables, status=status)
+        ec.decode_batch_device(rtables, out, n, out=y, status=status)
 
     def three_host():
         ec.byte_histogram(x_d, out=hist)

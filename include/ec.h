@@ -269,6 +269,26 @@ int huff_build_codebooks_device(const uint64_t *d_counts, uint32_t n_seg, void *
                                 hipStream_t stream);
 
 /*
+ * The receiving side: rebuild, on the GPU, the tables of the Huffman
+ * codebook each stream carries (the 256 code lengths that
+ * entropy_encode_batch[_device] embeds with embed_lengths = 1), so that a
+ * decoder needs nothing but the stream (single-stage Huffman page, abstract:
+ * the codebook transmitted with the data).  The tables equal those of
+ * huff_build_codebook_from_lengths.
+ *   d_in       n_seg streams at d_in + s * in_stride (in_len readable bytes
+ *              each; in_stride a multiple of 16 and >= in_len when n_seg > 1)
+ *   d_tables   as for huff_build_codebooks_device
+ *   d_status   device u32[n_seg], caller-zeroed, or NULL:
+ *              EC_S_BAD_HEADER   not a Huffman stream with embedded lengths,
+ *                                or its index does not fit in in_len;
+ *              EC_S_BAD_CODEBOOK the lengths are not a complete prefix code
+ *                                of 1..EC_MAX_CODE_LEN-bit codes.
+ *              Either way the segment's table is unusable (codec 0).
+ */
+int huff_tables_from_streams_device(const uint8_t *d_in, uint64_t in_stride, uint64_t in_len, uint32_t n_seg,
+                                    void *d_tables, uint32_t *d_status, hipStream_t stream);
+
+/*
  * Copy a host-built codebook's table, in the device table format, to host
  * memory `table` (ec_device_codebook_bytes() bytes).  Uploaded into a device
  * table array it serves the *_device functions like a device-built one.

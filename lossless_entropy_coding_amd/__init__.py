@@ -20,7 +20,7 @@ __all__ = [
     "max_encoded_bytes", "QLC_BASE", "QLC_ADAPTED", "CODEC_QLC", "CODEC_HUFFMAN",
     "CODEC_EXP_GOLOMB", "S_CAPACITY", "S_CORRUPT", "S_BAD_HEADER", "S_CODEBOOK_MISMATCH",
     "S_BAD_CODEBOOK", "EXPORTS", "device_codebook_bytes", "build_huffman_device", "own_max_encoded_bytes",
-    "encode_batch_device", "decode_batch_device",
+    "encode_batch_device", "decode_batch_device", "huffman_tables_from_streams",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libec.so")
@@ -62,6 +62,7 @@ EXPORTS = {
     "ec_device_codebook_bytes": (_u64, []),
     "huff_build_codebooks_device": (_int, [_vp, _u32, _vp, _vp, _vp]),
     "ec_codebook_export": (_int, [_vp, _vp]),
+    "huff_tables_from_streams_device": (_int, [_vp, _u64, _u64, _u32, _vp, _vp, _vp]),
     "entropy_own_max_encoded_bytes": (_u64, [_u64, _u32, _u32]),
     "entropy_encode_batch_device": (_int, [_vp, _u32, _vp, _u64, _u64, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
     "entropy_decode_batch_device": (_int, [_vp, _u32, _u32, _vp, _u64, _vp, _u64, _u64, _vp, _vp]),
@@ -329,6 +330,23 @@ def build_huffman_device(counts: torch.Tensor, out: torch.Tensor | None = None,
         status = torch.zeros(S, dtype=torch.int32, device=c.device)
     _check(lib().huff_build_codebooks_device(_ptr(c), S, _ptr(out), _ptr(status), _stream(stream)),
            "huff_build_codebooks_device")
+    return out, status
+
+
+def huffman_tables_from_streams(data: torch.Tensor, in_len: int | None = None, out: torch.Tensor | None = None,
+                                status: torch.Tensor | None = None, stream=None):
+    """huff_tables_from_streams_device over the rows of a 2-D uint8 tensor of
+    streams with embedded code lengths.  Returns (tables, status int32[S])."""
+    _u8_cuda(data, "data")
+    S = data.shape[0]
+    if out is None:
+        out = torch.empty((S, device_codebook_bytes()), dtype=torch.uint8, device=data.device)
+    _tables_cuda(out, S)
+    if status is None:
+        status = torch.zeros(S, dtype=torch.int32, device=data.device)
+    _check(lib().huff_tables_from_streams_device(_ptr(data), data.stride(0),
+                                                 data.shape[1] if in_len is None else in_len, S, _ptr(out),
+                                                 _ptr(status), _stream(stream)), "huff_tables_from_streams_device")
     return out, status
 
 

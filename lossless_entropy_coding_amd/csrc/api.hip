@@ -344,6 +344,15 @@ int huff_build_codebooks_device(const uint64_t *d_counts, uint32_t n_seg, void *
     return hip_rc(launch_huff_build(d_counts, n_seg, static_cast<DevTables *>(d_tables), d_status, stream));
 }
 
+int huff_tables_from_streams_device(const uint8_t *d_in, uint64_t in_stride, uint64_t in_len, uint32_t n_seg,
+                                    void *d_tables, uint32_t *d_status, hipStream_t stream) {
+    if (!d_in || !d_tables || n_seg == 0 || n_seg > 65535 || in_len < kHeaderBytes) return EC_E_INVAL;
+    if (!aligned16(d_in) || !aligned16(d_tables) || (n_seg > 1 && (in_stride % 16 || in_stride < in_len)))
+        return EC_E_INVAL;
+    return hip_rc(launch_huff_tables_from_streams(d_in, in_stride, in_len, n_seg, static_cast<DevTables *>(d_tables),
+                                                  d_status, stream));
+}
+
 int ec_codebook_export(const ec_codebook *cb, void *table) {
     if (!cb || !table) return EC_E_INVAL;
     memcpy(table, &cb->host, sizeof(DevTables));

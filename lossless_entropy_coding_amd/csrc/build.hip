@@ -21,6 +21,8 @@
 //      window's code length is one more than the number of 13-bit limits at
 //      or below it), the 40-bit canonical limits, the canonical symbol order,
 //      the code lengths and the FNV-1a codebook id.
+// The same steps 4 and 5 also rebuild a codebook from the code lengths a
+// stream carries (huff_tables_from_streams_kernel).
 // A code longer than EC_MAX_CODE_LEN bits, or a count of 2^55 or more, makes
 // the shard's table unusable (codec 0, all entries zero) and sets
 // EC_S_BAD_CODEBOOK in its status word.
@@ -70,6 +72,90 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
     return (uint64_t)hi << 32 | lo;
+}
+
+// An unusable table (codec 0, every entry zero), and the status bits saying why.
+__device__ void unusable_table(DevTables *t, uint32_t tid, uint32_t *status, uint32_t bits) {
+    uint4 *p = reinterpret_cast<uint4 *>(t);
+    for (uint32_t i = tid; i < sizeof(DevTables) / 16; i += kBuildThreads) p[i] = make_uint4(0, 0, 0, 0);
+    if (tid == 0) or_status(status, bits);
+}
+
+// Steps 4 and 5, from the code lengths in sm.len (a complete code, every
+// length 1..EC_MAX_CODE_LEN), their counts sm.blc and sm.max_len.  Called
+// by every thread of the workgroup.
+__device__ void canonical_tables(BuildSmem &sm, DevTables *t, uint32_t tid) {
+    const uint32_t wave = tid >> 6;
+    // 4. canonical codes.  first_code[l] = sum_{j<l} blc[j] << (l - j) and
+    // first_idx[l] = sum_{j<l} blc[j] (the recurrence c_l = (c_{l-1} +
+    // blc[l-1]) << 1 unrolled).
+    if (tid < 48) {
+        uint64_t fc = 0;
+        uint32_t fi = 0;
+        if (tid >= 1 && tid <= (uint32_t)EC_MAX_CODE_LEN) {
+            for (uint32_t j = 1; j < tid; ++j) {
+                fc += (uint64_t)sm.blc[j] << (tid - j);
+                fi += sm.blc[j];
+            }
+        }
+        sm.fcode[tid] = fc;
+        sm.fidx[tid] = fi;
+    }
+    const uint32_t my_len = sm.len[tid];
+    sm.w[tid] = my_len;   // (length, byte) keys for the canonical order
+    __syncthreads();
+    if (tid >= 1 && tid <= (uint32_t)kHuffBits)
+        sm.lim13[tid] = (uint32_t)((sm.fcode[tid] + sm.blc[tid]) << (kHuffBits - tid));
+    const uint32_t pos = rank256(sm.w, my_len, tid);
+    sm.symc[pos] = (uint8_t)tid;
+    const uint64_t code = sm.fcode[my_len] + (pos - sm.fidx[my_len]);
+    const uint32_t max_len = sm.max_len;
+    __syncthreads();
+
+    // 5. tables
+    t->enc64[tid] = (code << (64 - my_len)) | my_len;
+    t->enc32[tid] = max_len <= (uint32_t)kNarrowMaxLen ? ((uint32_t)code << (32 - my_len)) | my_len : 0u;
+    t->sym[tid] = sm.symc[tid];
+    t->code_len[tid] = (uint8_t)my_len;
+    for (uint32_t i = tid; i < (uint32_t)kL1Size; i += kBuildThreads) t->l1[i] = 0;
+    if (tid < 48) {
+        const bool in = tid >= 1 && tid <= (uint32_t)EC_MAX_CODE_LEN;
+        t->limit[tid] = in ? (sm.fcode[tid] + sm.blc[tid]) << (EC_MAX_CODE_LEN - tid) : 0ull;
+        t->first_code[tid] = in ? sm.fcode[tid] : 0ull;
+        t->first_idx[tid] = in ? sm.fidx[tid] : 0u;
+    }
+    if (wave == 0) {
+        // codebook id: FNV-1a 64 over the codec byte and the 256 code lengths
+        if (tid == 0) {
+            uint64_t h = 0xcbf29ce484222325ull;
+            h = (h ^ (uint64_t)EC_CODEC_HUFFMAN) * 0x100000001b3ull;
+            for (uint32_t s = 0; s < 256; ++s) h = (h ^ (uint64_t)sm.len[s]) * 0x100000001b3ull;
+            t->codebook_id = h;
+            t->codec = EC_CODEC_HUFFMAN;
+            t->max_len = max_len;
+            t->qlc_lens = 0;
+            t->eg_k = -1;
+            t->pad[0] = 0;
+            t->pad[1] = 0;
+        }
+    } else {
+        // 13-bit decode table: window w starts a code of length
+        // l = 1 + #{l' <= 13 : lim13[l'] <= w}; none when l > 13
+        uint32_t lim[kHuffBits + 1];
+#pragma unroll
+        for (int l = 1; l <= kHuffBits; ++l) lim[l] = sm.lim13[l];
+        for (uint32_t w = tid - 64; w < (uint32_t)kHuffSize; w += kBuildThreads - 64) {
+            uint32_t l = 1;
+#pragma unroll
+            for (int j = 1; j <= kHuffBits; ++j) l += lim[j] <= w ? 1u : 0u;
+            uint16_t e = 0;
+            if (l <= (uint32_t)kHuffBits) {
+                const uint32_t idx = sm.fidx[l] + (uint32_t)((w >> (kHuffBits - l)) - sm.fcode[l]);
+                e = (uint16_t)(sm.symc[idx & 255u] | (l << 8));
+            }
+            t->hl1[w] = e;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBuildThreads) void huff_build_kernel(const uint64_t *counts, DevTables *tabs,
@@ -173,88 +259,78 @@ __global__ __launch_bounds__(kBuildThreads) void huff_build_kernel(const uint64_
     atomicMax(&sm.max_len, d);
     __syncthreads();
 
-    const bool bad = sm.bad != 0;
-    if (bad) {
-        // unusable table: all zero, codec 0
-        uint4 *p = reinterpret_cast<uint4 *>(t);
-        for (uint32_t i = tid; i < sizeof(DevTables) / 16; i += kBuildThreads) p[i] = make_uint4(0, 0, 0, 0);
-        if (tid == 0) or_status(status ? status + seg : nullptr, EC_S_BAD_CODEBOOK);
+    if (sm.bad) {
+        unusable_table(t, tid, status ? status + seg : nullptr, EC_S_BAD_CODEBOOK);
         return;
     }
+    canonical_tables(sm, t, tid);
+}
 
-    // 4. canonical codes.  first_code[l] = sum_{j<l} blc[j] << (l - j) and
-    // first_idx[l] = sum_{j<l} blc[j] (the recurrence c_l = (c_{l-1} +
-    // blc[l-1]) << 1 unrolled).
-    if (tid < 48) {
-        uint64_t fc = 0;
-        uint32_t fi = 0;
-        if (tid >= 1 && tid <= (uint32_t)EC_MAX_CODE_LEN) {
-            for (uint32_t j = 1; j < tid; ++j) {
-                fc += (uint64_t)sm.blc[j] << (tid - j);
-                fi += sm.blc[j];
-            }
-        }
-        sm.fcode[tid] = fc;
-        sm.fidx[tid] = fi;
-    }
-    const uint32_t my_len = sm.len[tid];
-    sm.w[tid] = my_len;   // (length, byte) keys for the canonical order
-    __syncthreads();
-    if (tid >= 1 && tid <= (uint32_t)kHuffBits)
-        sm.lim13[tid] = (uint32_t)((sm.fcode[tid] + sm.blc[tid]) << (kHuffBits - tid));
-    const uint32_t pos = rank256(sm.w, my_len, tid);
-    sm.symc[pos] = (uint8_t)tid;
-    const uint64_t code = sm.fcode[my_len] + (pos - sm.fidx[my_len]);
-    const uint32_t max_len = sm.max_len;
-    __syncthreads();
+// The receiving side of the three-stage design: the tables of the codebook
+// a stream carries (its 256 embedded code lengths), so that the decoder
+// needs nothing from the encoder but the stream.  A header that is not a
+// Huffman stream with embedded lengths, or an index that does not fit in
+// in_len, sets EC_S_BAD_HEADER; lengths that are not a complete code of
+// 1..EC_MAX_CODE_LEN-bit codes set EC_S_BAD_CODEBOOK.  Either way the table
+// is unusable.
+__global__ __launch_bounds__(kBuildThreads) void huff_tables_from_streams_kernel(const uint8_t *in,
+                                                                                 uint64_t in_stride,
+                                                                                 uint64_t in_len, DevTables *tabs,
+                                                                                 uint32_t *status) {
+    __shared__ BuildSmem sm;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t seg = blockIdx.x;
+    DevTables *t = tabs + seg;
+    uint32_t *st = status ? status + seg : nullptr;
+    const uint8_t *stream = in + (uint64_t)seg * in_stride;
 
-    // 5. tables
-    t->enc64[tid] = (code << (64 - my_len)) | my_len;
-    t->enc32[tid] = max_len <= (uint32_t)kNarrowMaxLen ? ((uint32_t)code << (32 - my_len)) | my_len : 0u;
-    t->sym[tid] = sm.symc[tid];
-    t->code_len[tid] = (uint8_t)my_len;
-    for (uint32_t i = tid; i < (uint32_t)kL1Size; i += kBuildThreads) t->l1[i] = 0;
-    if (tid < 48) {
-        const bool in = tid >= 1 && tid <= (uint32_t)EC_MAX_CODE_LEN;
-        t->limit[tid] = in ? (sm.fcode[tid] + sm.blc[tid]) << (EC_MAX_CODE_LEN - tid) : 0ull;
-        t->first_code[tid] = in ? sm.fcode[tid] : 0ull;
-        t->first_idx[tid] = in ? sm.fidx[tid] : 0u;
+    const uint64_t *h = reinterpret_cast<const uint64_t *>(stream);
+    const uint64_t h0 = h[0], n = h[1], h2 = h[2];
+    const uint32_t C = (uint32_t)h2, nch = (uint32_t)(h2 >> 32);
+    bool ok = (uint32_t)h0 == kMagic && ((h0 >> 32) & 0xffffu) == kVersion &&
+              ((h0 >> 48) & 0xffu) == (uint64_t)EC_CODEC_HUFFMAN && (h0 >> 56) == 1u && n <= (1ull << 33) &&
+              C >= kMinChunk && C <= kMaxChunk && C % kSub == 0 && (uint64_t)nch == (n + C - 1) / C;
+    const uint64_t lens_at = kHeaderBytes + 8ull * (nch + 1) + 4ull * nch * (C / kSub);
+    ok = ok && lens_at + 256 <= in_len;
+    if (!ok) {
+        unusable_table(t, tid, st, EC_S_BAD_HEADER);
+        return;
     }
-    if (wave == 0) {
-        // codebook id: FNV-1a 64 over the codec byte and the 256 code lengths
-        if (tid == 0) {
-            uint64_t h = 0xcbf29ce484222325ull;
-            h = (h ^ (uint64_t)EC_CODEC_HUFFMAN) * 0x100000001b3ull;
-            for (uint32_t s = 0; s < 256; ++s) h = (h ^ (uint64_t)sm.len[s]) * 0x100000001b3ull;
-            t->codebook_id = h;
-            t->codec = EC_CODEC_HUFFMAN;
-            t->max_len = max_len;
-            t->qlc_lens = 0;
-            t->eg_k = -1;
-            t->pad[0] = 0;
-            t->pad[1] = 0;
-        }
-    } else {
-        // 13-bit decode table: window w starts a code of length
-        // l = 1 + #{l' <= 13 : lim13[l'] <= w}; none when l > 13
-        uint32_t lim[kHuffBits + 1];
-#pragma unroll
-        for (int l = 1; l <= kHuffBits; ++l) lim[l] = sm.lim13[l];
-        for (uint32_t w = tid - 64; w < (uint32_t)kHuffSize; w += kBuildThreads - 64) {
-            uint32_t l = 1;
-#pragma unroll
-            for (int j = 1; j <= kHuffBits; ++j) l += lim[j] <= w ? 1u : 0u;
-            uint16_t e = 0;
-            if (l <= (uint32_t)kHuffBits) {
-                const uint32_t idx = sm.fidx[l] + (uint32_t)((w >> (kHuffBits - l)) - sm.fcode[l]);
-                e = (uint16_t)(sm.symc[idx & 255u] | (l << 8));
-            }
-            t->hl1[w] = e;
-        }
+    if (tid == 0) {
+        sm.bad = 0;
+        sm.max_len = 0;
     }
+    if (tid < 64) sm.blc[tid] = 0;
+    __syncthreads();
+    const uint32_t l = stream[lens_at + tid];
+    sm.len[tid] = (uint8_t)l;
+    if (l == 0 || l > (uint32_t)EC_MAX_CODE_LEN) sm.bad = 1;
+    else atomicAdd(&sm.blc[l], 1u);
+    atomicMax(&sm.max_len, l);
+    __syncthreads();
+    if (tid == 0) {
+        // Kraft sum exactly 1: sum over lengths of count << (40 - length) == 2^40
+        uint64_t kraft = 0;
+        for (uint32_t j = 1; j <= (uint32_t)EC_MAX_CODE_LEN; ++j)
+            kraft += (uint64_t)sm.blc[j] << (EC_MAX_CODE_LEN - j);
+        if (kraft != (1ull << EC_MAX_CODE_LEN)) sm.bad = 1;
+    }
+    __syncthreads();
+    if (sm.bad) {
+        unusable_table(t, tid, st, EC_S_BAD_CODEBOOK);
+        return;
+    }
+    canonical_tables(sm, t, tid);
 }
 
 }  // namespace
+
+hipError_t launch_huff_tables_from_streams(const uint8_t *in, uint64_t in_stride, uint64_t in_len,
+                                           uint32_t n_seg, DevTables *tabs, uint32_t *status, hipStream_t s) {
+    hipLaunchKernelGGL(huff_tables_from_streams_kernel, dim3(n_seg), dim3(kBuildThreads), 0, s, in, in_stride,
+                       in_len, tabs, status);
+    return hipGetLastError();
+}
 
 hipError_t launch_huff_build(const uint64_t *counts, uint32_t n_seg, DevTables *tabs, uint32_t *status,
                              hipStream_t s) {

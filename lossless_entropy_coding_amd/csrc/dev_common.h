@@ -96,6 +96,8 @@ hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, u
                             uint64_t *counts, uint32_t *partial, hipStream_t s);
 hipError_t launch_huff_build(const uint64_t *counts, uint32_t n_seg, DevTables *tabs, uint32_t *status,
                              hipStream_t s);
+hipError_t launch_huff_tables_from_streams(const uint8_t *in, uint64_t in_stride, uint64_t in_len,
+                                           uint32_t n_seg, DevTables *tabs, uint32_t *status, hipStream_t s);
 hipError_t launch_pmf_average(const uint64_t *counts, uint32_t n_seg, float *pmf, hipStream_t s);
 hipError_t launch_pmf_kl(const uint64_t *p, uint32_t n_seg, const uint64_t *q, uint32_t q_add,
                          float *kl, hipStream_t s);

@@ -100,11 +100,15 @@ def test_device_three_stage_matches_oracle(ec, C):
     hist = ec.byte_histogram(x_d)
     tables, bstatus = ec.build_huffman_device(hist)
     out, lens, estatus = ec.encode_batch_device(tables, x_d, C, embed_lengths=True)
-    y, dstatus = ec.decode_batch_device(tables, out, n)
+    # the receiver rebuilds each codebook from the lengths its stream carries
+    rtables, rstatus = ec.huffman_tables_from_streams(out)
+    y, dstatus = ec.decode_batch_device(rtables, out, n)
     torch.cuda.synchronize()
     assert not bstatus.cpu().numpy().any()
     assert not estatus.cpu().numpy().any()
+    assert not rstatus.cpu().numpy().any()
     assert not dstatus.cpu().numpy().any()
+    assert torch.equal(rtables, tables)
     assert torch.equal(y, x_d)
     h = hist.cpu().numpy()
     L = lens.cpu().numpy()
@@ -177,3 +181,49 @@ def test_uploaded_host_tables(ec, codec):
     for i in range(2):
         want = st.encode_stream(x[i], ocb, C)
         assert out[i, : int(lens[i].item())].cpu().numpy().tobytes() == want
+
+
+def test_tables_from_streams(ec):
+    """Receiver-side tables: equal to the host builder's tables for the
+    oracle's code lengths; a stream without embedded lengths, a stream whose
+    lengths are not a complete code and an index past in_len are flagged,
+    and their segments do not decode."""
+    C = 4096
+    rows = [[int(c) for c in stats.histogram(synth.draw(r, 60 + i, 1 << 16))]
+            for i, r in enumerate(["ffn1", "grad", "ffn2", "normal"])]
+    rows.append([int(c) for c in deep_counts(40)])
+    S = len(rows)
+    n = 2 * C + 48
+    x = np.stack([synth.draw("ffn1", 70 + i, n) for i in range(S)])
+    x_d = torch.from_numpy(x).to(DEV)
+    tables, _ = ec.build_huffman_device(torch.tensor(rows, dtype=torch.int64, device=DEV))
+    cap = ec.max_encoded_bytes(ec.Codebook.huffman(rows[-1]), n, C, True)
+    out = torch.zeros((S, (cap + 255) // 256 * 256), dtype=torch.uint8, device=DEV)
+    out, lens, estatus = ec.encode_batch_device(tables, x_d, C, embed_lengths=True, out=out)
+    torch.cuda.synchronize()
+    assert not estatus.cpu().numpy().any()
+    good = out.clone()
+    # segment 1: lengths that overfill the code space; segment 2: lengths
+    # that underfill it; segment 3: flags say no lengths are embedded
+    nch = (n + C - 1) // C
+    lens_at = 64 + 8 * (nch + 1) + 4 * nch * (C // 256)
+    out[1, lens_at + 7] = max(1, int(out[1, lens_at + 7].item()) - 1)
+    out[2, lens_at + 9] = int(out[2, lens_at + 9].item()) + 1
+    out[3, 7] = 0
+    rtables, rstatus = ec.huffman_tables_from_streams(out)
+    y, dstatus = ec.decode_batch_device(rtables, out, n)
+    torch.cuda.synchronize()
+    assert rstatus.cpu().numpy().tolist() == [0, ec.S_BAD_CODEBOOK, ec.S_BAD_CODEBOOK, ec.S_BAD_HEADER, 0]
+    d = dstatus.cpu().numpy().tolist()
+    assert d[0] == 0 and d[4] == 0 and all(v & ec.S_CODEBOOK_MISMATCH for v in d[1:4])
+    rt = rtables.cpu().numpy()
+    for i in (0, 4):
+        ora = cbm.huffman_codebook(rows[i])
+        assert rt[i].tobytes() == ec.Codebook.huffman_from_lengths(ora.length).export()
+        assert torch.equal(y[i], x_d[i])
+    for i in (1, 2, 3):
+        assert not rt[i].any()
+    # an index that does not fit in in_len
+    _, st_short = ec.huffman_tables_from_streams(good, in_len=lens_at + 255)
+    torch.cuda.synchronize()
+    assert st_short.cpu().numpy().tolist() == [ec.S_BAD_HEADER] * S
