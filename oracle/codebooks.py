@@ -105,6 +105,65 @@ def qlc_codebook(counts, area_size=QLC_BASE_AREAS, suffix_bits=QLC_BASE_SUFFIX) 
                     suffix_bits=suffix_bits, codebook_id=fnv1a64(desc))
 
 
+def qlc_area_cost(sorted_counts, area_size, suffix_bits, prefix_bits=3) -> int:
+    """Payload bits of a QLC layout: rank r in area a costs prefix_bits +
+    suffix_bits[a] bits, areas taking consecutive ranks in prefix order."""
+    bits, r = 0, 0
+    for n_a, b_a in zip(area_size, suffix_bits):
+        bits += (prefix_bits + b_a) * sum(int(c) for c in sorted_counts[r:r + n_a])
+        r += n_a
+    return bits
+
+
+def qlc_optimal_areas(counts, max_lengths=4, n_areas=8, prefix_bits=3, max_suffix=8):
+    """QLC layout with the fewest payload bits for these counts.
+
+    The QLC page (section 2) lets the number of symbols per area and the code
+    lengths change with the distribution while at most four distinct code
+    lengths remain; its closing outlook names a mathematical optimisation of
+    exactly these choices as the next step.  Reading taken: with the 3-bit
+    prefix (n_areas = 8 areas), choose a suffix width b_a in 0..max_suffix
+    and a size n_a <= 2^b_a for every area, sizes summing to the alphabet,
+    at most ``max_lengths`` distinct lengths among non-empty areas, to
+    minimise sum over ranks of count x (prefix_bits + b_area).
+
+    Ranks sorted by decreasing count make two moves free of cost: putting
+    areas in order of increasing length, and filling an area before any rank
+    goes to a longer one.  So some optimum has non-decreasing widths, every
+    non-empty area but the last full, and the unused areas (size 0, width 0)
+    at the end; this function tries every such layout (the brute-force tests
+    over all layouts on small alphabets check the argument) and keeps the
+    cheapest, equal costs going to the lexicographically smallest width
+    sequence.  Returns (area_size, suffix_bits) as tuples of n_areas values.
+    """
+    M = len(counts)
+    ranked = sorted(range(M), key=lambda s: (-int(counts[s]), s))
+    sc = [int(counts[s]) for s in ranked]
+    best = None
+
+    def walk(widths, used):
+        nonlocal best
+        if used >= M:
+            sizes = [1 << b for b in widths]
+            sizes[-1] = M - sum(sizes[:-1])
+            cost = qlc_area_cost(sc, sizes, widths, prefix_bits)
+            key = (cost, tuple(widths))
+            if best is None or key < best[0]:
+                pad = n_areas - len(widths)
+                best = (key, tuple(sizes) + (0,) * pad, tuple(widths) + (0,) * pad)
+            return
+        if len(widths) == n_areas:
+            return
+        lo = widths[-1] if widths else 0
+        for b in range(lo, max_suffix + 1):
+            if len(set(widths + [b])) <= max_lengths:
+                walk(widths + [b], used + (1 << b))
+
+    walk([], 0)
+    assert best is not None, "no layout covers the alphabet"
+    return best[1], best[2]
+
+
 # ------------------------------------------------------------------ Huffman
 
 def huffman_lengths(weights) -> list:
