@@ -48,8 +48,8 @@ WORKLOAD_TEXT = {
 CODECS = {
     "tiny_qlc": ["qlc"],
     "ffn1": ["qlc", "huffman"],
-    "ffn2": ["qlc_adapted", "qlc", "huffman"],
-    "grad": ["eg", "qlc", "huffman"],
+    "ffn2": ["qlc_adapted", "qlc", "qlc_opt", "huffman"],
+    "grad": ["eg", "qlc", "qlc_opt", "huffman"],
 }
 
 
@@ -76,6 +76,8 @@ def make_codebook(ec, name, counts):
         return ec.Codebook.qlc(counts)
     if name == "qlc_adapted":
         return ec.Codebook.qlc(counts, *ec.QLC_ADAPTED)
+    if name == "qlc_opt":   # the cheapest layout with four code lengths
+        return ec.Codebook.qlc(counts, *ec.qlc_optimal_area_layout(counts, 4))
     if name == "huffman":
         return ec.Codebook.huffman(counts)
     if name == "eg":
@@ -116,6 +118,7 @@ def cpu_baseline(x, counts, codec_names, chunk, calib_rows):
     builders = {
         "qlc": lambda c: cbm.qlc_codebook(c),
         "qlc_adapted": lambda c: cbm.qlc_codebook(c, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX),
+        "qlc_opt": lambda c: cbm.qlc_codebook(c, *cbm.qlc_optimal_areas(c, 4)),
         "huffman": lambda c: cbm.huffman_codebook(c),
         "eg": lambda c: cbm.eg_codebook(c),
     }
@@ -265,6 +268,8 @@ def run_single(args, ec, torch):
         compression[n] = dict(stream_bytes=stream_len[j], payload_pct=round(100 * (1 - payload / N), 3),
                               stream_pct=round(100 * (1 - stream_len[j] / N), 3),
                               max_code_len=cbs[j].max_len)
+        if n == "qlc_opt":
+            compression[n]["layout"] = ec.qlc_optimal_area_layout(counts, 4)
 
     ms_per_step = wall / args.steps * 1e3
     value = len(codec_names) * N / (wall / args.steps) / 1e9

@@ -119,6 +119,25 @@ int qlc_build_codebook(const uint64_t counts[256], const uint16_t area_size[8],
                        const uint8_t suffix_bits[8], ec_codebook **out);
 
 /*
+ * QLC area layout with the fewest payload bits for these counts (QLC page,
+ * section 2: the symbols per area and the code lengths adapt to the
+ * distribution while at most four distinct lengths remain; section 5: a
+ * mathematical optimisation of both is the authors' next step).
+ *   counts[256]      byte frequencies, ranked as for qlc_build_codebook
+ *   max_lengths      1..8: most distinct code lengths among non-empty areas
+ *                    (4 keeps the quad-length property; 8 leaves it free)
+ *   area_size[8], suffix_bits[8]  out: a layout for qlc_build_codebook
+ * Minimises sum over ranks of count x (3 + suffix width of the rank's area).
+ * Of the cheapest layouts it returns the one whose non-empty areas have
+ * non-decreasing widths, all full (2^width symbols) but the last, followed
+ * by unused areas (size 0, width 0), with the lexicographically smallest
+ * width sequence.  Host memory only; EC_E_INVAL on NULL pointers or
+ * max_lengths outside 1..8.
+ */
+int qlc_optimal_area_layout(const uint64_t counts[256], uint32_t max_lengths, uint16_t area_size[8],
+                            uint8_t suffix_bits[8]);
+
+/*
  * Huffman codebook ("Single-Stage Huffman Encoder for ML Compression",
  * abstract and method steps 2-3: one tree built from the average
  * distribution of earlier batches).

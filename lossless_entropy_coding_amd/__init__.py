@@ -20,7 +20,7 @@ __all__ = [
     "max_encoded_bytes", "QLC_BASE", "QLC_ADAPTED", "CODEC_QLC", "CODEC_HUFFMAN",
     "CODEC_EXP_GOLOMB", "S_CAPACITY", "S_CORRUPT", "S_BAD_HEADER", "S_CODEBOOK_MISMATCH",
     "S_BAD_CODEBOOK", "EXPORTS", "device_codebook_bytes", "build_huffman_device", "own_max_encoded_bytes",
-    "encode_batch_device", "decode_batch_device", "huffman_tables_from_streams",
+    "encode_batch_device", "decode_batch_device", "huffman_tables_from_streams", "qlc_optimal_area_layout",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libec.so")
@@ -46,6 +46,7 @@ _int = ctypes.c_int
 # name -> (restype, argtypes); every function declared in include/ec.h
 EXPORTS = {
     "qlc_build_codebook": (_int, [_u64p, _u16p, _u8p, ctypes.POINTER(_vp)]),
+    "qlc_optimal_area_layout": (_int, [_u64p, _u32, _u16p, _u8p]),
     "huff_build_codebook": (_int, [_u64p, ctypes.POINTER(_vp)]),
     "huff_build_codebook_from_lengths": (_int, [_u8p, ctypes.POINTER(_vp)]),
     "eg_build_codebook": (_int, [_u64p, _int, ctypes.POINTER(_vp)]),
@@ -210,6 +211,16 @@ class Codebook:
             self.free()
         except Exception:
             pass
+
+
+def qlc_optimal_area_layout(counts, max_lengths: int = 4):
+    """(area_size, suffix_bits) of the cheapest QLC layout for these counts
+    with at most ``max_lengths`` distinct code lengths."""
+    n = (ctypes.c_uint16 * 8)()
+    b = (ctypes.c_uint8 * 8)()
+    _check(lib().qlc_optimal_area_layout(_arr(ctypes.c_uint64, counts), int(max_lengths), n, b),
+           "qlc_optimal_area_layout")
+    return tuple(int(v) for v in n), tuple(int(v) for v in b)
 
 
 def huff_code_lengths(weights) -> list:

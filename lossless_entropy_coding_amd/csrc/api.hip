@@ -240,6 +240,11 @@ int qlc_build_codebook(const uint64_t counts[256], const uint16_t area_size[8], 
     return build_qlc(counts, area_size, suffix_bits, out);
 }
 
+int qlc_optimal_area_layout(const uint64_t counts[256], uint32_t max_lengths, uint16_t area_size[8],
+                            uint8_t suffix_bits[8]) {
+    return qlc_optimal_areas(counts, max_lengths, area_size, suffix_bits);
+}
+
 int huff_build_codebook(const uint64_t counts[256], ec_codebook **out) {
     if (!counts || !out) return EC_E_INVAL;
     uint64_t w[256];

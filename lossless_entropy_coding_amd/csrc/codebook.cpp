@@ -119,6 +119,75 @@ int build_qlc(const uint64_t counts[256], const uint16_t area_size[8], const uin
     return EC_OK;
 }
 
+// QLC area layout with the fewest payload bits for these counts (QLC page,
+// section 2: sizes and lengths of the areas adapt to the distribution, at
+// most four distinct lengths; section 5: an optimised choice of both is the
+// authors' next step).  With ranks sorted by decreasing count, some optimum
+// has non-decreasing suffix widths, every non-empty area but the last full
+// (2^width symbols) and the unused areas (size 0, width 0) at the end, so a
+// layout is a non-decreasing width sequence that stops once its capacity
+// reaches 256.  Dynamic programme over (first uncoded rank, areas used, last
+// width, distinct widths): best[] holds the fewest bits for the ranks still
+// to code; the layout is then read forwards taking the smallest width that
+// keeps the optimum, which gives the lexicographically smallest width
+// sequence among the cheapest layouts.
+int qlc_optimal_areas(const uint64_t counts[256], uint32_t max_lengths, uint16_t area_size[8],
+                      uint8_t suffix_bits[8]) {
+    if (!counts || !area_size || !suffix_bits || max_lengths < 1 || max_lengths > 8) return EC_E_INVAL;
+    typedef unsigned __int128 u128;
+    const u128 kInf = ~(u128)0;
+    uint8_t sym[256];
+    rank_order(counts, sym);
+    u128 P[257];   // P[i]: counts of ranks below i
+    P[0] = 0;
+    for (int r = 0; r < 256; ++r) P[r + 1] = P[r] + counts[sym[r]];
+
+    // state (i, k, bp, d): ranks [i, 256) left, k areas used, last width bp,
+    // d distinct widths so far
+    static thread_local u128 best[257][9][9][9];
+    static thread_local uint8_t seen[257][9][9][9];
+    memset(seen, 0, sizeof(seen));
+    // cost of the next area of width b at state (i, k, bp, d), kInf if not allowed
+    auto step = [&](auto &self, uint32_t i, uint32_t k, uint32_t bp, uint32_t d, uint32_t b) -> u128 {
+        const uint32_t nd = d + ((k == 0 || b != bp) ? 1u : 0u);
+        if (nd > max_lengths) return kInf;
+        const uint32_t n = std::min<uint32_t>(1u << b, 256 - i);
+        const u128 c = (u128)(3 + b) * (P[i + n] - P[i]);
+        if (i + n == 256) return c;
+        if (k + 1 >= 8) return kInf;
+        const u128 rest = self(self, i + n, k + 1, b, nd);
+        return rest == kInf ? kInf : c + rest;
+    };
+    auto solve = [&](auto &self, uint32_t i, uint32_t k, uint32_t bp, uint32_t d) -> u128 {
+        if (seen[i][k][bp][d]) return best[i][k][bp][d];
+        u128 m = kInf;
+        for (uint32_t b = (k ? bp : 0); b <= 8; ++b) m = std::min(m, step(self, i, k, bp, d, b));
+        seen[i][k][bp][d] = 1;
+        best[i][k][bp][d] = m;
+        return m;
+    };
+    if (solve(solve, 0, 0, 0, 0) == kInf) return EC_E_INVAL;   // cannot happen: eight areas of 32 always fit
+
+    uint32_t i = 0, k = 0, bp = 0, d = 0;
+    for (int a = 0; a < 8; ++a) {
+        area_size[a] = 0;
+        suffix_bits[a] = 0;
+    }
+    while (i < 256) {
+        const u128 target = best[i][k][bp][d];
+        uint32_t b = k ? bp : 0;
+        while (step(solve, i, k, bp, d, b) != target) ++b;
+        const uint32_t n = std::min<uint32_t>(1u << b, 256 - i);
+        area_size[k] = (uint16_t)n;
+        suffix_bits[k] = (uint8_t)b;
+        d += (k == 0 || b != bp) ? 1u : 0u;
+        bp = b;
+        i += n;
+        ++k;
+    }
+    return EC_OK;
+}
+
 // -------------------------------------------------------------- Huffman
 
 // Two-queue Huffman: leaves sorted by (weight, index) in one queue, merged

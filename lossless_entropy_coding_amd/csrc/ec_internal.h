@@ -66,6 +66,8 @@ int build_qlc(const uint64_t counts[256], const uint16_t area_size[8], const uin
               ec_codebook **out);
 int build_huffman_lengths(const uint8_t code_len[256], ec_codebook **out);
 int build_eg(const uint64_t counts[256], int k, ec_codebook **out);
+int qlc_optimal_areas(const uint64_t counts[256], uint32_t max_lengths, uint16_t area_size[8],
+                      uint8_t suffix_bits[8]);
 int huffman_lengths(const uint64_t *weights, uint32_t n, uint8_t *len_out);
 
 }  // namespace ec

@@ -27,9 +27,9 @@ torch = pytest.importorskip("torch")
 DEV = "cuda:0"
 
 CASES = [("tiny_qlc", "qlc"),
-         ("ffn1", "qlc"), ("ffn1", "huffman"),
-         ("ffn2", "qlc_adapted"), ("ffn2", "qlc"), ("ffn2", "huffman"),
-         ("grad", "eg"), ("grad", "qlc"), ("grad", "huffman")]
+         ("ffn1", "qlc"), ("ffn1", "huffman"), ("ffn1", "qlc_opt"),
+         ("ffn2", "qlc_adapted"), ("ffn2", "qlc"), ("ffn2", "huffman"), ("ffn2", "qlc_opt"), ("ffn2", "qlc_free"),
+         ("grad", "eg"), ("grad", "qlc"), ("grad", "huffman"), ("grad", "qlc_opt")]
 
 
 @pytest.fixture(scope="module")
@@ -53,6 +53,11 @@ def _codebooks(ec, name, counts):
     if name == "qlc_adapted":
         return (ec.Codebook.qlc(counts, *ec.QLC_ADAPTED),
                 cbm.qlc_codebook(counts, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX))
+    if name in ("qlc_opt", "qlc_free"):
+        L = 4 if name == "qlc_opt" else 8
+        layout = ec.qlc_optimal_area_layout(counts, L)
+        assert layout == cbm.qlc_optimal_areas(counts, L)
+        return ec.Codebook.qlc(counts, *layout), cbm.qlc_codebook(counts, *cbm.qlc_optimal_areas(counts, L))
     if name == "huffman":
         return ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
     if name == "eg":

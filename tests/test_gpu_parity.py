@@ -40,6 +40,11 @@ def _pair(ec, name, counts):
     if name == "qlc_adapted":
         return (ec.Codebook.qlc(counts, *ec.QLC_ADAPTED),
                 cbm.qlc_codebook(counts, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX))
+    if name in ("qlc_opt", "qlc_free"):
+        L = 4 if name == "qlc_opt" else 8
+        layout = ec.qlc_optimal_area_layout(counts, L)
+        assert layout == cbm.qlc_optimal_areas(counts, L)
+        return ec.Codebook.qlc(counts, *layout), cbm.qlc_codebook(counts, *cbm.qlc_optimal_areas(counts, L))
     if name == "huffman":
         return ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
     if name == "eg":
@@ -67,7 +72,7 @@ def _gpu_decode(ec, cb, stream_bytes, n):
     return y.cpu().numpy(), int(status.item())
 
 
-CODECS = ["qlc", "qlc_adapted", "huffman", "eg", "eg0", "eg8"]
+CODECS = ["qlc", "qlc_adapted", "qlc_opt", "qlc_free", "huffman", "eg", "eg0", "eg8"]
 SIZES = [(1, 256), (255, 4096), (256, 256), (257, 256), (4095, 4096), (4096, 4096), (4097, 4096),
          (3 * 4096 + 17, 4096), (16384 * 3 + 999, 16384), (100_000, 1024), (70_001, 8192), (50_000, 12288)]
 
@@ -86,6 +91,37 @@ def test_stream_and_round_trip_match_oracle(ec, name, n, C):
     y, dstatus = _gpu_decode(ec, cb, want, n)
     assert dstatus == 0
     assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("C", [256, 4096, 16384])
+@pytest.mark.parametrize("layout_kind", ["optimal", "empty_areas"])
+def test_qlc_layout_with_three_bit_codes_and_empty_areas(ec, C, layout_kind):
+    # one symbol holds almost everything: the cheapest layout gives it a
+    # 3-bit code (an area of suffix width 0); the second layout also leaves
+    # areas 1, 2 and 4-7 empty, so their prefixes are never codewords.  The
+    # data mixes long runs of that symbol with every other byte.
+    print("case qlc spike layout", layout_kind, C, flush=True)
+    counts = [1] * 256
+    counts[0x40] = 1 << 40
+    if layout_kind == "optimal":
+        layout = ec.qlc_optimal_area_layout(counts, 4)
+        assert layout == cbm.qlc_optimal_areas(counts, 4)
+    else:
+        layout = ((1, 0, 0, 255, 0, 0, 0, 0), (0, 0, 0, 8, 0, 0, 0, 0))
+    assert layout[1][0] == 0
+    cb, ocb = ec.Codebook.qlc(counts, *layout), cbm.qlc_codebook(counts, *layout)
+    assert ocb.length[0x40] == 3
+    rng = np.random.default_rng(C)
+    n = 5 * C + 77
+    x = np.full(n, 0x40, dtype=np.uint8)
+    pos = rng.choice(n, n // 9, replace=False)
+    x[pos] = rng.integers(0, 256, pos.size, dtype=np.uint8)
+    x[: 3 * 256] = np.arange(3 * 256) % 256
+    want = st.encode_stream(x, ocb, C)
+    got, status = _gpu_encode(ec, cb, x, C)
+    assert status == 0 and got == want
+    y, dstatus = _gpu_decode(ec, cb, want, n)
+    assert dstatus == 0 and np.array_equal(y, x)
 
 
 def test_empty_input(ec):
