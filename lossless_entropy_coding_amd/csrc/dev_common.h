@@ -72,6 +72,8 @@ struct EncodeArgs {
     uint32_t stage_bytes;     // LDS stage of the staged packer (set at launch)
     uint32_t tables_unread;   // 1: the host never read the tables (device-built); the packers check
                               // each chunk's table for codes longer than kNarrowMaxLen themselves
+    uint32_t place_in_pack;   // 1: this pack launch sums the chunk sizes itself and writes chunk_off[],
+                              // the header and the index tail (no separate offsets launch)
     const DevTables *tabs[EC_MAX_BATCH];
 };
 

@@ -10,6 +10,10 @@
 //      the stream's chunk sizes -> chunk_off[], payload_bytes and the stream
 //      length; writes the header, the embedded code lengths and the zero
 //      padding in front of the payload; flags a stream that does not fit.
+//      Only for streams of more than kPlaceMaxChunks chunks: for shorter
+//      ones the first pack launch does this itself (every workgroup sums the
+//      sizes of the chunks before its own, the stream's last chunk writes
+//      the header, its first chunk the index tail), one launch fewer.
 //   3. encode_pack_*_kernel (one workgroup per chunk): loads the chunk again,
 //      looks each symbol's code up in the codebook's LUT in LDS (code
 //      left-aligned, length in the low byte), scans the piece lengths, ORs the
@@ -159,13 +163,50 @@ __global__ __launch_bounds__(kThreads) void encode_sizes_kernel(const EncodeArgs
 
 constexpr int kScanThreads = 1024;
 
-// Header fields, chunk_off[], payload_bytes, the stream length, the embedded
-// code lengths and the zero fill up to the payload of stream `blockIdx.x`.
+// Header fields, chunk_off[n_chunks] and the stream length of stream `seg`
+// whose payload has `payload` bytes; flags a stream that does not fit and an
+// unusable codebook.  One thread.
+__device__ void write_header(const EncodeArgs &a, uint32_t seg, uint64_t payload) {
+    const DevTables *tab = seg_tables<EncodeArgs>(seg);
+    uint8_t *out = a.out + (uint64_t)seg * a.out_stride;
+    const uint32_t n = a.chunks_per_seg;
+    reinterpret_cast<uint64_t *>(out + kHeaderBytes)[n] = payload;
+    const uint64_t end = (uint64_t)a.payload_offset + payload;
+    uint64_t *h = reinterpret_cast<uint64_t *>(out);
+    h[0] = (uint64_t)kMagic | ((uint64_t)kVersion << 32) | ((uint64_t)tab->codec << 48) |
+           ((uint64_t)(a.embed_lengths ? 1 : 0) << 56);
+    h[1] = a.seg_n;
+    h[2] = (uint64_t)a.chunk_symbols | ((uint64_t)n << 32);
+    h[3] = a.payload_offset;
+    h[4] = payload;
+    h[5] = tab->codebook_id;
+    h[6] = 0;
+    h[7] = 0;
+    a.out_len[seg] = end;
+    if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
+    if (tab->codec == 0) or_status(a.status ? a.status + seg : nullptr, EC_S_BAD_CODEBOOK);
+}
+
+// The embedded code lengths and the zero fill from the end of the index to
+// the payload of stream `seg`, by threads tid of nthreads.
+__device__ void write_index_tail(const EncodeArgs &a, uint32_t seg, uint32_t tid, uint32_t nthreads) {
+    const DevTables *tab = seg_tables<EncodeArgs>(seg);
+    uint8_t *out = a.out + (uint64_t)seg * a.out_stride;
+    const uint32_t index_end = a.sub_at + 4u * a.chunks_per_seg * (a.chunk_symbols / kSub);
+    uint32_t pad_from = index_end;
+    if (a.embed_lengths) {
+        for (uint32_t i = tid; i < 256; i += nthreads) out[index_end + i] = tab->code_len[i];
+        pad_from += 256;
+    }
+    for (uint32_t i = pad_from + tid; i < a.payload_offset; i += nthreads) out[i] = 0;
+}
+
+// chunk_off[], the header, the stream length, the embedded code lengths and
+// the zero fill up to the payload of stream `blockIdx.x` (long streams).
 __global__ __launch_bounds__(kScanThreads) void encode_offsets_kernel(const EncodeArgs a) {
     __shared__ uint64_t wsum[kScanThreads / 64];
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t seg = blockIdx.x;
-    const DevTables *tab = seg_tables<EncodeArgs>(seg);
     uint8_t *out = a.out + (uint64_t)seg * a.out_stride;
     const uint32_t n = a.chunks_per_seg;
     const uint32_t *sz = a.sizes + (uint64_t)seg * n;
@@ -232,31 +273,8 @@ __global__ __launch_bounds__(kScanThreads) void encode_offsets_kernel(const Enco
             run += sz[i];
         }
     }
-    const uint64_t payload = total * 16;
-    const uint64_t end = (uint64_t)a.payload_offset + payload;
-    if (tid == 0) {
-        chunk_off[n] = payload;
-        uint64_t *h = reinterpret_cast<uint64_t *>(out);
-        h[0] = (uint64_t)kMagic | ((uint64_t)kVersion << 32) | ((uint64_t)tab->codec << 48) |
-               ((uint64_t)(a.embed_lengths ? 1 : 0) << 56);
-        h[1] = a.seg_n;
-        h[2] = (uint64_t)a.chunk_symbols | ((uint64_t)n << 32);
-        h[3] = a.payload_offset;
-        h[4] = payload;
-        h[5] = tab->codebook_id;
-        h[6] = 0;
-        h[7] = 0;
-        a.out_len[seg] = end;
-        if (end > a.out_cap) or_status(a.status ? a.status + seg : nullptr, EC_S_CAPACITY);
-        if (tab->codec == 0) or_status(a.status ? a.status + seg : nullptr, EC_S_BAD_CODEBOOK);
-    }
-    const uint32_t index_end = a.sub_at + 4u * n * (a.chunk_symbols / kSub);
-    uint32_t pad_from = index_end;
-    if (a.embed_lengths) {
-        for (uint32_t i = tid; i < 256; i += kScanThreads) out[index_end + i] = tab->code_len[i];
-        pad_from += 256;
-    }
-    for (uint32_t i = pad_from + tid; i < a.payload_offset; i += kScanThreads) out[i] = 0;
+    if (tid == 0) write_header(a, seg, total * 16);
+    write_index_tail(a, seg, tid, kScanThreads);
 }
 
 // ----------------------------------------------------------------- 3. pack
@@ -291,12 +309,58 @@ __device__ __forceinline__ void or_code64(uint32_t *buf, uint32_t pos, uint32_t 
     atomicOr(&buf[w + 2], __builtin_amdgcn_alignbit(lo, 0u, pos));
 }
 
+// Chunks per stream up to which a pack launch places the chunks itself.
+constexpr uint32_t kPlaceMaxChunks = 4096;
+constexpr int kPlaceLoads = kPlaceMaxChunks / kThreads;
+
+// Placement by the pack launch, step 1: this thread's share of the sizes of
+// the stream's chunks before chunk p (kPlaceLoads loads, all in flight, from
+// the sizes kernel's output in L2).  Issued before the chunk's own loads.
+__device__ __forceinline__ void place_issue(const EncodeArgs &a, const ChunkPos &p, uint32_t tid,
+                                           uint32_t (&szv)[kPlaceLoads]) {
+    const uint32_t *sz = a.sizes + (uint64_t)p.seg * a.chunks_per_seg;
+    static_for<0, kPlaceLoads>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        const uint32_t i = tid + (uint32_t)k * kThreads;
+        szv[k] = i < p.lc ? sz[i] : 0u;
+    });
+}
+
+// Step 2 (the whole workgroup): the 16-byte units before chunk p, summed
+// over the workgroup; thread 0 records chunk_off[lc], the stream's last
+// chunk writes the header and its first chunk the index tail.  Returns the
+// byte offset of the chunk's payload in its stream.
+__device__ __forceinline__ uint64_t place_finish(const EncodeArgs &a, const ChunkPos &p, uint32_t tid, uint32_t lane,
+                                                 uint32_t wave, const uint32_t (&szv)[kPlaceLoads],
+                                                 uint32_t *red) {
+    uint32_t x = 0;
+    static_for<0, kPlaceLoads>([&](auto kc) __attribute__((always_inline)) { x += szv[decltype(kc)::value]; });
+    x = wave_incl_scan(x);
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) before += red[w];
+    if (tid == 0) {
+        reinterpret_cast<uint64_t *>(p.out + kHeaderBytes)[p.lc] = (uint64_t)before * 16;
+        if (p.lc == a.chunks_per_seg - 1)
+            write_header(a, p.seg, ((uint64_t)before + a.sizes[(uint64_t)p.seg * a.chunks_per_seg + p.lc]) * 16);
+    }
+    if (p.lc == 0) write_index_tail(a, p.seg, tid, kThreads);
+    return (uint64_t)a.payload_offset + (uint64_t)before * 16;
+}
+
 // Byte offset of the chunk's payload in its stream, or ~0 when the chunk
-// must not be written (the stream does not fit in out_cap).
-__device__ __forceinline__ uint64_t chunk_dst(const EncodeArgs &a, const ChunkPos &p, uint32_t units) {
-    const uint64_t off = reinterpret_cast<const uint64_t *>(p.out + kHeaderBytes)[p.lc];
-    const uint64_t end = (uint64_t)a.payload_offset + off + (uint64_t)units * 16;
-    return end > a.out_cap ? ~0ull : (uint64_t)a.payload_offset + off;
+// must not be written (the stream does not fit in out_cap).  `placed` is
+// place_finish's result when this launch places the chunks itself;
+// otherwise chunk_off[] was written by an earlier launch.
+__device__ __forceinline__ uint64_t chunk_dst(const EncodeArgs &a, const ChunkPos &p, uint32_t units,
+                                              uint64_t placed) {
+    const uint64_t at = a.place_in_pack
+                            ? placed
+                            : (uint64_t)a.payload_offset + reinterpret_cast<const uint64_t *>(p.out + kHeaderBytes)[p.lc];
+    const uint64_t end = at + (uint64_t)units * 16;
+    return end > a.out_cap ? ~0ull : at;
 }
 
 // Staged packing, for chunks of up to 4 rows (16384 symbols) and codes of up
@@ -400,14 +464,21 @@ __global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const E
     __shared__ uint32_t lut32[256];
     __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
 
+    __shared__ uint32_t red[kThreads / 64];
+
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const ChunkPos p = chunk_pos(a, blockIdx.x);
     // a table the host never saw may have codes too long for the 32-bit
     // entries (then all zero): its chunks go to the row-by-row packer
-    if (a.tables_unread && seg_tables<EncodeArgs>(p.seg)->max_len > (uint32_t)kNarrowMaxLen) return;
+    const bool skip = a.tables_unread && seg_tables<EncodeArgs>(p.seg)->max_len > (uint32_t)kNarrowMaxLen;
+    uint32_t szv[kPlaceLoads];
+    if (a.place_in_pack) place_issue(a, p, tid, szv);
     uint4 v[ROWS];
     uint32_t vb[ROWS];
-    load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
+    if (!skip) load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
+    // uniform over the launch; every chunk is placed, also those packed later
+    const uint64_t placed = a.place_in_pack ? place_finish(a, p, tid, lane, wave, szv, red) : 0;
+    if (skip) return;
     lut32[tid] = seg_tables<EncodeArgs>(p.seg)->enc32[tid];
     __syncthreads();
 
@@ -427,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const E
     uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
     const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
     const uint32_t units = (chunk_bits + 127) >> 7;
-    const uint64_t dst_at = chunk_dst(a, p, units);
+    const uint64_t dst_at = chunk_dst(a, p, units, placed);
     // uniform over the workgroup: chunks that do not fit are packed by the
     // row-by-row kernel that follows
     if (dst_at == ~0ull || !fits_stage(a, units)) return;
@@ -454,15 +525,21 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
     __shared__ uint64_t lut64[256];
     __shared__ uint32_t wave_tot[ROWS][kThreads / 64];
 
+    __shared__ uint32_t red[kThreads / 64];
+
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const ChunkPos p = chunk_pos(a, blockIdx.x);
-    // after the staged packer: only the chunks it left
+    // after the staged packer: only the chunks it left (the staged packer
+    // then placed every chunk, so place_in_pack is 0 here)
     if (a.stage_bytes && fits_stage(a, a.sizes[blockIdx.x]) &&
         !(a.tables_unread && seg_tables<EncodeArgs>(p.seg)->max_len > (uint32_t)kNarrowMaxLen))
         return;
+    uint32_t szv[kPlaceLoads];
+    if (a.place_in_pack) place_issue(a, p, tid, szv);
     uint4 v[ROWS];
     uint32_t vb[ROWS];
     load_pieces<ROWS>(p.src, p.cn, tid, v, vb);
+    const uint64_t placed = a.place_in_pack ? place_finish(a, p, tid, lane, wave, szv, red) : 0;
     lut64[tid] = seg_tables<EncodeArgs>(p.seg)->enc64[tid];
     __syncthreads();
 
@@ -479,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
     uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
     const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
     const uint32_t units = (chunk_bits + 127) >> 7;
-    const uint64_t dst_at = chunk_dst(a, p, units);
+    const uint64_t dst_at = chunk_dst(a, p, units, placed);
     if (dst_at == ~0ull) return;   // uniform over the workgroup: nobody reaches a later barrier
 
     uint32_t *dst = reinterpret_cast<uint32_t *>(p.out + dst_at);
@@ -518,7 +595,10 @@ template <int ROWS>
 hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t s) {
     EncodeArgs a = a_in;
     hipLaunchKernelGGL((encode_sizes_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(encode_offsets_kernel, dim3(a.n_seg), dim3(kScanThreads), 0, s, a);
+    // short streams: the first pack launch places the chunks itself
+    const bool place = a.chunks_per_seg <= kPlaceMaxChunks;
+    a.place_in_pack = place ? 1u : 0u;
+    if (!place) hipLaunchKernelGGL(encode_offsets_kernel, dim3(a.n_seg), dim3(kScanThreads), 0, s, a);
     // row buffer of the row-by-row packer: one row's bits plus the carried
     // word, the final padding and the spare words the three-word ORs may touch
     const uint32_t rows_lds = (kRowSyms * a.max_len / 32 + 8) * 4;
@@ -539,6 +619,7 @@ hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t 
             else
                 hipLaunchKernelGGL((encode_pack_staged_kernel<ROWS, false>), dim3(n_chunks), dim3(kThreads),
                                    a.stage_bytes, s, a);
+            a.place_in_pack = 0;   // the chunks are placed; the row packer reads chunk_off[]
         }
     }
     if (!all_staged)

@@ -275,22 +275,42 @@ def test_batch_matches_oracle(ec, per_segment, embed):
     assert np.array_equal(y.cpu().numpy(), x)
 
 
-def test_capacity_overflow_reports_required_length(ec):
+@pytest.mark.parametrize("chunks", [4095, 4096, 4097, 5000])
+@pytest.mark.parametrize("name", ["qlc", "huffman", "eg"])
+def test_streams_around_the_placement_switch(ec, name, chunks):
+    # up to 4096 chunks a stream the pack launch places the chunks itself;
+    # beyond, a separate scan launch does: both must give the oracle's stream
+    print("case chunks", name, chunks, flush=True)
+    C = 256
+    n = chunks * C - 7
+    counts = _calib_counts()
+    cb, ocb = _pair(ec, name, counts)
+    x = synth.draw("ffn1", 31 + chunks, n)
+    want = st.encode_stream(x, ocb, C)
+    got, status = _gpu_encode(ec, cb, x, C)
+    assert status == 0
+    assert got == want
+    y, dstatus = _gpu_decode(ec, cb, want, n)
+    assert dstatus == 0 and np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("n,C", [(200_000, 4096), (5000 * 256, 256)])
+def test_capacity_overflow_reports_required_length(ec, n, C):
     counts = _calib_counts()
     cb, ocb = _pair(ec, "qlc", counts)
-    x = synth.draw("ffn1", 11, 200_000)
-    want = st.encode_stream(x, ocb, 4096)
+    x = synth.draw("ffn1", 11, n)
+    want = st.encode_stream(x, ocb, C)
     xd = torch.from_numpy(x).to(DEV)
     cap = (len(want) - 1000) // 16 * 16
     big = torch.full((cap + 8192,), 0xCD, dtype=torch.uint8, device=DEV)
     out, guard = big[:cap], big[cap:]
-    _, out_len, status = ec.encode(cb, xd, 4096, out=out)
+    _, out_len, status = ec.encode(cb, xd, C, out=out)
     torch.cuda.synchronize()
     assert int(status.item()) & ec.S_CAPACITY
     assert int(out_len.item()) == len(want)
     assert bool((guard == 0xCD).all())
     with pytest.raises(ec.ECError):       # cannot even hold the index
-        ec.encode(cb, xd, 4096, out=torch.empty(100, dtype=torch.uint8, device=DEV))
+        ec.encode(cb, xd, C, out=torch.empty(100, dtype=torch.uint8, device=DEV))
 
 
 def test_corruption_and_header_errors_are_reported(ec):

@@ -1,4 +1,4 @@
-"""Pins for the QLC area-layout search (oracle) and the library's own search.
+"""Pins for the oracle's QLC area-layout search.
 
 The oracle enumerates only layouts of a canonical shape (widths that never
 decrease, every non-empty area but the last full); the brute-force tests
