@@ -187,12 +187,13 @@ int decode_impl(TableSrc ts, uint32_t codec, uint32_t n_seg, const uint8_t *d_in
         for (uint32_t i = 0; i < n_seg; ++i) a.tabs[i] = dev_table(ts.dev, i);
     } else {
         codec = ts.cbs[0] ? ts.cbs[0]->host.codec : 0;
+        max_len = 0;
         for (uint32_t i = 0; i < n_seg; ++i) {
             if (!ts.cbs[i] || ts.cbs[i]->host.codec != codec) return EC_E_INVAL;
             int rc = device_tables(ts.cbs[i], &a.tabs[i]);
             if (rc) return rc;
+            max_len = ts.cbs[i]->host.max_len > max_len ? ts.cbs[i]->host.max_len : max_len;
         }
-        max_len = ts.cbs[0]->host.max_len;
     }
     a.in = d_in;
     a.in_stride = in_stride;

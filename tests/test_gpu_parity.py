@@ -124,6 +124,35 @@ def test_qlc_layout_with_three_bit_codes_and_empty_areas(ec, C, layout_kind):
     assert dstatus == 0 and np.array_equal(y, x)
 
 
+@pytest.mark.parametrize("r,profile", [(0.9973, (8, 8, 0)), (0.9907, (7, 10, 3)), (0.979, (6, 13, 7)),
+                                       (0.9757, (5, 14, 8)), (0.9116, (4, 17, 9))])
+def test_huffman_length_profiles(ec, r, profile):
+    # Codebooks of one length only, of lengths up to 10 and 13 bits (every
+    # code in the decoder's 13-bit table), and with 14- and 17-bit codes
+    # (longer codes than the table covers); runs of the longest codes at odd
+    # offsets.
+    print("case huffman profile", profile, flush=True)
+    counts = [int(1e4 * r ** s) for s in range(256)]
+    ocb = cbm.huffman_codebook(counts)
+    lo, hi = min(ocb.length), max(ocb.length)
+    assert (lo, hi, max(min(hi - 1, 12) - lo + 1, 0)) == profile
+    cb = ec.Codebook.huffman(counts)
+    rng = np.random.default_rng(int(r * 1e4))
+    p = np.array(counts, dtype=np.float64) + 1
+    n = 150_000
+    x = rng.choice(256, size=n, p=p / p.sum()).astype(np.uint8)
+    x[:512] = np.arange(512) % 256                      # every code, the longest included
+    rare = np.argsort(ocb.length)[-8:]                  # runs of the longest codes at odd offsets
+    for k, at in enumerate((1031, 5000, 77_777, 120_003)):
+        x[at:at + 40] = rare[(np.arange(40) + k) % 8]
+    for C in (4096, 16384):
+        want = st.encode_stream(x, ocb, C)
+        got, status = _gpu_encode(ec, cb, x, C)
+        assert status == 0 and got == want
+        y, dstatus = _gpu_decode(ec, cb, want, n)
+        assert dstatus == 0 and np.array_equal(y, x)
+
+
 def test_empty_input(ec):
     counts = _calib_counts()
     for name in ("qlc", "huffman", "eg"):
@@ -292,6 +321,32 @@ def test_streams_around_the_placement_switch(ec, name, chunks):
     assert got == want
     y, dstatus = _gpu_decode(ec, cb, want, n)
     assert dstatus == 0 and np.array_equal(y, x)
+
+
+def test_batch_exp_golomb_of_mixed_orders(ec):
+    # order 1 codes fit two to a 32-bit window (at most 16 bits), order 0
+    # codes do not (up to 17 bits): the decoder's mode must suit every
+    # segment of the batch, not just the first
+    counts = _calib_counts()
+    S, seg_n, C = 3, 50_000, 4096
+    ks = [1, 0, 5]
+    cbs = [ec.Codebook.exp_golomb(counts, k) for k in ks]
+    ocbs = [cbm.eg_codebook(counts, k) for k in ks]
+    assert [max(o.length) for o in ocbs][:2] == [16, 17]
+    x = np.stack([synth.draw("ffn1", 300 + s, seg_n) for s in range(S)])
+    x[1, :256] = np.arange(256)
+    x[1, 300:340] = ocbs[1].rank_to_sym[255]   # back-to-back 17-bit codes in segment 1
+    xd = torch.from_numpy(x).to(DEV)
+    out, out_len, status = ec.encode_batch(cbs, xd, C)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    lens = out_len.cpu().numpy()
+    for s in range(S):
+        assert out[s, : int(lens[s])].cpu().numpy().tobytes() == st.encode_stream(x[s], ocbs[s], C)
+    y, dstatus = ec.decode_batch(cbs, out, seg_n)
+    torch.cuda.synchronize()
+    assert (dstatus.cpu().numpy() == 0).all()
+    assert np.array_equal(y.cpu().numpy(), x)
 
 
 @pytest.mark.parametrize("n,C", [(200_000, 4096), (5000 * 256, 256)])
