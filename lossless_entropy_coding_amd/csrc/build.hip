@@ -151,7 +151,7 @@ __device__ void canonical_tables(BuildSmem &sm, DevTables *t, uint32_t tid) {
             uint16_t e = 0;
             if (l <= (uint32_t)kHuffBits) {
                 const uint32_t idx = sm.fidx[l] + (uint32_t)((w >> (kHuffBits - l)) - sm.fcode[l]);
-                e = (uint16_t)(sm.symc[idx & 255u] | (l << 8));
+                e = (uint16_t)(l | ((uint32_t)sm.symc[idx & 255u] << 8));
             }
             t->hl1[w] = e;
         }

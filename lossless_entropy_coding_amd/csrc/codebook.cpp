@@ -274,14 +274,16 @@ int build_huffman_lengths(const uint8_t len[256], ec_codebook **out) {
     for (uint32_t l = 1; l <= (uint32_t)EC_MAX_CODE_LEN; ++l)
         t.limit[l] = ((uint64_t)t.first_code[l] + bl_count[l]) << (EC_MAX_CODE_LEN - l);
 
-    // 13-bit decode table: windows whose code has <= 13 bits; 0 marks the
-    // prefixes of longer codes (found by the canonical limit search)
+    // 13-bit decode table: windows whose code has <= 13 bits hold its length
+    // in the low byte and its byte value in the high byte (a shift by the
+    // entry then moves past the code); 0 marks the prefixes of longer codes
+    // (found by the canonical limit search)
     for (int w = 0; w < kHuffSize; ++w) t.hl1[w] = 0;
     for (int s = 0; s < 256; ++s) {
         uint32_t l = len[s];
         if (l == 0 || l > (uint32_t)kHuffBits) continue;
         uint32_t lo = (uint32_t)code[s] << (kHuffBits - l), hi = lo + (1u << (kHuffBits - l));
-        for (uint32_t w = lo; w < hi; ++w) t.hl1[w] = (uint16_t)(s | (l << 8));
+        for (uint32_t w = lo; w < hi; ++w) t.hl1[w] = (uint16_t)(l | ((uint32_t)s << 8));
     }
 
     uint8_t desc[257];

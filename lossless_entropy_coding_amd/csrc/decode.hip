@@ -17,8 +17,9 @@
 //            and a byte permute of the per-area lengths (no memory access on
 //            the dependency chain); the top 11 bits index a 2048-entry LDS
 //            table that yields the byte or flags an unused suffix.
-//   Huffman  the top 13 bits index a 16 KiB LDS table that yields the byte
-//            and the length of every code of up to 13 bits; longer codes
+//   Huffman  the top 13 bits index a 16 KiB LDS table that yields the length
+//            (low byte: a shift by the entry itself moves past the code) and
+//            the byte (high byte) of every code of up to 13 bits; longer codes
 //            (rare) are found by comparing a 40-bit window against the
 //            canonical code limits.
 //   EG       count leading zeros z; the code is 2z + k + 1 bits; rank -> byte
@@ -139,7 +140,8 @@ struct DeepTables {
 };
 
 // Huffman code longer than 13 bits (rare): canonical limit search on a
-// 40-bit left-justified window.  Returns symbol | length << 8.
+// 40-bit left-justified window.  Returns length | symbol << 8, the format
+// of the decode table's entries.
 __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt, const uint8_t *sym, uint32_t mx) {
     const uint64_t w40 = window >> (64 - EC_MAX_CODE_LEN);
     uint32_t l = kHuffBits + 1;
@@ -147,7 +149,7 @@ __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt
     const uint32_t i = l - kHuffBits - 1;
     const uint64_t code = w40 >> (EC_MAX_CODE_LEN - l);
     const uint32_t idx = dt->first_idx[i] + (uint32_t)(code - dt->first_code[i]);
-    return sym[idx & 255] | (l << 8);
+    return l | ((uint32_t)sym[idx & 255] << 8);
 }
 
 // Status bits from a rare path, behind a call: the decode loop then has a
@@ -174,12 +176,13 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             lhi |= ((lens >> (4 * k + 16)) & 15u) << (8 * k);
         }
     }
-    // The code that starts window w: its table entry (symbol in byte 0; for
-    // QLC bit 8 flags an unused suffix) and its length.  QLC takes the length
+    // The code that starts window w: its table entry and its length.  QLC
+    // and EG entries hold the symbol in byte 0 (QLC: bit 8 flags an unused
+    // suffix); Huffman entries hold the length in byte 0 and the symbol in
+    // byte 1 (0: a code longer than the table covers).  QLC takes the length
     // from the 3-bit prefix, off the memory dependency chain: a funnel shift
     // puts the prefix in byte 0 of a byte-select word whose other bytes
-    // select zero, and a byte permute picks that area's length.  Huffman and
-    // EG entries carry the length in bits 8 and up.
+    // select zero, and a byte permute picks that area's length.
     struct Code {
         uint32_t e, len;
     };
@@ -189,8 +192,8 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             return Code{l1[w >> 21], __builtin_amdgcn_perm(lhi, llo, sel)};
         } else if (CODEC == EC_CODEC_HUFFMAN) {
             uint32_t e = l1[w >> (32 - kHuffBits)];
-            if (e < 256u) e = huff_deep(S.win64(), dt, symtab, max_len);
-            return Code{e, e >> 8};
+            if (e == 0u) e = huff_deep(S.win64(), dt, symtab, max_len);
+            return Code{e, e & 0xffu};
         } else {
             const uint32_t zr = __clz(w);
             const uint32_t z = zr < 8u ? zr : 8u;   // more zeros: not a codeword
@@ -200,11 +203,15 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             return Code{symtab[rank & 255u], l};
         }
     };
+    // the symbol of an entry, and the byte permute that takes the symbols of
+    // two entries (first in byte 0, second in byte 1)
+    constexpr uint32_t kSymShift = CODEC == EC_CODEC_HUFFMAN ? 8 : 0;
+    constexpr uint32_t kPairSel = CODEC == EC_CODEC_HUFFMAN ? 0x0c0c0501u : 0x0c0c0400u;
     auto one = [&]() __attribute__((always_inline)) -> uint32_t {
         const Code c = code_at(S.win());
         if (CODEC == EC_CODEC_QLC) bad |= c.e;
         S.adv(c.len);
-        return c.e & 0xffu;
+        return (c.e >> kSymShift) & 0xffu;
     };
     // two codes from one window when both fit in it; returns byte0 | byte1 << 8
     auto two = [&]() __attribute__((always_inline)) -> uint32_t {
@@ -216,16 +223,18 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             // has at most 13 bits, so 19 bits of the window follow it.  A
             // longer code (rare) sends the lanes that hold one to the
             // canonical search and a fresh window for the second code.
+            // (shifts take their amount modulo 32: a shift by the entry is
+            // a shift by the code's length)
             uint32_t e1 = l1[w >> (32 - kHuffBits)];
-            uint32_t e2 = l1[(w << (e1 >> 8)) >> (32 - kHuffBits)];
-            if (min(e1, e2) < 256u) {
-                if (e1 < 256u) e1 = huff_deep(S.win64(), dt, symtab, max_len);
-                S.adv(e1 >> 8);
+            uint32_t e2 = l1[(w << (e1 & 31u)) >> (32 - kHuffBits)];
+            if (min(e1, e2) == 0u) {
+                if (e1 == 0u) e1 = huff_deep(S.win64(), dt, symtab, max_len);
+                S.adv(e1 & 0xffu);
                 e2 = l1[S.win() >> (32 - kHuffBits)];
-                if (e2 < 256u) e2 = huff_deep(S.win64(), dt, symtab, max_len);
-                S.adv(e2 >> 8);
+                if (e2 == 0u) e2 = huff_deep(S.win64(), dt, symtab, max_len);
+                S.adv(e2 & 0xffu);
             } else {
-                S.adv((e1 >> 8) + (e2 >> 8));
+                S.adv((e1 + e2) & 0xffu);   // lengths of at most 13 bits: no carry into the symbols
             }
             c1.e = e1;
             c2.e = e2;
@@ -234,7 +243,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             S.adv(c1.len + c2.len);
             if (CODEC == EC_CODEC_QLC) bad |= c1.e | c2.e;
         }
-        return __builtin_amdgcn_perm(c2.e, c1.e, 0x0c0c0400u);   // byte 0 of c1.e, byte 0 of c2.e
+        return __builtin_amdgcn_perm(c2.e, c1.e, kPairSel);   // c1's symbol, c2's symbol
     };
     // Four codes from one 64-bit window: the second pair's 32-bit window lies
     // inside the 64 bits when a pair has at most 32 bits (QLC: codes of at
@@ -255,18 +264,20 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             if (CODEC == EC_CODEC_QLC) bad |= c1.e | c2.e | c3.e | c4.e;
             return __builtin_amdgcn_perm(c2.e, c1.e, 0x0c0c0400u) | (__builtin_amdgcn_perm(c4.e, c3.e, 0x0c0c0400u) << 16);
         }
+        // entries hold the length in their low byte: shifts by an entry (or
+        // by the sum of two, for the 64-bit shift, modulo 64) move past the codes
         const uint32_t e1 = l1[w >> (32 - kHuffBits)];
-        const uint32_t e2 = l1[(w << (e1 >> 8)) >> (32 - kHuffBits)];
-        const uint32_t L1 = (e1 >> 8) + (e2 >> 8);
-        const uint32_t v = (uint32_t)((W << L1) >> 32);
+        const uint32_t e2 = l1[(w << (e1 & 31u)) >> (32 - kHuffBits)];
+        const uint32_t e12 = e1 + e2;   // lengths add in the low byte (at most 26)
+        const uint32_t v = (uint32_t)((W << (e12 & 63u)) >> 32);
         const uint32_t e3 = l1[v >> (32 - kHuffBits)];
-        const uint32_t e4 = l1[(v << (e3 >> 8)) >> (32 - kHuffBits)];
-        if (min(min(e1, e2), min(e3, e4)) < 256u) {
+        const uint32_t e4 = l1[(v << (e3 & 31u)) >> (32 - kHuffBits)];
+        if (min(min(e1, e2), min(e3, e4)) == 0u) {
             const uint32_t p0 = two(), p1 = two();
             return p0 | (p1 << 16);
         }
-        S.adv(L1 + (e3 >> 8) + (e4 >> 8));
-        return __builtin_amdgcn_perm(e2, e1, 0x0c0c0400u) | (__builtin_amdgcn_perm(e4, e3, 0x0c0c0400u) << 16);
+        S.adv((e12 + e3 + e4) & 0xffu);
+        return __builtin_amdgcn_perm(e2, e1, kPairSel) | (__builtin_amdgcn_perm(e4, e3, kPairSel) << 16);
     };
     // eight codes -> two output words
     auto eight = [&](uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {

@@ -155,13 +155,13 @@ def test_index_and_max_sizes(ec):
 
 def expected_hl1(ora) -> np.ndarray:
     """13-bit decode table from the oracle's codes, by brute force: window w
-    holds s | len << 8 when it starts with s's code of at most 13 bits."""
+    holds len | s << 8 when it starts with s's code of at most 13 bits."""
     w = np.arange(8192, dtype=np.int64)
     out = np.zeros(8192, dtype=np.uint16)
     for s in range(256):
         L = ora.length[s]
         if L <= 13:
-            out[(w >> (13 - L)) == ora.code[s]] = s | (L << 8)
+            out[(w >> (13 - L)) == ora.code[s]] = L | (s << 8)
     return out
 
 
