@@ -74,6 +74,8 @@ struct EncodeArgs {
                               // each chunk's table for codes longer than kNarrowMaxLen themselves
     uint32_t place_in_pack;   // 1: this pack launch sums the chunk sizes itself and writes chunk_off[],
                               // the header and the index tail (no separate offsets launch)
+    uint32_t staged_rows;     // 1: the staged packer packs a chunk that overflows its stage row by row
+                              // in the stage itself (the row packer then skips such chunks)
     const DevTables *tabs[EC_MAX_BATCH];
 };
 

@@ -451,6 +451,43 @@ __device__ __forceinline__ void emit_row(const PairCache<ROWS> &cc, int r, uint3
     }
 }
 
+// Row-by-row packing inside the staged packer's stage, for a chunk whose
+// packed bits do not fit it (codes far longer than the codebook's typical
+// ones): each row of 4096 codes is ORed into the zeroed stage after the
+// previous row's partial last word (the carry), then its whole words are
+// stored.  A row needs at most kRowSyms * 26 / 32 words plus the carry, the
+// padding to 16 bytes and the spare word (under 8), which the launch checks
+// against the stage.
+template <int ROWS, bool WIDE>
+__device__ __forceinline__ void pack_rows_in_stage(const PairCache<ROWS> &cc, const uint32_t (&excl)[ROWS],
+                                                   const uint32_t (&row_start)[ROWS], const uint32_t (&row_bits)[ROWS],
+                                                   const bool (&wide)[ROWS], const uint32_t (&vb)[ROWS],
+                                                   const uint8_t *src, uint32_t units, uint32_t *stage,
+                                                   uint32_t *dst, uint32_t tid, const uint32_t *lut32) {
+    const uint32_t base_bit = lds_addr(stage) * 8;
+    const uint32_t total_words = units * 4;
+    uint32_t carry = 0;
+    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        constexpr bool last = r == ROWS - 1;
+        const uint32_t rs = row_start[r], re = rs + row_bits[r];
+        const uint32_t wbase = rs >> 5;
+        const uint32_t nbuf = (last ? total_words : (re + 31) >> 5) - wbase;
+        // the row's words plus the spare word a two-word OR may touch
+        for (uint32_t i = tid; i < nbuf + 1; i += kThreads) stage[i] = i == 0 ? carry : 0u;
+        __syncthreads();
+        emit_row<ROWS, WIDE>(cc, r, base_bit + excl[r] - wbase * 32, wide[r], src + (uint32_t)(r * kThreads + tid) * kPiece,
+                             vb[r], lut32);
+        __syncthreads();
+        const uint32_t nwrite = last ? nbuf : (re >> 5) - wbase;
+        for (uint32_t i = tid; i < nwrite; i += kThreads) dst[wbase + i] = stage[i];
+        if (!last) {
+            carry = (re & 31) ? stage[(re >> 5) - wbase] : 0u;
+            __syncthreads();
+        }
+    });
+}
+
 // A chunk fits the staged packer when its 16-byte groups plus the spare
 // group the two-word ORs may touch fit the stage.
 __device__ __forceinline__ bool fits_stage(const EncodeArgs &a, uint32_t units) {
@@ -499,9 +536,16 @@ __global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const E
     const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
     const uint32_t units = (chunk_bits + 127) >> 7;
     const uint64_t dst_at = chunk_dst(a, p, units, placed);
-    // uniform over the workgroup: chunks that do not fit are packed by the
-    // row-by-row kernel that follows
-    if (dst_at == ~0ull || !fits_stage(a, units)) return;
+    // uniform over the workgroup: a chunk that does not fit is packed row by
+    // row, here or (without staged_rows) by the row packer that follows
+    if (dst_at == ~0ull) return;
+    if (!fits_stage(a, units)) {
+        if (a.staged_rows)
+            pack_rows_in_stage<ROWS, WIDE>(cc, excl, row_start, row_bits, wide, vb, p.src, units,
+                                           reinterpret_cast<uint32_t *>(stage4),
+                                           reinterpret_cast<uint32_t *>(p.out + dst_at), tid, lut32);
+        return;
+    }
 
     for (uint32_t i = tid; i < units + 1; i += kThreads) stage4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
@@ -531,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
     const ChunkPos p = chunk_pos(a, blockIdx.x);
     // after the staged packer: only the chunks it left (the staged packer
     // then placed every chunk, so place_in_pack is 0 here)
-    if (a.stage_bytes && fits_stage(a, a.sizes[blockIdx.x]) &&
+    if (a.stage_bytes && (a.staged_rows || fits_stage(a, a.sizes[blockIdx.x])) &&
         !(a.tables_unread && seg_tables<EncodeArgs>(p.seg)->max_len > (uint32_t)kNarrowMaxLen))
         return;
     uint32_t szv[kPlaceLoads];
@@ -604,6 +648,7 @@ hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t 
     const uint32_t rows_lds = (kRowSyms * a.max_len / 32 + 8) * 4;
     bool all_staged = false;
     a.stage_bytes = 0;
+    a.staged_rows = 0;
     // tables the host never read: staged packing for the chunks whose table
     // has 32-bit entries, sized for the longest such code
     const uint32_t narrow_len = a.tables_unread ? (uint32_t)kNarrowMaxLen : a.max_len;
@@ -612,7 +657,10 @@ hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t 
             // stage: the worst-case chunk plus a spare group, capped
             const uint32_t worst = ((a.chunk_symbols * narrow_len + 127) / 128 + 1) * 16;
             a.stage_bytes = worst < kStageCap ? worst : kStageCap;
-            all_staged = worst <= kStageCap && !a.tables_unread;
+            // a chunk that overflows the stage: packed row by row in it when a
+            // row of the longest narrow codes (plus carry and spare words) fits
+            a.staged_rows = (kRowSyms * narrow_len / 32 + 8) * 4 <= a.stage_bytes ? 1u : 0u;
+            all_staged = (worst <= kStageCap || a.staged_rows) && !a.tables_unread;
             if (narrow_len > 16)
                 hipLaunchKernelGGL((encode_pack_staged_kernel<ROWS, true>), dim3(n_chunks), dim3(kThreads),
                                    a.stage_bytes, s, a);
