@@ -14,6 +14,8 @@ What it computes, each part citing the passage it follows:
   (plain C in ``csrc/oracle_codec.c``, driven from Python).
 * ``stats``      histogram, PMF, average PMF, entropy and KL divergence
   (single-stage Huffman page, TL;DR, method steps 1-2, figure 3), in fp64.
+* ``bf16exp``    exponent coding of BF16 tensors: seven frequent exponents
+  in 3-bit codes, the rest escaped (ZipCCL page, methodology A-C).
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against
 closed forms, brute force, invariants or library routines.  Parity is
@@ -21,5 +23,5 @@ unpinned only for the pages' own compression figures, which come from Gemma
 tensors that are not available.
 """
 
-from . import codebooks, stats, stream  # noqa: F401
+from . import bf16exp, codebooks, stats, stream  # noqa: F401
 from ._clib import build  # noqa: F401

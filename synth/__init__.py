@@ -17,6 +17,9 @@ available here.  The recipes below stand in for them:
 * ``grad``      - Laplace(0, 0.02) scaled by 2^(6+e) per 128-element block,
                   e uniform in {-2..2}, standing in for gradients.
 
+For the BF16 exponent codec (ZipCCL page: near-Gaussian training tensors in
+BF16), ``bf16_draw`` gives N(0, sigma^2) samples as BF16 bit patterns.
+
 numpy does not promise stream stability across versions, so callers that
 record results also record ``numpy.__version__`` and a SHA-256 of the bytes.
 """
@@ -39,6 +42,9 @@ __all__ = [
     "batch_shards",
     "sha256",
     "WORKLOADS",
+    "bf16_bits",
+    "bf16_draw",
+    "BF16_WORKLOAD",
 ]
 
 E4M3_MAX = 448.0
@@ -194,3 +200,25 @@ def batch_shards(count: int = 64, shard_n: int = 1 << 22, first_seed: int = 1000
 
 def sha256(b: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(b).tobytes()).hexdigest()
+
+
+# ------------------------------------------------------------------- BF16
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp64 values -> BF16 bit patterns (uint16): to fp32 with numpy's
+    round-to-nearest-even cast, then to the upper 16 bits with round half to
+    even (finite inputs only)."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_draw(seed: int, n: int, sigma: float = 0.02) -> np.ndarray:
+    """n BF16 bit patterns of N(0, sigma^2) samples (numpy PCG64, ``seed``)."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.standard_normal(n) * sigma)
+
+
+# BF16 workload: a 64 MiB weight-like tensor (2^25 values), N(0, 0.02^2),
+# seed 5, chunks of 16384 values.
+BF16_WORKLOAD = dict(n=1 << 25, seed=5, sigma=0.02, chunk=16384)
