@@ -13,7 +13,7 @@ kernel (its average duration gives the roofline figure); the per-op
 breakdown under "kernels" comes from an untimed pass with events around
 every op, since each recorded event adds a few microseconds of queue time.
 
-Prints ONE JSON line.  Options: --workload {ffn1,tiny_qlc,ffn2,grad,batch}.
+Prints ONE JSON line.  Options: --workload {ffn1,tiny_qlc,ffn2,grad,batch,bf16}.
 """
 
 from __future__ import annotations
@@ -44,6 +44,8 @@ WORKLOAD_TEXT = {
     "grad": "gradient-like shard 2048x16384 e4m3 (32 MiB): Laplace(0,0.02)*2^(6+e) per 128 block, seed 4; "
             "calibration seeds 100-107",
     "batch": "64 shards x 4 MiB FFN1-like e4m3 (256 MiB), sigma~U(0.4,0.6), seeds 1000-1063",
+    "bf16": "BF16 exponent coding (seven frequent exponents in 3-bit codes, the rest escaped): 2^25 BF16 values "
+            "(64 MiB) of N(0, 0.02^2), seed 5, chunks of 16384 values, table from sigma",
 }
 CODECS = {
     "tiny_qlc": ["qlc"],
@@ -381,6 +383,71 @@ def run_batch(args, ec, torch):
                 roofline=None, cpu_baseline=None)
 
 
+def run_bf16(args, ec, torch):
+    """BF16 exponent coding: one step = bf16_exp_encode + bf16_exp_decode of
+    one 64 MiB tensor."""
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.BF16_WORKLOAD
+    n, chunk = w["n"], w["chunk"]
+    x = synth.bf16_draw(w["seed"], n, w["sigma"])
+    table = ec.bf16_exp_table_from_sigma(w["sigma"])
+    x_d = torch.from_numpy(x.view(np.int16)).to(dev)
+    sets = []
+    for i in range(args.sets):
+        sets.append(dict(x=x_d if i == 0 else x_d.clone(),
+                         s=torch.empty(ec.bf16_exp_max_encoded_bytes(n, chunk), dtype=torch.uint8, device=dev),
+                         y=torch.empty(n, dtype=torch.bfloat16, device=dev),
+                         n=torch.zeros(1, dtype=torch.int64, device=dev)))
+    status = torch.zeros(2, dtype=torch.int32, device=dev)
+
+    def step(S, ev=None):
+        if ev:
+            ev[0].record()
+        ec.bf16_exp_encode(table, S["x"], chunk, out=S["s"], out_len=S["n"], status=status[0:1])
+        if ev:
+            ev[1].record()
+        ec.bf16_exp_decode(S["s"], n, out=S["y"], status=status[1:2])
+        if ev:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    enc_us = statistics.mean(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+    dec_us = statistics.mean(e[1].elapsed_time(e[2]) * 1e3 for e in evs)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if status.cpu().numpy().any():
+        raise SystemExit("device status bits set: %s" % status.cpu().numpy())
+    for S in sets:
+        if not torch.equal(S["y"].view(torch.int16), S["x"]):
+            raise SystemExit("bf16 round trip mismatch")
+    L = int(sets[0]["n"].item())
+    moved = 2 * n + L
+    dom, dom_us = ("bf16_exp_decode", dec_us) if dec_us >= enc_us else ("bf16_exp_encode", enc_us)
+    kernels = {o: dict(us=round(u, 2), GBps_uncompressed=round(2 * n / u / 1e3, 1),
+                       roofline_frac=round(moved / u / 1e3 / HBM_PEAK_GBPS, 4))
+               for o, u in (("bf16_exp_encode", enc_us), ("bf16_exp_decode", dec_us))}
+    return dict(metric=METRIC, value=round(2 * n / (wall / args.steps) / 1e9, 2), unit="GB/s", n_gpus=1,
+                steps=args.steps, warmup=args.warmup, ms_per_step=round(wall / args.steps * 1e3, 4),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="u16", data="synthetic",
+                config=dict(workload=WORKLOAD_TEXT["bf16"], name="bf16", n_bytes=2 * n, chunk_values=chunk,
+                            table=list(table), step="bf16_exp_encode + bf16_exp_decode"),
+                roofline=dict(kernel=dom, bound="hbm", achieved=round(moved / dom_us / 1e3, 1), peak=HBM_PEAK_GBPS,
+                              unit="GB/s", frac=round(moved / dom_us / 1e3 / HBM_PEAK_GBPS, 4), traffic=None,
+                              algorithmic_bytes=moved, avg_us=round(dom_us, 2)),
+                kernels=kernels, compression=dict(stream_bytes=L, stream_pct=round(100 * (1 - L / (2 * n)), 3)),
+                cpu_baseline=None)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -393,7 +460,12 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     ec.lib()
-    out = run_batch(args, ec, torch) if args.workload == "batch" else run_single(args, ec, torch)
+    if args.workload == "batch":
+        out = run_batch(args, ec, torch)
+    elif args.workload == "bf16":
+        out = run_bf16(args, ec, torch)
+    else:
+        out = run_single(args, ec, torch)
     print(json.dumps(out), flush=True)
 
 

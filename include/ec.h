@@ -375,6 +375,62 @@ int pmf_average(const uint64_t *d_counts, uint32_t n_seg, float *d_pmf, hipStrea
 int pmf_kl(const uint64_t *d_p, uint32_t n_seg, const uint64_t *d_q, uint32_t q_add,
            float *d_kl_bits, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Exponent coding of BF16 tensors ("ZipCCL: Efficient Lossless Data
+ * Compression of Communication Collectives for Accelerating LLM Training",
+ * methodology A-C).  A value splits into its sign-and-mantissa byte and its
+ * 8-bit exponent; the seven exponents of a table get the 3-bit codes 1..7,
+ * any other exponent code 0 and a place in an escape array.  Stream layout
+ * (little-endian): 64-byte header (magic "EB16", version 1, n, chunk values,
+ * chunk count, the 7 table exponents, escape count, section offsets); u64
+ * esc_off[n_chunks + 1] (escapes before each chunk); zero fill to 256; n
+ * sign-mantissa bytes (sign << 7 | mantissa); zero fill to 16; three code
+ * planes (bit k of value i's code is bit i & 7 of byte i >> 3 of plane k),
+ * each zero-padded to a multiple of 16 bytes; the escaped exponents in value
+ * order.
+ * ------------------------------------------------------------------------- */
+
+/* The seven exponents with the largest counts (counts[e] for exponent e),
+ * most frequent first, equal counts to the smaller exponent.  Host memory. */
+int bf16_exp_table_from_counts(const uint64_t counts[256], uint8_t table[7]);
+
+/* The table predicted from the standard deviation alone (ZipCCL page,
+ * methodology A: near-Gaussian tensors): the seven exponents whose octaves
+ * [2^(e-127), 2^(e-126)) hold the most N(0, sigma^2) mass, largest first,
+ * equal masses to the smaller exponent.  EC_E_INVAL unless sigma > 0. */
+int bf16_exp_table_from_sigma(double sigma, uint8_t table[7]);
+
+/* Bytes that always hold the stream of n values (every exponent escaped);
+ * 0 on bad arguments.  chunk: values per chunk, a multiple of 2048 from
+ * 2048 to 2^20. */
+uint64_t bf16_exp_max_encoded_bytes(uint64_t n, uint32_t chunk);
+
+/*
+ * Encode n BF16 values (d_in: device, 16-byte aligned, bit patterns) with
+ * table[7] (seven distinct exponents, host memory) in chunks of `chunk`
+ * values into d_out (device, 16-byte aligned, out_cap bytes).  The stream
+ * length is stored in device *d_out_len.  At most 8192 chunks a stream
+ * (EC_E_UNSUPPORTED beyond).  EC_E_CAPACITY when out_cap cannot hold the
+ * sections before the escapes; when the escapes do not fit, nothing is
+ * written past out_cap, *d_out_len still gets the needed length and
+ * EC_S_CAPACITY is OR-ed into *d_status (device u32 or NULL).  Asynchronous
+ * on `stream`; uses library scratch (an escape count per chunk and a staging
+ * area of chunk bytes per chunk): two encodes in flight on one device race.
+ */
+int bf16_exp_encode(const uint8_t table[7], const uint16_t *d_in, uint64_t n, uint32_t chunk, uint8_t *d_out,
+                    uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream);
+
+/*
+ * Decode a stream of bf16_exp_encode (d_in: device, 16-byte aligned, in_len
+ * readable bytes) into n BF16 values at d_out (device, 16-byte aligned).
+ * The table and chunk size come from the stream's header.  Into *d_status:
+ * EC_S_BAD_HEADER (wrong magic or version, n differs, sections not where
+ * the layout puts them or beyond in_len) or EC_S_CORRUPT (escape index
+ * inconsistent with the code planes).  Asynchronous on `stream`.
+ */
+int bf16_exp_decode(const uint8_t *d_in, uint64_t in_len, uint16_t *d_out, uint64_t n, uint32_t *d_status,
+                    hipStream_t stream);
+
 /* Static text for an ec_error value or for a set of EC_S_* status bits. */
 const char *ec_error_string(int code);
 const char *ec_status_string(uint32_t status);

@@ -21,6 +21,8 @@ __all__ = [
     "CODEC_EXP_GOLOMB", "S_CAPACITY", "S_CORRUPT", "S_BAD_HEADER", "S_CODEBOOK_MISMATCH",
     "S_BAD_CODEBOOK", "EXPORTS", "device_codebook_bytes", "build_huffman_device", "own_max_encoded_bytes",
     "encode_batch_device", "decode_batch_device", "huffman_tables_from_streams", "qlc_optimal_area_layout",
+    "bf16_exp_table_from_counts", "bf16_exp_table_from_sigma", "bf16_exp_max_encoded_bytes", "bf16_exp_encode",
+    "bf16_exp_decode",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libec.so")
@@ -70,6 +72,11 @@ EXPORTS = {
     "byte_histogram": (_int, [_vp, _u64, _u32, _u64, _vp, _vp]),
     "pmf_average": (_int, [_vp, _u32, _vp, _vp]),
     "pmf_kl": (_int, [_vp, _u32, _vp, _u32, _vp, _vp]),
+    "bf16_exp_table_from_counts": (_int, [_u64p, _u8p]),
+    "bf16_exp_table_from_sigma": (_int, [ctypes.c_double, _u8p]),
+    "bf16_exp_max_encoded_bytes": (_u64, [_u64, _u32]),
+    "bf16_exp_encode": (_int, [_u8p, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]),
+    "bf16_exp_decode": (_int, [_vp, _u64, _vp, _u64, _vp, _vp]),
     "ec_error_string": (ctypes.c_char_p, [_int]),
     "ec_status_string": (ctypes.c_char_p, [_u32]),
 }
@@ -228,6 +235,62 @@ def huff_code_lengths(weights) -> list:
     out = (ctypes.c_uint8 * n)()
     _check(lib().huff_code_lengths(_arr(ctypes.c_uint64, weights), n, out), "huff_code_lengths")
     return list(out)
+
+
+# ----------------------------------------------------- BF16 exponent coding
+
+def _bf16_cuda(t: torch.Tensor, name: str):
+    if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2):
+        raise ECError("%s must be a contiguous CUDA tensor of 2-byte elements (BF16 bit patterns)" % name)
+
+
+def bf16_exp_table_from_counts(counts) -> tuple:
+    """The seven most frequent exponents (counts[e] for exponent e)."""
+    t = (ctypes.c_uint8 * 7)()
+    _check(lib().bf16_exp_table_from_counts(_arr(ctypes.c_uint64, counts), t), "bf16_exp_table_from_counts")
+    return tuple(int(v) for v in t)
+
+
+def bf16_exp_table_from_sigma(sigma: float) -> tuple:
+    """The seven exponents of largest N(0, sigma^2) octave mass."""
+    t = (ctypes.c_uint8 * 7)()
+    _check(lib().bf16_exp_table_from_sigma(float(sigma), t), "bf16_exp_table_from_sigma")
+    return tuple(int(v) for v in t)
+
+
+def bf16_exp_max_encoded_bytes(n: int, chunk: int = 16384) -> int:
+    return int(lib().bf16_exp_max_encoded_bytes(n, chunk))
+
+
+def bf16_exp_encode(table, x: torch.Tensor, chunk: int = 16384, out: torch.Tensor | None = None,
+                    out_len: torch.Tensor | None = None, status: torch.Tensor | None = None, stream=None):
+    """bf16_exp_encode.  Returns (out buffer, out_len int64[1], status int32[1])."""
+    _bf16_cuda(x, "x")
+    n = x.numel()
+    dev = x.device
+    if out is None:
+        out = torch.empty(bf16_exp_max_encoded_bytes(n, chunk), dtype=torch.uint8, device=dev)
+    if out_len is None:
+        out_len = torch.zeros(1, dtype=torch.int64, device=dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    _check(lib().bf16_exp_encode(_arr(ctypes.c_uint8, table), _ptr(x), n, chunk, _ptr(out), out.numel(),
+                                 _ptr(out_len), _ptr(status), _stream(stream)), "bf16_exp_encode")
+    return out, out_len, status
+
+
+def bf16_exp_decode(data: torch.Tensor, n: int, out: torch.Tensor | None = None,
+                    status: torch.Tensor | None = None, in_len: int | None = None, stream=None):
+    """bf16_exp_decode.  Returns (out bfloat16[n], status int32[1])."""
+    _u8_cuda(data, "data")
+    if out is None:
+        out = torch.empty(max(n, 8), dtype=torch.bfloat16, device=data.device)[:n]
+    _bf16_cuda(out, "out")
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=data.device)
+    _check(lib().bf16_exp_decode(_ptr(data), data.numel() if in_len is None else in_len, _ptr(out), n,
+                                 _ptr(status), _stream(stream)), "bf16_exp_decode")
+    return out, status
 
 
 def index_bytes(n: int, chunk_symbols: int, embed_lengths: bool = False) -> int:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libec.so")
 
-SOURCES = ["api.hip", "encode.hip", "decode.hip", "histogram.hip", "build.hip", "codebook.cpp"]
+SOURCES = ["api.hip", "encode.hip", "decode.hip", "histogram.hip", "build.hip", "bf16exp.hip", "codebook.cpp"]
 
 ARCH = "gfx950"
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

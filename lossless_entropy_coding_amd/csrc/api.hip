@@ -2,6 +2,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -16,10 +18,11 @@ constexpr int kMaxDevices = 16;
 
 // Scratch of one device, one buffer per use (so that an encode and a
 // histogram in flight on different streams never share one): the encoder's
-// chunk sizes and the histogram's partial counts.  Grown by doubling;
+// chunk sizes, the histogram's partial counts, and the BF16 encoder's
+// per-chunk escape counts and staged escapes.  Grown by doubling;
 // retired buffers are kept (a kernel still in flight may use them) until the
 // process ends.
-enum ScratchSlot { kScratchSizes = 0, kScratchHist = 1, kScratchSlots = 2 };
+enum ScratchSlot { kScratchSizes = 0, kScratchHist = 1, kScratchBfCounts = 2, kScratchBfEsc = 3, kScratchSlots = 4 };
 
 struct DeviceState {
     std::mutex mu;
@@ -411,3 +414,116 @@ int pmf_kl(const uint64_t *d_p, uint32_t n_seg, const uint64_t *d_q, uint32_t q_
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ BF16 exponents
+
+namespace ec {
+namespace {
+
+constexpr uint32_t kBfRow = 2048;          // values per row of the kernels
+constexpr uint32_t kBfMaxChunks = 8192;    // chunks per stream (the placement sums them per workgroup)
+
+struct BfLayout {
+    uint64_t n_chunks, sm_at, plane_at, plane_bytes, esc_at;
+};
+
+BfLayout bf_layout(uint64_t n, uint32_t chunk) {
+    BfLayout l;
+    l.n_chunks = (n + chunk - 1) / chunk;
+    const uint64_t idx_end = kHeaderBytes + 8 * (l.n_chunks + 1);
+    l.sm_at = (idx_end + 255) / 256 * 256;
+    l.plane_at = (l.sm_at + n + 15) / 16 * 16;
+    l.plane_bytes = ((n + 7) / 8 + 15) / 16 * 16;
+    l.esc_at = l.plane_at + 3 * l.plane_bytes;
+    return l;
+}
+
+bool bf_chunk_ok(uint32_t chunk) { return chunk >= kBfRow && chunk <= (1u << 20) && chunk % kBfRow == 0; }
+
+}  // namespace
+}  // namespace ec
+
+using namespace ec;
+
+int bf16_exp_table_from_counts(const uint64_t counts[256], uint8_t table[7]) {
+    if (!counts || !table) return EC_E_INVAL;
+    int order[256];
+    for (int e = 0; e < 256; ++e) order[e] = e;
+    std::stable_sort(order, order + 256, [&](int x, int y) { return counts[x] > counts[y]; });
+    for (int k = 0; k < 7; ++k) table[k] = (uint8_t)order[k];
+    return EC_OK;
+}
+
+int bf16_exp_table_from_sigma(double sigma, uint8_t table[7]) {
+    if (!table || !(sigma > 0) || !std::isfinite(sigma)) return EC_E_INVAL;
+    // Gaussian mass of the octave of exponent e: |x| in [2^(e-127), 2^(e-126)),
+    // [0, 2^-126) for e = 0
+    double mass[255];
+    const double s = sigma * std::sqrt(2.0);
+    for (int e = 0; e < 255; ++e) {
+        const double lo = e == 0 ? 0.0 : std::ldexp(1.0, e - 127), hi = std::ldexp(1.0, e - 126);
+        mass[e] = std::erf(hi / s) - std::erf(lo / s);
+    }
+    int order[255];
+    for (int e = 0; e < 255; ++e) order[e] = e;
+    std::stable_sort(order, order + 255, [&](int x, int y) { return mass[x] > mass[y]; });
+    for (int k = 0; k < 7; ++k) table[k] = (uint8_t)order[k];
+    return EC_OK;
+}
+
+uint64_t bf16_exp_max_encoded_bytes(uint64_t n, uint32_t chunk) {
+    if (!bf_chunk_ok(chunk) || n > kMaxSegSymbols) return 0;
+    return bf_layout(n, chunk).esc_at + n;
+}
+
+int bf16_exp_encode(const uint8_t table[7], const uint16_t *d_in, uint64_t n, uint32_t chunk, uint8_t *d_out,
+                    uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream) {
+    if (!table || !d_out || !d_out_len || (n && !d_in) || !bf_chunk_ok(chunk) || n > kMaxSegSymbols)
+        return EC_E_INVAL;
+    if (!aligned16(d_in) || !aligned16(d_out)) return EC_E_INVAL;
+    for (int i = 0; i < 7; ++i)
+        for (int j = 0; j < i; ++j)
+            if (table[i] == table[j]) return EC_E_INVAL;
+    const BfLayout L = bf_layout(n, chunk);
+    if (L.n_chunks > kBfMaxChunks) return EC_E_UNSUPPORTED;
+    if (out_cap < L.esc_at) return EC_E_CAPACITY;
+    BfArgs a;
+    memset(&a, 0, sizeof(a));
+    a.in = d_in;
+    a.n = n;
+    a.out = d_out;
+    a.out_cap = out_cap;
+    a.out_len = d_out_len;
+    a.status = d_status;
+    a.sm_at = L.sm_at;
+    a.plane_at = L.plane_at;
+    a.plane_bytes = L.plane_bytes;
+    a.esc_at = L.esc_at;
+    a.chunk = chunk;
+    a.n_chunks = (uint32_t)L.n_chunks;
+    for (int k = 0; k < 7; ++k) a.table[1 + k] = table[k];
+    if (L.n_chunks) {
+        void *p = nullptr;
+        int rc = device_scratch(kScratchBfCounts, L.n_chunks * 4, &p);
+        if (rc) return rc;
+        a.counts = static_cast<uint32_t *>(p);
+        rc = device_scratch(kScratchBfEsc, L.n_chunks * chunk, &p);
+        if (rc) return rc;
+        a.esc_tmp = static_cast<uint8_t *>(p);
+    }
+    return hip_rc(launch_bf16_encode(a, stream));
+}
+
+int bf16_exp_decode(const uint8_t *d_in, uint64_t in_len, uint16_t *d_out, uint64_t n, uint32_t *d_status,
+                    hipStream_t stream) {
+    if (!d_in || in_len < kHeaderBytes || (n && !d_out) || n > kMaxSegSymbols) return EC_E_INVAL;
+    if (!aligned16(d_in) || !aligned16(d_out)) return EC_E_INVAL;
+    BfDecArgs a;
+    memset(&a, 0, sizeof(a));
+    a.in = d_in;
+    a.in_len = in_len;
+    a.out = d_out;
+    a.n = n;
+    a.status = d_status;
+    return hip_rc(launch_bf16_decode(a, stream));
+}

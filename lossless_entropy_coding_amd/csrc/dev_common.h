@@ -92,6 +92,32 @@ struct DecodeArgs {
     const DevTables *tabs[EC_MAX_BATCH];
 };
 
+// BF16 exponent coding (bf16exp.hip).
+struct BfArgs {
+    const uint16_t *in;
+    uint64_t n;
+    uint8_t *out;
+    uint64_t out_cap;
+    uint64_t *out_len;
+    uint32_t *status;         // or null
+    uint32_t *counts;         // escapes per chunk (scratch)
+    uint8_t *esc_tmp;         // escapes of chunk c staged at esc_tmp + c * chunk (scratch)
+    uint64_t sm_at, plane_at, plane_bytes, esc_at;
+    uint32_t chunk, n_chunks;
+    uint8_t table[8];         // table[1..7]: the exponent of code k
+};
+
+struct BfDecArgs {
+    const uint8_t *in;
+    uint64_t in_len;
+    uint16_t *out;
+    uint64_t n;
+    uint32_t *status;         // or null
+};
+
+hipError_t launch_bf16_encode(const BfArgs &a, hipStream_t s);
+hipError_t launch_bf16_decode(const BfDecArgs &a, hipStream_t s);
+
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t max_len, hipStream_t s);
 // Partial-count rows per segment of a histogram launch (uint32 x 256 each).
