@@ -16,9 +16,9 @@
 //      earlier chunks, records esc_off[c], copies the chunk's escapes to
 //      their place; the last chunk writes the header, the first the zero
 //      fill between sections.
-// Decode (one workgroup per row of 2048 values): the row's first escape is
-// esc_off[chunk] plus the code-0 values of the chunk's earlier rows, counted
-// from the planes, so a launch does not depend on the stream's chunk size.
+// Decode (persistent workgroups, whole chunks each, row by row): a chunk's
+// escapes start at esc_off[c]; each row's code-0 values advance the
+// position, which must reach esc_off[c + 1] exactly.
 #include "dev_common.h"
 
 namespace ec {
@@ -201,66 +201,65 @@ __global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(const BfDecArgs
 #pragma unroll
     for (int k = 0; k < 7; ++k) table[1 + k] = (uint32_t)(tab >> (8 * k)) & 0xffu;
     const uint8_t *plane = a.in + plane_at;
-    const uint64_t r0 = (uint64_t)blockIdx.x * kBfRowVals;   // the row's first value
-    if (r0 >= n) return;
-    const uint32_t c = (uint32_t)(r0 / chunk);
-    const uint64_t c0 = (uint64_t)c * chunk;
-    // escapes of the chunk's earlier rows: code-0 values in their plane bytes
-    uint32_t x = 0;
-    for (uint64_t b = (c0 >> 3) + tid; b < (r0 >> 3); b += kBfThreads)
-        x += __popc(esc_mask(plane[b], plane[pb + b], plane[2 * pb + b], 8));
-    uint32_t earlier;
-    (void)block_excl_scan(x, lane, wave, wsum, &earlier);
     const uint64_t *esc_off = reinterpret_cast<const uint64_t *>(a.in + kHeaderBytes);
-    const uint64_t lo = esc_off[c], hi = esc_off[c + 1];
 
-    const uint64_t i = r0 + (uint64_t)tid * kBfPiece;
-    const uint32_t nv = i < n ? (uint32_t)min(n - i, (uint64_t)kBfPiece) : 0u;
-    uint32_t b0 = 0, b1 = 0, b2 = 0;
-    uint32_t sm_lo = 0, sm_hi = 0;
-    if (nv) {
-        b0 = plane[i >> 3];
-        b1 = plane[pb + (i >> 3)];
-        b2 = plane[2 * pb + (i >> 3)];
-        if (nv == kBfPiece) {
-            const uint2 s = *reinterpret_cast<const uint2 *>(a.in + sm_at + i);
-            sm_lo = s.x;
-            sm_hi = s.y;
-        } else {
-            for (uint32_t j = 0; j < nv; ++j) {
-                const uint32_t s = a.in[sm_at + i + j];
-                if (j < 4) sm_lo |= s << (8 * j);
-                else sm_hi |= s << (8 * (j - 4));
+    // persistent workgroups: whole chunks, row by row, carrying the escape position
+    for (uint32_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+        const uint64_t c0 = (uint64_t)c * chunk;
+        const uint32_t cn = (uint32_t)min((uint64_t)chunk, n - c0);
+        const uint32_t rows = (cn + kBfRowVals - 1) / kBfRowVals;
+        const uint64_t lo = esc_off[c], hi = esc_off[c + 1];
+        bool bad = lo > hi || hi > n_esc;   // uniform
+        uint64_t run = lo;
+        for (uint32_t r = 0; r < rows; ++r) {
+            const uint32_t ic = (r * kBfThreads + tid) * kBfPiece;   // first value of the piece in the chunk
+            const uint64_t i = c0 + ic;
+            const uint32_t nv = ic < cn ? min(cn - ic, kBfPiece) : 0u;
+            uint32_t b0 = 0, b1 = 0, b2 = 0, sm_lo = 0, sm_hi = 0;
+            if (nv) {
+                b0 = plane[i >> 3];
+                b1 = plane[pb + (i >> 3)];
+                b2 = plane[2 * pb + (i >> 3)];
+                if (nv == kBfPiece) {
+                    const uint2 sv = *reinterpret_cast<const uint2 *>(a.in + sm_at + i);
+                    sm_lo = sv.x;
+                    sm_hi = sv.y;
+                } else {
+                    for (uint32_t j = 0; j < nv; ++j) {
+                        const uint32_t sb = a.in[sm_at + i + j];
+                        if (j < 4) sm_lo |= sb << (8 * j);
+                        else sm_hi |= sb << (8 * (j - 4));
+                    }
+                }
             }
-        }
-    }
-    const uint32_t em = esc_mask(b0, b1, b2, nv);
-    uint32_t row_esc;
-    uint64_t pos = lo + earlier + block_excl_scan(__popc(em), lane, wave, wsum, &row_esc);
-    // a consistent index keeps every escape of the row inside its chunk's
-    // range; the chunk's last row must end exactly at the next chunk's start
-    const uint64_t row_end = lo + earlier + row_esc;
-    const bool last_row = r0 + kBfRowVals >= min(c0 + chunk, n);
-    bool bad = lo > hi || hi > n_esc || row_end > hi || (last_row && row_end != hi);
-    uint32_t out[kBfPiece];
+            const uint32_t em = esc_mask(b0, b1, b2, nv);
+            uint32_t row_esc;
+            uint64_t pos = run + block_excl_scan(__popc(em), lane, wave, wsum, &row_esc);
+            // a consistent index keeps the chunk's escapes inside its range
+            bad = bad || run + row_esc > hi;
+            uint32_t out[kBfPiece];
 #pragma unroll
-    for (uint32_t j = 0; j < kBfPiece; ++j) {
-        const uint32_t k = ((b0 >> j) & 1u) | (((b1 >> j) & 1u) << 1) | (((b2 >> j) & 1u) << 2);
-        uint32_t e = table[k];
-        if ((em >> j) & 1u) {
-            e = (!bad && pos < n_esc) ? (uint32_t)a.in[esc_at + pos] : 0u;
-            ++pos;
+            for (uint32_t j = 0; j < kBfPiece; ++j) {
+                const uint32_t k = ((b0 >> j) & 1u) | (((b1 >> j) & 1u) << 1) | (((b2 >> j) & 1u) << 2);
+                uint32_t e = table[k];
+                if ((em >> j) & 1u) {
+                    e = (!bad && pos < n_esc) ? (uint32_t)a.in[esc_at + pos] : 0u;
+                    ++pos;
+                }
+                const uint32_t sb = (j < 4 ? sm_lo >> (8 * j) : sm_hi >> (8 * (j - 4))) & 0xffu;
+                out[j] = ((sb & 0x80u) << 8) | (e << 7) | (sb & 0x7fu);
+            }
+            if (nv == kBfPiece) {
+                *reinterpret_cast<uint4 *>(a.out + i) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
+                                                                   out[4] | (out[5] << 16), out[6] | (out[7] << 16));
+            } else {
+                for (uint32_t j = 0; j < nv; ++j) a.out[i + j] = (uint16_t)out[j];
+            }
+            run += row_esc;
         }
-        const uint32_t s = (j < 4 ? sm_lo >> (8 * j) : sm_hi >> (8 * (j - 4))) & 0xffu;
-        out[j] = ((s & 0x80u) << 8) | (e << 7) | (s & 0x7fu);
+        // the chunk's escapes must end exactly where the next chunk's start
+        if ((bad || run != hi) && tid == 0) or_status(a.status, EC_S_CORRUPT);
     }
-    if (nv == kBfPiece) {
-        *reinterpret_cast<uint4 *>(a.out + i) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
-                                                           out[4] | (out[5] << 16), out[6] | (out[7] << 16));
-    } else {
-        for (uint32_t j = 0; j < nv; ++j) a.out[i + j] = (uint16_t)out[j];
-    }
-    if (bad && tid == 0) or_status(a.status, EC_S_CORRUPT);
 }
 
 }  // namespace
@@ -272,8 +271,11 @@ hipError_t launch_bf16_encode(const BfArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_bf16_decode(const BfDecArgs &a, hipStream_t s) {
+    // the chunk size is in the stream: at most one workgroup per 2048-value
+    // row (no more than there can be chunks), and persistent beyond 2048
     const uint64_t rows = (a.n + kBfRowVals - 1) / kBfRowVals;
-    hipLaunchKernelGGL(bf16_decode_kernel, dim3(rows ? (uint32_t)rows : 1u), dim3(kBfThreads), 0, s, a);
+    const uint32_t grid = rows == 0 ? 1u : (uint32_t)min(rows, (uint64_t)2048);
+    hipLaunchKernelGGL(bf16_decode_kernel, dim3(grid), dim3(kBfThreads), 0, s, a);
     return hipGetLastError();
 }
 
