@@ -425,6 +425,11 @@ def run_bf16(args, ec, torch):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_ref:   # plain copies of the input, for the hardware-counter scale factor
+        dst = torch.empty_like(x_d)
+        for _ in range(5):
+            dst.copy_(sets[-1]["x"])
+        torch.cuda.synchronize()
     if status.cpu().numpy().any():
         raise SystemExit("device status bits set: %s" % status.cpu().numpy())
     for S in sets:
