@@ -57,7 +57,6 @@ constexpr uint32_t guard_rows() {
 // every 8 codes, so reads stay inside the allocation (rows past a lane's data
 // hold other data or guard rows) and the end check flags the stream.
 struct ColBits {
-    static constexpr bool kStaged = true;
     uint32_t Y;      // see above
     uint32_t col;    // 4 * lane
     uint32_t base;   // Y of the lane's bit 0
@@ -83,7 +82,6 @@ struct ColBits {
 // do not fit in LDS): a 64-bit MSB-aligned buffer refilled 32 bits at a time,
 // loads clamped to the payload.
 struct GlobalBits {
-    static constexpr bool kStaged = false;
     const uint32_t *base;   // lane's first payload word
     uint32_t last;          // last readable word, relative to base
     uint64_t buf;           // next stream bits, MSB-aligned
