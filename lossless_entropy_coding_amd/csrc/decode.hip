@@ -11,6 +11,10 @@
 // has the lanes read at scattered addresses: about twice the LDS time in bank
 // conflicts).  One window serves four codes.  (A global load inside the
 // decode loop would stall on the output stores too: one counter tracks both.)
+// QLC and EG stage the whole sub-chunk at once.  Huffman stages it in two
+// halves of a shorter column (the blocks still unread move down at the
+// half-run point), so that twelve waves per CU fit the LDS instead of eight:
+// its loop mostly waits on LDS reads, and more waves in flight hide them.
 // A sub-chunk too long for the region (data that barely compresses) is
 // decoded straight from global memory.
 //   QLC      the 3-bit prefix gives the code length through a funnel shift
@@ -32,8 +36,13 @@ namespace ec {
 
 namespace {
 
-constexpr int kThreads = 512;                        // one workgroup per CU shares one copy of the tables
-constexpr int kWaves = kThreads / 64;
+// Waves of the one workgroup per CU (which shares one copy of the tables):
+// three per SIMD for Huffman codes (its decode loop fits 168 VGPRs and
+// waits mostly on LDS), else two.
+template <int CODEC>
+constexpr int waves_for() {
+    return CODEC == EC_CODEC_HUFFMAN ? 12 : 8;
+}
 constexpr uint32_t kLdsBytes = 160 * 1024;
 constexpr uint32_t kRowBytes = 64 * 4;               // one word per lane
 // Rows past the last region that a lane may read: a position is clamped to
@@ -157,10 +166,11 @@ __device__ __noinline__ void flag(uint32_t *status, uint32_t bits) { or_status(s
 
 // Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
 // run) from source S into dst; returns the bits of the QLC / EG "not a
-// codeword" flags (bit 8 and up).  FULL > 0: a whole run from an LDS column
-// (the common case), in code with a fixed number of stores, so that the
-// compiler can count the memory operations in flight across it.
-template <int CODEC, int PAIRS, int FULL, class Src>
+// codeword" flags (bit 8 and up).  FULL > 0: half HALF (symbols
+// 128 * HALF ..; 2: both halves) of a whole run from an LDS column (the
+// common case), in code with a fixed number of stores, so that the compiler
+// can count the memory operations in flight across it.
+template <int CODEC, int PAIRS, int FULL, class Src, int HALF = 0>
 __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *dst, const uint16_t *l1,
                                                const uint8_t *symtab, const DeepTables *dt, uint32_t max_len,
                                                uint32_t lens, uint32_t k_eg) {
@@ -304,7 +314,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
         // counter) and leave as one whole 128-byte line per lane: 16-byte
         // stores to 64 lanes' separate lines leave partial lines in L2 that
         // get written back several times.
-        static_for<0, 2>([&](auto hf) __attribute__((always_inline)) {
+        static_for<(HALF == 2 ? 0 : HALF), (HALF == 2 ? 2 : HALF + 1)>([&](auto hf) __attribute__((always_inline)) {
             constexpr int half = decltype(hf)::value;
             uint32_t o[32];
 #pragma nounroll
@@ -333,7 +343,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
         // 128 decoded bytes are collected in registers and written as one
         // whole cache line: 16-byte stores to 64 lanes' separate lines leave
         // partial lines in L2 that get written back more than once
-        static_for<0, 2>([&](auto hf) __attribute__((always_inline)) {
+        static_for<(HALF == 2 ? 0 : HALF), (HALF == 2 ? 2 : HALF + 1)>([&](auto hf) __attribute__((always_inline)) {
             constexpr int half = decltype(hf)::value;
             uint32_t o[32];
             static_for<0, 16>([&](auto hc) __attribute__((always_inline)) {
@@ -366,14 +376,12 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
 }
 
 // A lane's sub-chunk: its bits [sb, eb) in the payload and its symbols,
-// the 16-byte payload blocks that hold them, and the wave's largest block
-// count.
+// and the 16-byte payload blocks that hold them.
 struct LaneTask {
     uint64_t sb, eb;
     uint64_t first_sym;
     uint64_t blk0;      // first block
     uint32_t nv;        // blocks (0: nothing to decode)
-    uint32_t nv_max;    // over the wave
     uint32_t cnt;       // symbols (0: no sub-chunk)
     bool ok;            // index entries valid
 };
@@ -420,28 +428,25 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
     const bool live = t.ok && t.cnt > 0 && t.eb > t.sb;
     t.blk0 = live ? t.sb >> 7 : 0;
     t.nv = live ? (uint32_t)(((t.eb - 1) >> 7) - t.blk0 + 1) : 0u;
-    uint32_t m = t.nv;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d, 64));
-    t.nv_max = m;
     return t;
 }
 
-// The first K blocks of a lane's sub-chunk, loaded into registers (indexes
-// clamped to the lane's last block, or to the payload's first block for
-// lanes with nothing to decode, so every load stays inside the payload).
-template <int K>
+// Blocks FIRST .. FIRST + K - 1 of a lane's sub-chunk, loaded into
+// registers (indexes clamped to the lane's last block, or to the payload's
+// first block for lanes with nothing to decode, so every load stays inside
+// the payload).
+template <int K, int FIRST = 0>
 __device__ __forceinline__ void issue_blocks(const StreamInfo &si, const LaneTask &t, uint4 (&v)[K]) {
     const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + t.blk0;
     const uint32_t last = t.nv ? t.nv - 1 : 0u;
     static_for<0, K>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
-        v[k] = src[min((uint32_t)k, last)];
+        v[k] = src[min((uint32_t)(FIRST + k), last)];
     });
 }
 
 // Blocks first .. nv_max - 1 of the lanes' sub-chunks (those not
-// prefetched) into their LDS columns; a rare path, behind a call.
+// prefetched) into their LDS columns, behind a call (whole-run staging).
 __device__ __noinline__ void stage_rest(uint32_t col_word0, const uint4 *src, uint32_t nv, uint32_t first,
                                         uint32_t nv_max) {
     typedef __attribute__((address_space(3))) uint32_t lds_u32;
@@ -464,28 +469,17 @@ __device__ __noinline__ void stage_rest(uint32_t col_word0, const uint4 *src, ui
     }
 }
 
-// Everything but a whole staged run, behind a call: a segment's last,
-// shorter run; runs of a wave whose longest sub-chunk does not fit its LDS
-// region (read straight from global memory); sub-chunks without bits.
+// Everything but a whole run decoded from the lane's column, behind a call,
+// read straight from global memory: a segment's last, shorter run; runs
+// whose halves do not fit the column's stages (data that barely compresses);
+// sub-chunks without bits.
 template <int CODEC, int PAIRS>
-__device__ __noinline__ void decode_rest(const LaneTask &L, bool fits, uint32_t region, uint32_t ylim, uint32_t lane,
-                                         const uint32_t *payload, uint64_t pb, uint8_t *dst, const uint16_t *l1,
-                                         const uint8_t *symtab, const DeepTables *dt, uint32_t max_len, uint32_t lens,
-                                         uint32_t k_eg, uint32_t *status) {
+__device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payload, uint64_t pb, uint8_t *dst,
+                                         const uint16_t *l1, const uint8_t *symtab, const DeepTables *dt,
+                                         uint32_t max_len, uint32_t lens, uint32_t k_eg, uint32_t *status) {
     uint32_t bad = 0;
     uint64_t end_pos = 1, want_pos = 0;
-    if (L.nv == 0) {
-        // symbols but no bits: corrupt
-    } else if (fits) {
-        ColBits S;
-        S.col = 4 * lane;
-        S.base = region / 8 + 31;
-        S.Y = S.base + (uint32_t)(L.sb - L.blk0 * 128);
-        S.ylim = ylim;
-        bad = decode_run<CODEC, PAIRS, 0>(S, L.cnt, dst, l1, symtab, dt, max_len, lens, k_eg);
-        end_pos = S.bit();
-        want_pos = L.eb - L.blk0 * 128;
-    } else {
+    if (L.nv > 0) {   // (symbols but no bits: corrupt)
         GlobalBits S;
         S.init(payload, pb >> 2, L.sb);
         bad = decode_run<CODEC, PAIRS, 0>(S, L.cnt, dst, l1, symtab, dt, max_len, lens, k_eg);
@@ -496,9 +490,19 @@ __device__ __noinline__ void decode_rest(const LaneTask &L, bool fits, uint32_t 
 }
 
 // Persistent workgroups: workgroup b takes tasks b, b + G, ... (G = grid);
-// a task is 512 consecutive sub-chunks of one stream, 64 per wave.
+// a task is 64 consecutive sub-chunks of one stream per wave.
+//
+// A lane's column holds kStage blocks at a time, in two stages.  Stage 1
+// is the sub-chunk's first kStage blocks (prefetched in registers while the
+// wave decoded its previous task); the blocks after them are loaded into
+// registers meanwhile.  At the half-run point (128 symbols) the blocks not
+// yet consumed move down to the column's first slots and the loaded ones
+// follow them (stage 2).  A lane whose first half reads past stage 1, or
+// whose rest does not fit stage 2, decodes its run again from global memory.
 template <int CODEC, int PAIRS>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const DecodeArgs a) {
+    constexpr uint32_t kWaves = waves_for<CODEC>();
+    constexpr uint32_t kThreads = 64 * kWaves;
     constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
                                    : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
                                                                : 1;
@@ -513,6 +517,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     // the rest of the CU's LDS: one region of kRows rows per wave, then guard rows
     constexpr uint32_t kHeadBytes = (sizeof(Head) + kRowBytes - 1) / kRowBytes * kRowBytes;
     constexpr uint32_t kRows = (kLdsBytes - kHeadBytes - kGuardRows * kRowBytes) / (kWaves * kRowBytes);
+    // Huffman: two stages of kStage blocks; other codecs: the whole run
+    // staged at once (up to kRows rows), kStage blocks of it prefetched
+    constexpr bool kTwo = CODEC == EC_CODEC_HUFFMAN;
+    constexpr int kStage = kTwo ? (int)((kRows - 1) / 4 < 16 ? (kRows - 1) / 4 : 16) : 16;
+    static_assert(kStage >= 8 && (kTwo || 1 + 4 * kStage <= kRows), "column stages too short");
     struct Smem {
         Head h;
         alignas(256) uint32_t cols[kWaves][kRows * 64];
@@ -526,14 +535,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     const uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads > 0 ? (a.blocks_per_seg + kThreads - 1) / kThreads
                                                                            : 1u;
     const uint32_t n_tasks = gx * a.n_seg;
+    // One stream: the last, partial round of tasks (every task, when the
+    // grid is larger than the task count) is spread over every workgroup
+    // wave by wave (wave w of workgroup b takes the round's (w * G + b)-th
+    // run of 64 sub-chunks), so that its waves sit on the SIMDs of all CUs
+    // instead of filling a few CUs.
+    const uint32_t tail_at = n_tasks / gridDim.x * gridDim.x;   // first task of a partial round
+    const bool spread = a.n_seg == 1 && tail_at != n_tasks;
+    const uint32_t n_iter = spread ? tail_at + gridDim.x : n_tasks;
+    auto seg_of = [&](uint32_t tt) __attribute__((always_inline)) { return spread ? 0u : tt / gx; };
+    // the wave's first sub-chunk in task tt
+    auto first_sub = [&](uint32_t tt) __attribute__((always_inline)) -> uint32_t {
+        if (spread && tt >= tail_at) return tail_at * kThreads + (wave * gridDim.x + blockIdx.x) * 64;
+        return (tt - tt / gx * gx) * kThreads + wave * 64;
+    };
     typedef __attribute__((address_space(3))) uint32_t lds_u32;
     const uint32_t region = (uint32_t)(size_t)(lds_u32 *)sm.cols[wave];   // 256-byte aligned
     lds_u32 *my_col = (lds_u32 *)(size_t)(region + 4 * lane);
 
-    // Blocks of the next task that a lane loads into registers while it
-    // decodes the current one (a whole sub-chunk at 16384-symbol chunks of
-    // codes averaging under 8 bits).
-    constexpr int kPre = 16;
     uint32_t cur_seg = ~0u;
     StreamInfo si = {};
     const DevTables *tab = nullptr;
@@ -544,12 +563,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
     bool have_cur = false, have_next_raw = false, have_first = false, seg_ok = false;
     LaneTask cur = {};
     IndexRaw next_raw = {}, first_raw = {};
-    uint4 pre[kPre];
+    // blocks in flight: during a first half this task's blocks kStage ..,
+    // during a second half the next task's first kStage blocks
+    uint4 pre[kStage];
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) pre[k] = make_uint4(0u, 0u, 0u, 0u);
+    for (int k = 0; k < kStage; ++k) pre[k] = make_uint4(0u, 0u, 0u, 0u);
 
-    for (uint32_t t = blockIdx.x; t < n_tasks; t += gridDim.x) {
-        const uint32_t seg = t / gx, bx = t - seg * gx;
+    for (uint32_t t = blockIdx.x; t < n_iter; t += gridDim.x) {
+        const uint32_t seg = seg_of(t);
         if (seg != cur_seg) {
             __syncthreads();   // the previous segment's tables are no longer read
             tab = seg_tables<DecodeArgs>(seg);
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                 if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
                     bits = EC_S_BAD_HEADER;
             }
-            if (bits && bx == 0 && tid == 0) flag(status, bits);
+            if (bits && t == seg * gx && tid == 0) flag(status, bits);   // once, by the segment's first task
             seg_ok = bits == 0;
             cur_seg = seg;
             si.stream = stream;
@@ -595,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
             si.nch = nch;
             si.spc = C / kSub;
             have_cur = have_next_raw = false;
-            const uint32_t g0f = bx * kThreads + wave * 64;
+            const uint32_t g0f = first_sub(t);
             have_first = seg_ok && g0f < a.blocks_per_seg;
             if (have_first) first_raw = issue_index(a, si, g0f + lane);
 #pragma unroll
@@ -617,31 +638,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
         }
         if (!seg_ok) continue;   // uniform over the workgroup
 
-        const uint32_t g0 = bx * kThreads + wave * 64;   // the wave's first sub-chunk
+        const uint32_t g0 = first_sub(t);   // the wave's first sub-chunk
         // the wave's next task, if it is in the same stream
         const uint32_t t1 = t + gridDim.x;
-        const bool next_same = t1 < n_tasks && t1 / gx == seg;
-        const uint32_t g0n = (t1 - seg * gx) * kThreads + wave * 64;
+        const bool next_same = t1 < n_iter && seg_of(t1) == seg;
+        const uint32_t g0n = first_sub(t1);
         const bool next_busy = next_same && g0n < a.blocks_per_seg;
         if (g0 >= a.blocks_per_seg) {   // uniform over the wave
             have_cur = have_next_raw = false;
             continue;
         }
-        if (!have_cur) {   // nothing prefetched: this task's index and blocks now
+        if (!have_cur) {   // nothing prefetched: this task's index and first blocks now
             cur = resolve(a, si, have_first ? first_raw : issue_index(a, si, g0 + lane), g0 + lane, status);
-            issue_blocks<kPre>(si, cur, pre);
+            issue_blocks<kStage>(si, cur, pre);
         }
         have_first = false;
         if (next_busy && !have_next_raw) next_raw = issue_index(a, si, g0n + lane);
         const LaneTask L = cur;
         const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
+        // a whole run decoded from the lane's column: for two stages of at
+        // most kStage blocks each; else when the wave's longest sub-chunk fits
+        uint32_t nv_max = 0;
+        if constexpr (!kTwo) {
+            nv_max = L.nv;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) nv_max = max(nv_max, (uint32_t)__shfl_xor((int)nv_max, d, 64));
+        }
+        const bool fits = kTwo || 1 + 4 * nv_max <= kRows;   // uniform over the wave
+        bool full = live && fits && L.cnt == kSub && L.nv > 0 && (!kTwo || L.nv <= (uint32_t)(2 * kStage));
 
-        // stage the lane's blocks in its column if the wave's longest
-        // sub-chunk fits the region: the prefetched ones from registers, any
-        // further ones loaded now
-        const bool fits = 1 + 4 * L.nv_max <= kRows;
+        // stage 1 (two stages: the first kStage blocks), from registers
         if (fits) {
-            static_for<0, kPre>([&](auto kc) __attribute__((always_inline)) {
+            static_for<0, kStage>([&](auto kc) __attribute__((always_inline)) {
                 constexpr int k = decltype(kc)::value;
                 if ((uint32_t)k < L.nv) {
                     lds_u32 *w = my_col + (1 + 4 * k) * 64;   // rows 1 + 4 k ...
@@ -651,47 +679,99 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
                     w[192] = pre[k].w;
                 }
             });
-            if (L.nv_max > (uint32_t)kPre)
+            if (!kTwo && nv_max > (uint32_t)kStage)
                 stage_rest(region + kRowBytes + 4 * lane, reinterpret_cast<const uint4 *>(si.stream + si.po) + L.blk0,
-                           L.nv, kPre, L.nv_max);
-            // each lane reads only its own column: program order suffices
-            asm volatile("" ::: "memory");
+                           L.nv, kStage, nv_max);
         }
-
-        // prefetch: the next task's blocks, and the index entries of the one after
-        if (next_busy) {
-            cur = resolve(a, si, next_raw, g0n + lane, status);
-            issue_blocks<kPre>(si, cur, pre);
-            have_cur = true;
-            const uint32_t t2 = t1 + gridDim.x;
-            const uint32_t g0nn = (t2 - seg * gx) * kThreads + wave * 64;
-            have_next_raw = t2 < n_tasks && t2 / gx == seg && g0nn < a.blocks_per_seg;
-            if (have_next_raw) next_raw = issue_index(a, si, g0nn + lane);
+        // each lane reads only its own column: program order suffices
+        asm volatile("" ::: "memory");
+        auto prefetch_next = [&]() __attribute__((always_inline)) {
+            // the next task's first blocks, and the index entries of the one after
+            if (next_busy) {
+                cur = resolve(a, si, next_raw, g0n + lane, status);
+                issue_blocks<kStage>(si, cur, pre);
+                have_cur = true;
+                const uint32_t t2 = t1 + gridDim.x;
+                const uint32_t g0nn = first_sub(t2);
+                have_next_raw = t2 < n_iter && seg_of(t2) == seg && g0nn < a.blocks_per_seg;
+                if (have_next_raw) next_raw = issue_index(a, si, g0nn + lane);
+            } else {
+                have_cur = have_next_raw = false;
+            }
+        };
+        if constexpr (kTwo) {
+            // the blocks after stage 1, in flight during the first half
+            if (__ballot(full && L.nv > (uint32_t)kStage)) issue_blocks<kStage, kStage>(si, L, pre);
         } else {
-            have_cur = have_next_raw = false;
+            prefetch_next();
         }
 
         uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + L.first_sym;
         const uint32_t ylim = region / 8 + kRows * 32 - 1;
-        const bool full = live && fits && L.cnt == kSub && L.nv > 0;
+        constexpr int kFull = CODEC == EC_CODEC_QLC ? 1 : 2;
+        const uint32_t want = (uint32_t)(L.eb - L.blk0 * 128);
+        ColBits S;
+        S.col = 4 * lane;
+        S.base = region / 8 + 31;
+        S.Y = S.base + (uint32_t)(L.sb - L.blk0 * 128);
+        S.ylim = ylim;
+        uint32_t bad = 0;
+        if (full)
+            bad = decode_run<CODEC, PAIRS, kFull, ColBits, kTwo ? 0 : 2>(S, kSub, dst, l1, symtab, sm.h.deep,
+                                                                        seg_max_len, seg_lens, seg_k_eg);
+
+        uint32_t bh = 0;
+        if constexpr (kTwo) {
+            // stage 2: blocks bh .. nv - 1, where bh holds the first bit not
+            // yet consumed.  The first half was read from stage 1 when no bit
+            // before the position lay past it.
+            const uint32_t pos = S.bit();
+            bh = pos >> 7;
+            full = full && pos <= (uint32_t)kStage * 128 && bh < L.nv && L.nv - bh <= (uint32_t)kStage;
+            if (full) {
+                // blocks bh .. kStage - 1 move down to slots 0 .. (slot j is
+                // read before any later write lands on it: bh + j >= j)
+                const uint32_t keep = min(L.nv, (uint32_t)kStage) - bh;   // bh <= kStage (pos bound)
+#pragma nounroll
+                for (uint32_t j = 0; j < keep; ++j) {
+                    const lds_u32 *r = my_col + (1 + 4 * (bh + j)) * 64;
+                    const uint32_t x0 = r[0], x1 = r[64], x2 = r[128], x3 = r[192];
+                    lds_u32 *w = my_col + (1 + 4 * j) * 64;
+                    w[0] = x0;
+                    w[64] = x1;
+                    w[128] = x2;
+                    w[192] = x3;
+                }
+                // block kStage + k goes to slot keep + k (at most kStage - 1)
+                static_for<0, kStage>([&](auto kc) __attribute__((always_inline)) {
+                    constexpr int k = decltype(kc)::value;
+                    if ((uint32_t)(kStage + k) < L.nv) {
+                        lds_u32 *w = my_col + (1 + 4 * (keep + k)) * 64;
+                        w[0] = pre[k].x;
+                        w[64] = pre[k].y;
+                        w[128] = pre[k].z;
+                        w[192] = pre[k].w;
+                    }
+                });
+                S.Y -= bh * 128;
+            } else {
+                bh = 0;
+            }
+            asm volatile("" ::: "memory");
+            prefetch_next();
+        }
+
         bool corrupt = false;
-        if (full) {   // the common case: a whole run from the lane's column
-            const uint32_t p0 = (uint32_t)(L.sb - L.blk0 * 128), want = (uint32_t)(L.eb - L.blk0 * 128);
-            ColBits S;
-            S.col = 4 * lane;
-            S.base = region / 8 + 31;
-            S.Y = S.base + p0;
-            S.ylim = ylim;
-            constexpr int kFull = CODEC == EC_CODEC_QLC ? 1 : 2;
-            const uint32_t bad = decode_run<CODEC, PAIRS, kFull>(S, kSub, dst, l1, symtab, sm.h.deep, seg_max_len,
-                                                                 seg_lens, seg_k_eg);
-            corrupt = (bad & ~0xffu) || S.bit() != want;
+        if (full) {
+            if constexpr (kTwo)
+                bad |= decode_run<CODEC, PAIRS, kFull, ColBits, 1>(S, kSub, dst, l1, symtab, sm.h.deep, seg_max_len,
+                                                                   seg_lens, seg_k_eg);
+            corrupt = (bad & ~0xffu) || S.bit() + bh * 128 != want;
         }
         if (__ballot(live && !full))
             if (live && !full)
-                decode_rest<CODEC, PAIRS>(L, fits, region, ylim, lane, reinterpret_cast<const uint32_t *>(si.stream + si.po),
-                                          si.pb, dst, l1, symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg,
-                                          status);
+                decode_rest<CODEC, PAIRS>(L, reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb, dst, l1,
+                                          symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg, status);
         if (corrupt) flag(status, EC_S_CORRUPT);
         // the column is rewritten at the next task, after this lane's reads
         asm volatile("" ::: "memory");
@@ -701,11 +781,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs a) {
 // Workgroups of a persistent launch: as many as can be resident at once,
 // never more than there are tasks.
 template <class K>
-hipError_t decode_grid(K kernel, uint32_t n_tasks, uint32_t *grid) {
+hipError_t decode_grid(K kernel, uint32_t threads, uint32_t n_tasks, uint32_t *grid) {
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
     if (e != hipSuccess) return e;
     const uint64_t g = (uint64_t)(per_cu > 0 ? per_cu : 1) * (uint64_t)(cus > 0 ? cus : 1);
     *grid = g < n_tasks ? (uint32_t)g : n_tasks;
@@ -714,10 +794,15 @@ hipError_t decode_grid(K kernel, uint32_t n_tasks, uint32_t *grid) {
 
 template <int CODEC, int PAIRS>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
+    constexpr uint32_t kThreads = 64 * waves_for<CODEC>();
     uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads;
     if (gx == 0) gx = 1;   // still validate the header
+    // one stream: up to one workgroup per run of 64 sub-chunks, its waves
+    // spread over the workgroups; else up to one per task
+    const uint32_t runs = (a.blocks_per_seg + 63) / 64;
+    const uint32_t cap = a.n_seg == 1 ? (runs > gx ? runs : gx) : gx * a.n_seg;
     uint32_t grid = 0;
-    const hipError_t e = decode_grid(decode_kernel<CODEC, PAIRS>, gx * a.n_seg, &grid);
+    const hipError_t e = decode_grid(decode_kernel<CODEC, PAIRS>, kThreads, cap, &grid);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_kernel<CODEC, PAIRS>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
