@@ -215,6 +215,37 @@ def test_chunks_of_mixed_code_length(ec, C, depth):
     assert dstatus == 0 and np.array_equal(y, x)
 
 
+@pytest.mark.parametrize("C", [4096, 16384])
+def test_huffman_sub_chunks_that_leave_the_column_stages(ec, C):
+    """Sub-chunks of different code-length profiles side by side, so that one
+    wave holds lanes decoded from their LDS column in two stages and lanes
+    that decode again from global memory: a first half too long for the
+    first stage, a second half too long for the second, both halves long
+    enough that the second stage takes blocks from registers, and short
+    ones."""
+    counts = [int(c) for c in deep_counts(20)]
+    cb, ocb = ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
+    length = np.array(ocb.length)
+    by_len = {int(l): int(np.flatnonzero(length == l)[0]) for l in (3, 9, 12)}
+    s3, s9, s12 = by_len[3], by_len[9], by_len[12]
+    rng = np.random.default_rng(C)
+    kinds = [
+        np.full(256, s3),                                        # short
+        np.concatenate([np.full(128, s12), np.full(128, s3)]),   # first half past stage 1
+        np.concatenate([np.full(128, s3), np.full(128, s12)]),   # rest past stage 2
+        np.full(256, s9),                                        # both stages full
+        rng.integers(0, 256, 256),                               # mixed
+    ]
+    pick = rng.integers(0, len(kinds), 3 * C // 256 + 5)
+    x = np.concatenate([kinds[k] for k in pick] + [np.full(77, s12)]).astype(np.uint8)
+    print("case huffman stages", C, x.size, flush=True)
+    want = st.encode_stream(x, ocb, C)
+    got, status = _gpu_encode(ec, cb, x, C)
+    assert status == 0 and got == want
+    y, dstatus = _gpu_decode(ec, cb, want, x.size)
+    assert dstatus == 0 and np.array_equal(y, x)
+
+
 def test_encode_is_deterministic(ec):
     counts = _calib_counts()
     cb, _ = _pair(ec, "huffman", counts)
