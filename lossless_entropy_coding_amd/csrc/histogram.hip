@@ -3,12 +3,12 @@
 // Histogram, two launches:
 //   1. histogram_kernel: the workgroups of a segment sweep it together in
 //      rounds of 32 KiB per workgroup, counting into LDS counters; each then
-//      stores its 256 partial counts with plain stores.  The workgroup's
-//      counters form 64 columns of 256, one column per lane index: lane l of
-//      every wave adds into column l, so the counter of byte b is word
-//      64 b + l and the lanes of one LDS atomic always hit different banks and
-//      addresses, whatever bytes they hold (fewer columns let lanes that hold
-//      bytes of the skewed e4m3 distributions collide on a bank or a word);
+//      stores its 256 partial counts with plain stores.  Every wave owns 16 columns of 256 counters; lane l adds
+//      into column l & 15, so the counter of byte b is word 16 b + (l & 15):
+//      whatever bytes the 32 lanes of one LDS pass hold, at most two of them
+//      share a bank (random addresses into one shared table, and the skewed
+//      e4m3 distributions where a few bytes dominate, cost several times
+//      more);
 //   2. histogram_reduce_kernel: sums the partial rows of each segment into
 //      the 64-bit counts, one wave per bin.
 // No global atomics: same-address atomics from many workgroups serialise at
@@ -20,8 +20,8 @@ namespace ec {
 namespace {
 
 constexpr int kHistThreads = 256;
-constexpr int kHistCols = 64;                          // counter columns (one per lane index)
-constexpr int kHistWords = 256 * kHistCols;            // 64 KiB of counters per workgroup
+constexpr int kHistCols = 16;                          // counter columns per wave (lane & 15)
+constexpr int kHistWaveWords = 256 * kHistCols;        // 16 KiB of counters per wave
 constexpr int kHistRoundVec = 8;                       // 16-byte loads in flight per thread per round
 constexpr uint64_t kHistRound = (uint64_t)kHistRoundVec * kHistThreads;   // vectors per workgroup round
 constexpr int kHistRoundsPerBlock = 4;                 // target rounds per workgroup (128 KiB)
@@ -29,13 +29,14 @@ constexpr int kHistRoundsPerBlock = 4;                 // target rounds per work
 __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
                                                                  uint64_t seg_n, uint64_t in_stride,
                                                                  uint32_t *__restrict__ partial) {
-    __shared__ uint4 hv[kHistWords / 4];
+    constexpr int kWaves = kHistThreads / 64;
+    __shared__ uint4 hv[kWaves * kHistWaveWords / 4];
     uint32_t *h = reinterpret_cast<uint32_t *>(hv);
-    const uint32_t tid = threadIdx.x, lane = tid & 63;
-    for (uint32_t i = tid; i < kHistWords / 4; i += kHistThreads) hv[i] = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (uint32_t i = tid; i < kWaves * kHistWaveWords / 4; i += kHistThreads) hv[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    // a word takes the bytes of one lane index of the workgroup's waves: far below 2^32
-    uint32_t *mine = h + lane;
+    // a word takes the bytes of 4 lanes of one workgroup: far below 2^32
+    uint32_t *mine = h + wave * kHistWaveWords + (lane & (kHistCols - 1));
 
     const uint32_t seg = blockIdx.y;
     const uint8_t *base = in + (uint64_t)seg * in_stride;
@@ -57,42 +58,41 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
         }
     };
     // grid-stride rounds: at any time the workgroups of a segment read one
-    // contiguous window of it.  The next round's loads are issued before the
-    // current round is counted, so every wave keeps a round in flight; load
-    // indexes are clamped to the last vector rather than predicated, so that
-    // the compiler counts the loads in flight exactly and each count waits
-    // for its own round only.
-    auto load = [&](uint64_t rr, uint4 (&d)[kHistRoundVec]) __attribute__((always_inline)) {
+    // contiguous window of it; every load of a round is issued before its
+    // first count, and each count waits for its own load only
+    for (uint64_t r0 = (uint64_t)blockIdx.x * kHistRound; r0 < n_vec; r0 += (uint64_t)gridDim.x * kHistRound) {
+        const uint64_t v = r0 + tid;
+        uint4 q[kHistRoundVec];
+        if (r0 + kHistRound <= n_vec) {
 #pragma unroll
-        for (int k = 0; k < kHistRoundVec; ++k) {
-            const uint64_t i = rr + tid + (uint64_t)k * kHistThreads;
-            d[k] = vp[i < n_vec ? i : n_vec - 1];
+            for (int k = 0; k < kHistRoundVec; ++k) q[k] = vp[v + k * kHistThreads];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) count(q[k]);
+        } else {   // the segment's last, partial round
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) {
+                if (v + k * kHistThreads < n_vec) q[k] = vp[v + k * kHistThreads];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < kHistRoundVec; ++k) {
+                if (v + k * kHistThreads < n_vec) count(q[k]);
+            }
         }
-    };
-    const uint64_t stride = (uint64_t)gridDim.x * kHistRound;
-    uint64_t r0 = (uint64_t)blockIdx.x * kHistRound;
-    uint4 q[kHistRoundVec];
-    if (r0 < n_vec) load(r0, q);   // (n_vec > 0 wherever a load is issued)
-    for (; r0 < n_vec; r0 += stride) {   // uniform over the workgroup
-        uint4 qn[kHistRoundVec];
-        load(r0 + stride, qn);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < kHistRoundVec; ++k) {
-            if (r0 + tid + (uint64_t)k * kHistThreads < n_vec) count(q[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < kHistRoundVec; ++k) q[k] = qn[k];
     }
     if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid] * kHistCols], 1u);
     if (blockIdx.x == 0 && tid < tail) atomicAdd(&mine[vbase[n_vec * 16 + tid] * kHistCols], 1u);
     __syncthreads();
 
-    // thread t sums byte t over all columns, starting at column t & 63 so
+    // thread t sums byte t over all columns, starting at column t & 15 so
     // that the lanes of one access spread over the banks
     uint32_t sum = 0;
 #pragma unroll
-    for (int j = 0; j < kHistCols; ++j) sum += h[tid * kHistCols + ((j + tid) & (kHistCols - 1))];
+    for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+        for (int j = 0; j < kHistCols; ++j) sum += h[w * kHistWaveWords + tid * kHistCols + ((j + tid) & (kHistCols - 1))];
+    }
     partial[((uint64_t)seg * 256 + tid) * gridDim.x + blockIdx.x] = sum;   // bin-major rows
 }
 
