@@ -447,7 +447,8 @@ def run_bf16(args, ec, torch):
                 config=dict(workload=WORKLOAD_TEXT["bf16"], name="bf16", n_bytes=2 * n, chunk_values=chunk,
                             table=list(table), step="bf16_exp_encode + bf16_exp_decode"),
                 roofline=dict(kernel=dom, bound="hbm", achieved=round(moved / dom_us / 1e3, 1), peak=HBM_PEAK_GBPS,
-                              unit="GB/s", frac=round(moved / dom_us / 1e3 / HBM_PEAK_GBPS, 4), traffic=None,
+                              unit="GB/s", frac=round(moved / dom_us / 1e3 / HBM_PEAK_GBPS, 4),
+                              traffic=load_traffic("bf16exp.hip", "bf16", dom),
                               algorithmic_bytes=moved, avg_us=round(dom_us, 2)),
                 kernels=kernels, compression=dict(stream_bytes=L, stream_pct=round(100 * (1 - L / (2 * n)), 3)),
                 cpu_baseline=None)
