@@ -11,14 +11,16 @@
 //   1. bf16_encode_kernel (one workgroup per chunk): loads 8 values per
 //      thread and 16-byte load, writes their sign-mantissa bytes (one 8-byte
 //      store) and one byte of each plane, and stages the chunk's escaped
-//      exponents, in value order, in scratch; records the chunk's count.
+//      exponents, in value order, in scratch (each row's gathered in LDS
+//      first, then stored contiguously); records the chunk's count.
 //   2. bf16_place_kernel (one workgroup per chunk): sums the counts of the
 //      earlier chunks, records esc_off[c], copies the chunk's escapes to
 //      their place; the last chunk writes the header, the first the zero
 //      fill between sections.
 // Decode (persistent workgroups, whole chunks each, row by row): a chunk's
 // escapes start at esc_off[c]; each row's code-0 values advance the
-// position, which must reach esc_off[c + 1] exactly.
+// position, which must reach esc_off[c + 1] exactly.  A row's escapes are
+// loaded into LDS with contiguous loads, then taken in value order.
 #include "dev_common.h"
 
 namespace ec {
@@ -65,8 +67,9 @@ __device__ __forceinline__ void load_piece(const uint16_t *src, uint32_t nv, uin
     }
 }
 
-__global__ __launch_bounds__(kBfThreads) void bf16_encode_kernel(const BfArgs a) {
+__global__ __launch_bounds__(kBfThreads, 8) void bf16_encode_kernel(const BfArgs a) {
     __shared__ uint8_t code_of[256];
+    __shared__ uint8_t esc_row[kBfRowVals];   // one row's escapes (reused after the next row's scan barriers)
     __shared__ uint32_t wsum[kBfThreads / 64];
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t cd = 0;
@@ -112,12 +115,18 @@ __global__ __launch_bounds__(kBfThreads) void bf16_encode_kernel(const BfArgs a)
             plane[a.plane_bytes + (i >> 3)] = (uint8_t)p1;
             plane[2 * a.plane_bytes + (i >> 3)] = (uint8_t)p2;
         }
+        // the row's escapes, in value order: each thread's into LDS at its
+        // scanned place, then the row's bytes to scratch with contiguous
+        // stores (a byte store per escaped value would issue up to eight
+        // divergent stores per row)
         uint32_t row_total;
-        uint32_t pos = chunk_esc + block_excl_scan(__popc(escm), lane, wave, wsum, &row_total);
+        uint32_t pos = block_excl_scan(__popc(escm), lane, wave, wsum, &row_total);
 #pragma unroll
         for (uint32_t j = 0; j < kBfPiece; ++j) {
-            if (escm & (1u << j)) esc_tmp[pos++] = (uint8_t)e[j];
+            if (escm & (1u << j)) esc_row[pos++] = (uint8_t)e[j];
         }
+        __syncthreads();
+        for (uint32_t k = tid; k < row_total; k += kBfThreads) esc_tmp[chunk_esc + k] = esc_row[k];
         chunk_esc += row_total;
     }
     if (tid == 0) a.counts[c] = chunk_esc;
@@ -175,8 +184,9 @@ __device__ __forceinline__ uint32_t esc_mask(uint32_t b0, uint32_t b1, uint32_t 
     return ~(b0 | b1 | b2) & ((1u << nv) - 1u);
 }
 
-__global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(const BfDecArgs a) {
+__global__ __launch_bounds__(kBfThreads, 8) void bf16_decode_kernel(const BfDecArgs a) {
     __shared__ uint32_t wsum[kBfThreads / 64];
+    __shared__ uint8_t esc_row[kBfRowVals];   // one row's escapes (reused after the next row's scan barriers)
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // the header, read and checked by every thread (uniform)
     const uint64_t *h = reinterpret_cast<const uint64_t *>(a.in);
@@ -234,18 +244,20 @@ __global__ __launch_bounds__(kBfThreads) void bf16_decode_kernel(const BfDecArgs
             }
             const uint32_t em = esc_mask(b0, b1, b2, nv);
             uint32_t row_esc;
-            uint64_t pos = run + block_excl_scan(__popc(em), lane, wave, wsum, &row_esc);
+            uint32_t pos = block_excl_scan(__popc(em), lane, wave, wsum, &row_esc);
             // a consistent index keeps the chunk's escapes inside its range
             bad = bad || run + row_esc > hi;
+            // the row's escapes (at most one per value) into LDS with
+            // contiguous loads, instead of a byte load per escaped value
+            for (uint32_t k = tid; k < row_esc; k += kBfThreads)
+                esc_row[k] = (!bad && run + k < n_esc) ? a.in[esc_at + run + k] : (uint8_t)0;
+            __syncthreads();
             uint32_t out[kBfPiece];
 #pragma unroll
             for (uint32_t j = 0; j < kBfPiece; ++j) {
                 const uint32_t k = ((b0 >> j) & 1u) | (((b1 >> j) & 1u) << 1) | (((b2 >> j) & 1u) << 2);
                 uint32_t e = table[k];
-                if ((em >> j) & 1u) {
-                    e = (!bad && pos < n_esc) ? (uint32_t)a.in[esc_at + pos] : 0u;
-                    ++pos;
-                }
+                if ((em >> j) & 1u) e = esc_row[pos++];
                 const uint32_t sb = (j < 4 ? sm_lo >> (8 * j) : sm_hi >> (8 * (j - 4))) & 0xffu;
                 out[j] = ((sb & 0x80u) << 8) | (e << 7) | (sb & 0x7fu);
             }
