@@ -28,8 +28,9 @@ namespace ec {
 namespace {
 
 constexpr int kBfThreads = 256;
-constexpr uint32_t kBfPiece = 8;                          // values per thread and row (one 16-byte load)
-constexpr uint32_t kBfRowVals = kBfThreads * kBfPiece;    // 2048
+constexpr uint32_t kBfPiece = 16;                         // values per thread and row (two 16-byte loads)
+constexpr uint32_t kBfRowVals = kBfThreads * kBfPiece;    // 4096
+constexpr uint32_t kBfChunkUnit = 2048;                   // a chunk holds a multiple of this many values
 constexpr uint32_t kBfMagic = 0x36314245u;                // "EB16"
 constexpr uint32_t kBfVersion = 1;
 
@@ -51,13 +52,13 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t lane, u
     return before + incl - x;
 }
 
-// The 8 values of a piece (count nv <= 8; the others read as 0).
+// The 16 values of a piece (count nv <= 16; the others read as 0).
 __device__ __forceinline__ void load_piece(const uint16_t *src, uint32_t nv, uint32_t (&v)[kBfPiece]) {
     if (nv == kBfPiece) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(src);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        const uint4 q0 = reinterpret_cast<const uint4 *>(src)[0], q1 = reinterpret_cast<const uint4 *>(src)[1];
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
             v[2 * k] = w[k] & 0xffffu;
             v[2 * k + 1] = w[k] >> 16;
         }
@@ -92,13 +93,12 @@ __global__ __launch_bounds__(kBfThreads, 8) void bf16_encode_kernel(const BfArgs
         uint32_t v[kBfPiece];
         load_piece(a.in + c0 + i, nv, v);
         uint32_t e[kBfPiece];
-        uint32_t sm_lo = 0, sm_hi = 0, p0 = 0, p1 = 0, p2 = 0, escm = 0;
+        uint32_t smw[kBfPiece / 4] = {0, 0, 0, 0}, p0 = 0, p1 = 0, p2 = 0, escm = 0;
 #pragma unroll
         for (uint32_t j = 0; j < kBfPiece; ++j) {
             e[j] = (v[j] >> 7) & 0xffu;
             const uint32_t s = ((v[j] >> 8) & 0x80u) | (v[j] & 0x7fu);
-            if (j < 4) sm_lo |= s << (8 * j);
-            else sm_hi |= s << (8 * (j - 4));
+            smw[j / 4] |= s << (8 * (j % 4));
             const uint32_t k = j < nv ? (uint32_t)code_of[e[j]] : 0u;
             p0 |= (k & 1u) << j;
             p1 |= ((k >> 1) & 1u) << j;
@@ -106,18 +106,24 @@ __global__ __launch_bounds__(kBfThreads, 8) void bf16_encode_kernel(const BfArgs
             escm |= (j < nv && k == 0u) ? 1u << j : 0u;
         }
         if (nv == kBfPiece) {
-            *reinterpret_cast<uint2 *>(sm_out + i) = make_uint2(sm_lo, sm_hi);
+            *reinterpret_cast<uint4 *>(sm_out + i) = make_uint4(smw[0], smw[1], smw[2], smw[3]);
         } else {
-            for (uint32_t j = 0; j < nv; ++j) sm_out[i + j] = (uint8_t)((j < 4 ? sm_lo >> (8 * j) : sm_hi >> (8 * (j - 4))));
+            for (uint32_t j = 0; j < nv; ++j) sm_out[i + j] = (uint8_t)(smw[j / 4] >> (8 * (j % 4)));
         }
-        if (nv) {
+        // plane bytes: two for a piece with values past its first eight (a
+        // 2-byte aligned pair: i is a multiple of 16), else one
+        if (nv > 8) {
+            *reinterpret_cast<uint16_t *>(plane + (i >> 3)) = (uint16_t)p0;
+            *reinterpret_cast<uint16_t *>(plane + a.plane_bytes + (i >> 3)) = (uint16_t)p1;
+            *reinterpret_cast<uint16_t *>(plane + 2 * a.plane_bytes + (i >> 3)) = (uint16_t)p2;
+        } else if (nv) {
             plane[i >> 3] = (uint8_t)p0;
             plane[a.plane_bytes + (i >> 3)] = (uint8_t)p1;
             plane[2 * a.plane_bytes + (i >> 3)] = (uint8_t)p2;
         }
         // the row's escapes, in value order: each thread's into LDS at its
         // scanned place, then the row's bytes to scratch with contiguous
-        // stores (a byte store per escaped value would issue up to eight
+        // stores (a byte store per escaped value would issue up to sixteen
         // divergent stores per row)
         uint32_t row_total;
         uint32_t pos = block_excl_scan(__popc(escm), lane, wave, wsum, &row_total);
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(kBfThreads, 8) void bf16_decode_kernel(const BfDecA
                    esc_at = h[7];
     const uint32_t chunk = (uint32_t)h2, n_chunks = (uint32_t)(h2 >> 32);
     bool ok = (uint32_t)h0 == kBfMagic && (h0 >> 32) == kBfVersion && n == a.n && chunk > 0 &&
-              chunk % kBfRowVals == 0 && (uint64_t)n_chunks == (n + chunk - 1) / chunk && n_esc <= n;
+              chunk % kBfChunkUnit == 0 && (uint64_t)n_chunks == (n + chunk - 1) / chunk && n_esc <= n;
     if (ok) {   // the sections where the layout puts them
         const uint64_t idx_end = kHeaderBytes + 8ull * (n_chunks + 1);
         const uint64_t e_sm = (idx_end + 255) / 256 * 256, e_pl = (e_sm + n + 15) / 16 * 16;
@@ -225,22 +231,26 @@ __global__ __launch_bounds__(kBfThreads, 8) void bf16_decode_kernel(const BfDecA
             const uint32_t ic = (r * kBfThreads + tid) * kBfPiece;   // first value of the piece in the chunk
             const uint64_t i = c0 + ic;
             const uint32_t nv = ic < cn ? min(cn - ic, kBfPiece) : 0u;
-            uint32_t b0 = 0, b1 = 0, b2 = 0, sm_lo = 0, sm_hi = 0;
-            if (nv) {
+            // plane bits: two bytes (2-byte aligned: i is a multiple of 16)
+            // for a piece with values past its first eight, else one
+            uint32_t b0 = 0, b1 = 0, b2 = 0, smw[kBfPiece / 4] = {0, 0, 0, 0};
+            if (nv > 8) {
+                b0 = *reinterpret_cast<const uint16_t *>(plane + (i >> 3));
+                b1 = *reinterpret_cast<const uint16_t *>(plane + pb + (i >> 3));
+                b2 = *reinterpret_cast<const uint16_t *>(plane + 2 * pb + (i >> 3));
+            } else if (nv) {
                 b0 = plane[i >> 3];
                 b1 = plane[pb + (i >> 3)];
                 b2 = plane[2 * pb + (i >> 3)];
-                if (nv == kBfPiece) {
-                    const uint2 sv = *reinterpret_cast<const uint2 *>(a.in + sm_at + i);
-                    sm_lo = sv.x;
-                    sm_hi = sv.y;
-                } else {
-                    for (uint32_t j = 0; j < nv; ++j) {
-                        const uint32_t sb = a.in[sm_at + i + j];
-                        if (j < 4) sm_lo |= sb << (8 * j);
-                        else sm_hi |= sb << (8 * (j - 4));
-                    }
-                }
+            }
+            if (nv == kBfPiece) {
+                const uint4 sv = *reinterpret_cast<const uint4 *>(a.in + sm_at + i);
+                smw[0] = sv.x;
+                smw[1] = sv.y;
+                smw[2] = sv.z;
+                smw[3] = sv.w;
+            } else {
+                for (uint32_t j = 0; j < nv; ++j) smw[j / 4] |= (uint32_t)a.in[sm_at + i + j] << (8 * (j % 4));
             }
             const uint32_t em = esc_mask(b0, b1, b2, nv);
             uint32_t row_esc;
@@ -258,12 +268,15 @@ __global__ __launch_bounds__(kBfThreads, 8) void bf16_decode_kernel(const BfDecA
                 const uint32_t k = ((b0 >> j) & 1u) | (((b1 >> j) & 1u) << 1) | (((b2 >> j) & 1u) << 2);
                 uint32_t e = table[k];
                 if ((em >> j) & 1u) e = esc_row[pos++];
-                const uint32_t sb = (j < 4 ? sm_lo >> (8 * j) : sm_hi >> (8 * (j - 4))) & 0xffu;
+                const uint32_t sb = (smw[j / 4] >> (8 * (j % 4))) & 0xffu;
                 out[j] = ((sb & 0x80u) << 8) | (e << 7) | (sb & 0x7fu);
             }
             if (nv == kBfPiece) {
-                *reinterpret_cast<uint4 *>(a.out + i) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
-                                                                   out[4] | (out[5] << 16), out[6] | (out[7] << 16));
+                uint4 *o = reinterpret_cast<uint4 *>(a.out + i);
+                o[0] = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16), out[4] | (out[5] << 16),
+                                  out[6] | (out[7] << 16));
+                o[1] = make_uint4(out[8] | (out[9] << 16), out[10] | (out[11] << 16), out[12] | (out[13] << 16),
+                                  out[14] | (out[15] << 16));
             } else {
                 for (uint32_t j = 0; j < nv; ++j) a.out[i + j] = (uint16_t)out[j];
             }
