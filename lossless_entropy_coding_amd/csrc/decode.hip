@@ -164,6 +164,19 @@ __device__ __noinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt
 // flight exactly instead of waiting for every store.
 __device__ __noinline__ void flag(uint32_t *status, uint32_t bits) { or_status(status, bits); }
 
+// Whether any bit of the payload in [from, to) is set: the zero padding
+// between a chunk's last code and its end (to is a multiple of 32, since
+// chunks start at 16-byte offsets).  Behind a call, like every rare path.
+__device__ __noinline__ bool padding_set(const uint32_t *payload, uint64_t from, uint64_t to) {
+    uint32_t any = 0;
+    for (uint64_t w = from >> 5; w < (to >> 5); ++w) {
+        uint32_t x = payload[w];
+        if (w == (from >> 5)) x &= 0xffffffffu >> (from & 31);   // bits at and after `from` (MSB first)
+        any |= x;
+    }
+    return any != 0;
+}
+
 // Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
 // run) from source S into dst; returns the bits of the QLC / EG "not a
 // codeword" flags (bit 8 and up).  FULL > 0: half HALF (symbols
@@ -379,6 +392,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
 // and the 16-byte payload blocks that hold them.
 struct LaneTask {
     uint64_t sb, eb;
+    uint64_t pad_end;   // the chunk's end bit when this is its last sub-chunk, else 0
     uint64_t first_sym;
     uint64_t blk0;      // first block
     uint32_t nv;        // blocks (0: nothing to decode)
@@ -391,6 +405,7 @@ struct LaneTask {
 struct IndexRaw {
     uint64_t co0, co1;        // the lane's chunk: byte offsets of its start and end in the payload
     uint32_t e_start, e_end;  // the lane's sub-chunk: start and end bit in its chunk
+    bool last;                // the sub-chunk is its chunk's last: the padding after it is checked
 };
 
 // Stream fields the tasks of a segment share (validated once per segment).
@@ -410,6 +425,7 @@ __device__ __forceinline__ IndexRaw issue_index(const DecodeArgs &a, const Strea
     r.co1 = chunk_off[c + 1];
     r.e_end = sub_end[(uint64_t)c * si.spc + j];
     r.e_start = j ? sub_end[(uint64_t)c * si.spc + j - 1] : 0u;
+    r.last = j == si.spc - 1 || gl == a.blocks_per_seg - 1;
     return r;
 }
 
@@ -423,6 +439,7 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
     if (active && !t.ok) flag(status, EC_S_CORRUPT);
     t.sb = r.co0 * 8 + r.e_start;
     t.eb = r.co0 * 8 + r.e_end;
+    t.pad_end = r.last ? r.co1 * 8 : 0;
     t.first_sym = (uint64_t)g * kSub;
     t.cnt = !active ? 0u : (a.seg_n - t.first_sym < kSub ? (uint32_t)(a.seg_n - t.first_sym) : (uint32_t)kSub);
     const bool live = t.ok && t.cnt > 0 && t.eb > t.sb;
@@ -486,7 +503,9 @@ __device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payl
         end_pos = S.bit();
         want_pos = L.eb;
     }
-    if ((bad & ~0xffu) || end_pos != want_pos) or_status(status, EC_S_CORRUPT);
+    bool pad = false;
+    if (end_pos == want_pos && L.pad_end > L.eb) pad = padding_set(payload, L.eb, L.pad_end);
+    if ((bad & ~0xffu) || end_pos != want_pos || pad) or_status(status, EC_S_CORRUPT);
 }
 
 // Persistent workgroups: workgroup b takes tasks b, b + G, ... (G = grid);
@@ -768,6 +787,10 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
                                                                    seg_lens, seg_k_eg);
             corrupt = (bad & ~0xffu) || S.bit() + bh * 128 != want;
         }
+        // the zero padding after a chunk's last sub-chunk
+        const bool pad_check = full && !corrupt && L.pad_end > L.eb;
+        if (__ballot(pad_check))
+            if (pad_check) corrupt = padding_set(reinterpret_cast<const uint32_t *>(si.stream + si.po), L.eb, L.pad_end);
         if (__ballot(live && !full))
             if (live && !full)
                 decode_rest<CODEC, PAIRS>(L, reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb, dst, l1,

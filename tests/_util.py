@@ -41,3 +41,29 @@ def parse_table(b: bytes) -> dict:
         sym=list(np.frombuffer(b, np.uint8, 256, T_SYM)),
         codebook_id=int(np.frombuffer(b, np.uint64, 1, T_ID)[0]),
         codec=int(codec), max_len=int(max_len))
+
+
+def padding_flips(stream: bytes):
+    """Copies of a stream with one padding bit set: the first and the last
+    padding bit of the first chunk that has padding and of the last chunk.
+    Reads only the container's index (header offsets 16-24, chunk_off[],
+    sub_end[]); bit p of the payload is bit 31 - p % 32 of 32-bit LE word
+    p // 32."""
+    n = int(np.frombuffer(stream, "<u8", 1, 8)[0])
+    C, n_chunks = (int(v) for v in np.frombuffer(stream, "<u4", 2, 16))
+    po = int(np.frombuffer(stream, "<u8", 1, 24)[0])
+    spc = C // 256
+    chunk_off = np.frombuffer(stream, "<u8", n_chunks + 1, 64).astype(np.int64)
+    sub_end = np.frombuffer(stream, "<u4", n_chunks * spc, 64 + 8 * (n_chunks + 1)).astype(np.int64)
+    assert n > 0
+    out = []
+    padded = [c for c in range(n_chunks) if chunk_off[c] * 8 + sub_end[c * spc + spc - 1] < chunk_off[c + 1] * 8]
+    for c in sorted({padded[0], padded[-1]} if padded else set()):
+        start = int(chunk_off[c] * 8 + sub_end[c * spc + spc - 1])
+        for p in (start, int(chunk_off[c + 1] * 8) - 1):
+            word, b = divmod(p, 32)
+            bitw = 31 - b
+            t = bytearray(stream)
+            t[po + word * 4 + bitw // 8] ^= 1 << (bitw % 8)
+            out.append(((c, p), bytes(t)))
+    return out

@@ -5,9 +5,9 @@ decode told the whole buffer length, chunks of the workload's size.
 Every stream is compared byte for byte with the oracle's (the oracle's C
 encoder finishes a 64 MiB shard in a few seconds); the decoded bytes must
 equal the input and the histograms must equal the oracle's.  The 256 MiB
-multi-shard batch checks every shard's histogram and round trip and a
-sample of 8 shards' streams against the oracle, for the fixed codebook and
-for per-shard codebooks built on the host and on the GPU.
+multi-shard batch checks every shard's histogram, round trip and stream
+against the oracle, for the fixed codebook and for per-shard codebooks built
+on the host and on the GPU.
 """
 
 import functools
@@ -139,7 +139,8 @@ def test_full_size_batch_matches_oracle(ec, mode):
     assert not status.cpu().numpy().any()
     assert torch.equal(y, x_d)
     L = lens.cpu().numpy()
-    for i in range(0, S, 9):
+    got = out.cpu().numpy()
+    for i in range(S):   # every shard's stream
         want = st.encode_stream(x[i], cbm.huffman_codebook(rows[i]), C, embed_lengths=per_shard)
         assert int(L[i]) == len(want), i
-        assert out[i, : int(L[i])].cpu().numpy().tobytes() == want, i
+        assert got[i, : int(L[i])].tobytes() == want, i

@@ -12,7 +12,7 @@ from oracle import codebooks as cbm
 from oracle import stats
 from oracle import stream as st
 
-from _util import deep_counts
+from _util import deep_counts, padding_flips
 
 pytestmark = pytest.mark.gpu
 
@@ -295,6 +295,21 @@ def test_pmf_average_and_kl_match_oracle(ec):
     assert abs(float(kl0.item())) <= 1e-7       # D(P || P) = 0
 
 
+def test_kl_with_counts_beyond_2_to_31_matches_oracle(ec):
+    # row totals past 2^31 take the kernel's double-precision ratio branch
+    rng = np.random.default_rng(9)
+    q = rng.integers(1 << 30, 1 << 34, 256).astype(np.int64)
+    # (deviations of 2^18 and more: at smaller ones the fp64 oracle's own
+    # rounding, about 1e-17 bits, nears 1e-5 of the divergence)
+    rows = [q + rng.integers(-(1 << d), 1 << d, 256) for d in (18, 22, 28)]
+    p_t = torch.from_numpy(np.stack(rows)).to(DEV)
+    kl = ec.pmf_kl(p_t, torch.from_numpy(q).to(DEV), q_add=0).cpu().numpy().astype(np.float64)
+    for i, r in enumerate(rows):
+        assert r.sum() >= 1 << 31
+        want = stats.kl_bits(r, q)
+        assert want > 0 and abs(kl[i] - want) <= 1e-5 * want, (i, kl[i], want)
+
+
 def test_kl_closed_forms(ec):
     p = np.zeros(256, np.int64)
     q = np.zeros(256, np.int64)
@@ -434,6 +449,25 @@ def test_corruption_and_header_errors_are_reported(ec):
         _, status = ec.decode(cb, d, x.size - 1)
         torch.cuda.synchronize()
         assert int(status.item()) & ec.S_BAD_HEADER
+
+
+@pytest.mark.parametrize("n,C", [(100_000, 4096), (70_001, 16384)])
+def test_a_set_padding_bit_is_corrupt(ec, n, C):
+    # the oracle rejects any set bit between a chunk's last code and its end
+    counts = _calib_counts()
+    x = synth.draw("ffn1", 13, n)
+    for name in ("qlc", "huffman", "eg"):
+        cb, ocb = _pair(ec, name, counts)
+        s = st.encode_stream(x, ocb, C)
+        flips = padding_flips(s)
+        assert len(flips) >= 2
+        for where, t in flips:
+            with pytest.raises(st.CorruptStream):
+                st.decode_stream(t, ocb)
+            y, status = _gpu_decode(ec, cb, t, n)
+            assert status & ec.S_CORRUPT, (name, where)
+        y, status = _gpu_decode(ec, cb, s, n)
+        assert status == 0 and np.array_equal(y, x)
 
 
 def test_qlc_unused_suffix_is_corrupt(ec):

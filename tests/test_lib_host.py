@@ -143,6 +143,13 @@ def test_exp_golomb_codebook_matches_oracle(ec, seed, k):
     assert info["codebook_id"] == ora.codebook_id
 
 
+def test_exp_golomb_best_order_closed_forms(ec):
+    # the hand-summed cases pinned for the oracle (ties to the smaller order)
+    from test_oracle_codes import EG_CLOSED_FORM
+    for counts, k in EG_CLOSED_FORM:
+        assert ec.Codebook.exp_golomb(counts, -1).info()["eg_k"] == k
+
+
 def test_index_and_max_sizes(ec):
     from oracle import stream as st
     for n, C in [(0, 4096), (1, 256), (1 << 20, 4096), (1 << 26, 16384), (12345, 1024)]:

@@ -263,6 +263,37 @@ def test_exp_golomb_best_order_is_argmin():
         assert _is_prefix_free(cb.code, cb.length)
 
 
+# Closed-form cases for the best Exp-Golomb order, summed by hand from the
+# codeword lengths 2m - k + 1 (m = floor(log2(rank + 2^k))):
+#  - 256 equal counts: k = 8 gives 256 x 9 bits; k = 7 gives 128 x 8 + 128 x 10;
+#    k = 6 gives 64 x 7 + 128 x 9 + 64 x 11; all 2304, while k = 5 gives
+#    32 x 6 + 64 x 8 + 128 x 10 + 32 x 12 = 2368 and k = 4 gives 2496: the
+#    three-way tie goes to the smallest order, 6;
+#  - one symbol only: its rank-0 codeword has k + 1 bits, so k = 0;
+#  - counts 2^(10 - r) on ranks 0..10 (geometric): k = 0 costs
+#    1024 + 3 x 768 + 5 x 240 + 7 x 15 = 4633, k = 1 costs
+#    2 x 1536 + 4 x 480 + 6 x 31 = 5178, k = 2 costs 3 x 1920 + 5 x 127 = 6395;
+#  - equal counts on ranks 0..15: k = 2, 3, 4 all cost 80 per count (k = 1
+#    costs 84, k = 5 costs 96): the tie goes to 2;
+#  - equal counts on ranks 0..7: k = 1, 2, 3 cost 32 (k = 0 costs 34): 1;
+#  - weight 3 on ranks 0..3 and 1 on ranks 4..11: k = 0, 1, 2, 3, 4 cost
+#    86, 80, 76, 88, 100: 2, strictly.
+EG_CLOSED_FORM = [
+    ([5] * 256, 6),
+    ([0] * 77 + [1000] + [0] * 178, 0),
+    ([2 ** (10 - r) for r in range(11)] + [0] * 245, 0),
+    ([1] * 16 + [0] * 240, 2),
+    ([1] * 8 + [0] * 248, 1),
+    ([3] * 4 + [1] * 8 + [0] * 244, 2),
+]
+
+
+@pytest.mark.parametrize("counts,k", EG_CLOSED_FORM)
+def test_exp_golomb_best_order_closed_forms(counts, k):
+    assert cbm.eg_best_order(counts) == k
+    assert cbm.eg_codebook(counts).k == k
+
+
 def test_codebook_ids_differ_and_are_stable():
     counts = _random_counts(30)
     a = cbm.qlc_codebook(counts)

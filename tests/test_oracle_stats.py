@@ -101,6 +101,23 @@ def test_kl_exact_rational_inputs_high_precision():
         assert stats.kl_bits(p, q, q_add=1) == pytest.approx(float(want), rel=1e-12)
 
 
+def test_kl_exact_with_counts_beyond_2_to_31():
+    # totals past 2^31 (the device kernel takes another branch there)
+    mpmath.mp.dps = 60
+    rng = np.random.default_rng(8)
+    for trial in range(3):
+        q = [int(v) for v in rng.integers(1 << 30, 1 << 34, 256)]
+        p = [int(v + rng.integers(-(1 << 20), 1 << 20)) for v in q]
+        Np, Nq = sum(p), sum(q)
+        assert Np >= 1 << 31 and Nq >= 1 << 31
+        want = mpmath.mpf(0)
+        for s in range(256):
+            want += mpmath.mpf(p[s]) / Np * mpmath.log((mpmath.mpf(p[s]) * Nq) / (mpmath.mpf(q[s]) * Np), 2)
+        assert want > 0
+        # (fp64 rounding of the plain sum limits the agreement at such small divergences)
+        assert stats.kl_bits(p, q) == pytest.approx(float(want), rel=1e-7)
+
+
 def test_kl_infinite_when_q_has_a_hole():
     p = [1] * 256
     q = [1] * 256

@@ -15,7 +15,7 @@ from oracle import codebooks as cbm
 from oracle import stats
 from oracle import stream as st
 
-from _util import deep_counts
+from _util import deep_counts, padding_flips
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -157,6 +157,21 @@ def test_corruption_is_detected_or_changes_the_output():
             except st.CorruptStream:
                 continue
             assert not (y == x).all()
+
+
+def test_a_set_padding_bit_is_corrupt():
+    # the container fixes the bits after a chunk's last code as zero
+    x = synth.draw("normal", 3, 20000)
+    counts = stats.histogram(synth.draw("normal", 1, 1 << 16))
+    for name in ("qlc", "huffman", "eg"):
+        cb = _codebooks(counts)[name]
+        s = st.encode_stream(x, cb, 4096)
+        assert (st.decode_stream(s, cb) == x).all()
+        flips = padding_flips(s)
+        assert len(flips) >= 2
+        for _, t in flips:
+            with pytest.raises(st.CorruptStream):
+                st.decode_stream(t, cb)
 
 
 def test_header_checks():
