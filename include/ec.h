@@ -22,12 +22,16 @@
  *     function and released with ec_codebook_free.  Its device tables are
  *     allocated on the current device at its first GPU use and freed with
  *     the handle.
- *   - The library keeps two scratch buffers per device, allocated at first
- *     use, grown by doubling and kept until the process ends: the encoder's
- *     chunk sizes (4 bytes per chunk of a launch) and the histogram's
- *     partial counts (1 KiB per partial row).  GPU calls of the same kind
- *     that overlap in time on one device (different streams) share one and
- *     race: order them (one stream, or events).
+ *   - The library keeps four scratch buffers per device, allocated with
+ *     hipMalloc on first use, grown by doubling and kept until the process
+ *     ends: the encoder's chunk sizes (4 bytes per chunk of a launch), the
+ *     histogram's partial counts (1 KiB per partial row), and the BF16
+ *     encoder's escape counts and staged escapes.  An allocation or growth
+ *     inside an asynchronous entry point synchronises the device implicitly
+ *     and cannot happen under stream capture: entropy_encode_noalloc takes
+ *     none.  GPU calls of the same kind that overlap in time on one device
+ *     (different streams) share one buffer and race: order them (one stream,
+ *     or events).
  *   - Device codebook tables (the *_device functions) live in caller-owned
  *     device memory: n_seg consecutive tables of ec_device_codebook_bytes()
  *     bytes each, 16-byte aligned.
@@ -224,6 +228,24 @@ uint64_t entropy_max_encoded_bytes(const ec_codebook *cb, uint64_t n, uint32_t c
 int entropy_encode(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols,
                    uint8_t *d_out, uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status,
                    hipStream_t stream);
+
+/*
+ * entropy_encode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, same stream, but no allocation of any kind.
+ *   - The codebook's device tables must already be on the current device:
+ *     any earlier GPU call with this codebook on this device (for example
+ *     one entropy_encode) puts them there.  EC_E_INVAL otherwise.
+ *   - The per-chunk sizes go to a fixed library array on each device, of
+ *     65536 entries: at most 65536 chunks a call (ceil(n / chunk_symbols)),
+ *     EC_E_UNSUPPORTED beyond.  The array keeps the last call's contents;
+ *     nothing in it needs clearing (each call writes every entry it reads).
+ *   - Every call on one device shares that array: two of these calls that
+ *     overlap in time on one device (different streams) race.  Order them.
+ */
+int entropy_encode_noalloc(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols,
+                           uint8_t *d_out, uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status,
+                           hipStream_t stream);
 
 /*
  * Decode a stream made by entropy_encode with the same codebook (QLC page,

@@ -15,7 +15,7 @@ import os
 import torch  # loaded first: libec binds to the HIP runtime torch already mapped
 
 __all__ = [
-    "Codebook", "ECError", "lib", "encode", "decode", "encode_batch", "decode_batch",
+    "Codebook", "ECError", "lib", "encode", "encode_noalloc", "decode", "encode_batch", "decode_batch",
     "byte_histogram", "pmf_average", "pmf_kl", "huff_code_lengths", "index_bytes",
     "max_encoded_bytes", "QLC_BASE", "QLC_ADAPTED", "CODEC_QLC", "CODEC_HUFFMAN",
     "CODEC_EXP_GOLOMB", "S_CAPACITY", "S_CORRUPT", "S_BAD_HEADER", "S_CODEBOOK_MISMATCH",
@@ -58,6 +58,7 @@ EXPORTS = {
     "entropy_index_bytes": (_u64, [_u64, _u32, _u32]),
     "entropy_max_encoded_bytes": (_u64, [_vp, _u64, _u32, _u32]),
     "entropy_encode": (_int, [_vp, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]),
+    "entropy_encode_noalloc": (_int, [_vp, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]),
     "entropy_decode": (_int, [_vp, _vp, _u64, _vp, _u64, _vp, _vp]),
     "entropy_encode_batch": (_int, [ctypes.POINTER(_vp), _u32, _vp, _u64, _u64, _u32, _u32, _vp, _u64, _vp,
                                     _vp, _vp]),
@@ -316,6 +317,17 @@ def encode(cb: Codebook, x: torch.Tensor, chunk_symbols: int, out: torch.Tensor 
         status = torch.zeros(1, dtype=torch.int32, device=dev)
     _check(lib().entropy_encode(cb.handle, _ptr(x), n, chunk_symbols, _ptr(out), out.numel(), _ptr(out_len),
                                 _ptr(status), _stream(stream)), "entropy_encode")
+    return out, out_len, status
+
+
+def encode_noalloc(cb: Codebook, x: torch.Tensor, chunk_symbols: int, out: torch.Tensor,
+                   out_len: torch.Tensor, status: torch.Tensor | None = None, stream=None):
+    """entropy_encode_noalloc: entropy_encode into caller buffers, with no
+    allocation in the library (the codebook must have been used on this
+    device before).  Returns (out, out_len, status)."""
+    _u8_cuda(x, "x")
+    _check(lib().entropy_encode_noalloc(cb.handle, _ptr(x), x.numel(), chunk_symbols, _ptr(out), out.numel(),
+                                        _ptr(out_len), _ptr(status), _stream(stream)), "entropy_encode_noalloc")
     return out, out_len, status
 
 

@@ -10,8 +10,16 @@
 
 #include "dev_common.h"
 
+// Chunk sizes of entropy_encode_noalloc, in a fixed device array instead of
+// allocated scratch: one u32 per chunk, up to 65536 chunks a call.  In host
+// code the name `scratch` only stands for the symbol; kernels get the array's
+// device address on each device, looked up once per device.
+static __device__ __align__(256) uint32_t scratch[65536];
+
 namespace ec {
 namespace {
+
+constexpr uint64_t kNoAllocChunks = sizeof(scratch) / sizeof(scratch[0]);
 
 constexpr uint64_t kMaxSegSymbols = 1ull << 33;   // per stream
 constexpr int kMaxDevices = 16;
@@ -79,6 +87,19 @@ int device_tables(const ec_codebook *cbc, const DevTables **out) {
     return EC_OK;
 }
 
+// The codebook's tables on the current device if an earlier call put them
+// there (no allocation): EC_E_INVAL otherwise.
+int resident_tables(const ec_codebook *cbc, const DevTables **out) {
+    ec_codebook *cb = const_cast<ec_codebook *>(cbc);
+    int dev;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(cb->mu);
+    if (!cb->dev[dev]) return EC_E_INVAL;
+    *out = cb->dev[dev];
+    return EC_OK;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 bool chunk_ok(uint32_t C) { return C >= kMinChunk && C <= kMaxChunk && C % kSub == 0; }
@@ -116,9 +137,12 @@ const DevTables *dev_table(const uint8_t *base, uint32_t i) {
     return reinterpret_cast<const DevTables *>(base + (uint64_t)i * sizeof(DevTables));
 }
 
+// fixed_sizes: chunk-size scratch the caller provides (fixed_chunks entries;
+// the codebook tables must then already be resident), else library scratch.
 int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
                 uint64_t in_stride, uint32_t C, uint32_t embed, uint8_t *d_out, uint64_t out_stride,
-                uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t s) {
+                uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t s,
+                uint32_t *fixed_sizes = nullptr, uint64_t fixed_chunks = 0) {
     if ((!ts.cbs && !ts.dev) || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_out || !d_out_len || !chunk_ok(C))
         return EC_E_INVAL;
     if (seg_n > kMaxSegSymbols || (seg_n && !d_in) || !aligned16(ts.dev)) return EC_E_INVAL;
@@ -139,7 +163,7 @@ int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n
         }
         const ec_codebook *cb = ts.cbs[i];
         if (!cb) return EC_E_INVAL;
-        int rc = device_tables(cb, &a.tabs[i]);
+        int rc = fixed_sizes ? resident_tables(cb, &a.tabs[i]) : device_tables(cb, &a.tabs[i]);
         if (rc) return rc;
         max_len = cb->host.max_len > max_len ? cb->host.max_len : max_len;
         if (embed && cb->host.codec != EC_CODEC_HUFFMAN) return EC_E_INVAL;
@@ -163,7 +187,10 @@ int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n
     a.sub_at = (uint32_t)L.sub_at;
     a.embed_lengths = embed ? 1 : 0;
     a.max_len = max_len;
-    if (L.n_chunks) {
+    if (L.n_chunks && fixed_sizes) {
+        if (L.n_chunks * n_seg > fixed_chunks) return EC_E_UNSUPPORTED;
+        a.sizes = fixed_sizes;
+    } else if (L.n_chunks) {
         void *p = nullptr;
         int rc = device_scratch(kScratchSizes, L.n_chunks * n_seg * 4, &p);
         if (rc) return rc;
@@ -208,6 +235,26 @@ int decode_impl(TableSrc ts, uint32_t codec, uint32_t n_seg, const uint8_t *d_in
     a.n_seg = n_seg;
     a.blocks_per_seg = (uint32_t)((seg_n + kSub - 1) / kSub);
     return hip_rc(launch_decode(a, codec, max_len, s));
+}
+
+struct ScratchAddr {
+    std::once_flag once;
+    uint32_t *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with it current).
+int noalloc_scratch(uint32_t **out) {
+    int dev;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    ScratchAddr &sa = g_scratch_addr[dev];
+    std::call_once(sa.once, [&] { sa.err = hipGetSymbolAddress((void **)&sa.ptr, HIP_SYMBOL(scratch)); });
+    if (sa.err != hipSuccess || !sa.ptr) return EC_E_HIP;
+    *out = sa.ptr;
+    return EC_OK;
 }
 
 }  // namespace
@@ -321,6 +368,19 @@ int entropy_encode(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint3
     const ec_codebook *cbs[1] = {cb};
     return encode_impl(TableSrc{cbs, nullptr}, 1, d_in, n, 0, chunk_symbols, 0, d_out, 0, out_cap, d_out_len,
                        d_status, stream);
+}
+
+int entropy_encode_noalloc(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols,
+                           uint8_t *d_out, uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status,
+                           hipStream_t stream) {
+    if (!chunk_ok(chunk_symbols)) return EC_E_INVAL;
+    if ((n + chunk_symbols - 1) / chunk_symbols > kNoAllocChunks) return EC_E_UNSUPPORTED;
+    uint32_t *sizes = nullptr;
+    int rc = noalloc_scratch(&sizes);
+    if (rc) return rc;
+    const ec_codebook *cbs[1] = {cb};
+    return encode_impl(TableSrc{cbs, nullptr}, 1, d_in, n, 0, chunk_symbols, 0, d_out, 0, out_cap, d_out_len,
+                       d_status, stream, sizes, kNoAllocChunks);
 }
 
 int entropy_decode(const ec_codebook *cb, const uint8_t *d_in, uint64_t in_len, uint8_t *d_out, uint64_t n,
