@@ -2,21 +2,31 @@
 //
 // Every 256-symbol sub-chunk starts at a bit offset recorded in the stream
 // index, so one lane decodes one sub-chunk serially and a wave64 decodes 64
-// sub-chunks side by side.  Each lane first copies the 16-byte blocks that
-// hold its sub-chunk from the payload into its own column of the wave's LDS
-// region: word k of lane l's bits goes to row k, column l.  A 64-bit window
-// at any bit position is then one read of three rows of the lane's column
-// plus two funnel shifts, and the 64 lanes of a read always hit 64 different
-// banks, whatever their positions (a contiguous copy of the compressed span
-// has the lanes read at scattered addresses: about twice the LDS time in bank
-// conflicts).  One window serves four codes.  (A global load inside the
-// decode loop would stall on the output stores too: one counter tracks both.)
-// QLC and EG stage the whole sub-chunk at once.  Huffman stages it in two
-// halves of a shorter column (the blocks still unread move down at the
-// half-run point), so that twelve waves per CU fit the LDS instead of eight:
-// its loop mostly waits on LDS reads, and more waves in flight hide them.
-// A sub-chunk too long for the region (data that barely compresses) is
-// decoded straight from global memory.
+// consecutive sub-chunks side by side (a "run").  Each lane's serial chain is
+// bound by LDS latency (about 70 cycles a table or window read), so the
+// decoder keeps as many chains in flight as a CU holds: sixteen waves, one
+// workgroup per CU, which covers a 64 MiB shard (4096 runs) in one round.
+//
+// LDS ring.  A lane's bits reach LDS through a ring of eight 16-byte blocks
+// in its own column of the wave's region: word k of the lane's data sits in
+// row (k + 1) mod 32, one 4-byte column per lane, so a 32-bit window at any
+// bit position is one read of two rows plus a funnel shift, and the 64 lanes
+// of a read always hit 64 different banks.  Rows 32 and 33 repeat rows 0 and
+// 1, so a window that reaches past row 31 reads on without wrapping.  A run
+// starts with its first four blocks in the ring and the next four in two
+// register buffers of two blocks, which take turns at uniform refill points
+// every 16 symbols: a lane writes the turn's buffer into its ring if it
+// holds blocks, then reloads it with its next two blocks not already in the
+// other buffer when the ring will have room for them two points later (else
+// it loads one block that all such lanes share: one request).  So a buffer's
+// blocks are always written at its next turn, two points (32 symbols) after
+// their loads were issued, and every point issues the same two load
+// instructions: the wave waits for the loads of two points before, never for
+// the ones just issued, nothing is fetched twice, and a wave starts decoding
+// as soon as its first four blocks arrive.  Ring addresses are taken modulo the ring, so no read ever leaves
+// the region, whatever the data.  A lane that consumed bits the ring did not
+// yet hold (more than 16 bits a symbol for 32 symbols: long codes only)
+// decodes its run again from global memory afterwards.
 //   QLC      the 3-bit prefix gives the code length through a funnel shift
 //            and a byte permute of the per-area lengths (no memory access on
 //            the dependency chain); the top 11 bits index a 2048-entry LDS
@@ -28,71 +38,64 @@
 //            canonical code limits.
 //   EG       count leading zeros z; the code is 2z + k + 1 bits; rank -> byte
 //            through a 256-entry LDS table.
-// After its last symbol a lane checks that it stopped exactly where the index
-// says its sub-chunk ends.
+// Decoded bytes gather in registers and leave as one whole 128-byte line per
+// lane and half run.  After its last symbol a lane checks that it stopped
+// exactly where the index says its sub-chunk ends, and the lane of a chunk's
+// last sub-chunk checks that the padding after it is zero.
 #include "dev_common.h"
 
 namespace ec {
 
 namespace {
 
-// Waves of the one workgroup per CU (which shares one copy of the tables):
-// three per SIMD for Huffman codes (its decode loop fits 168 VGPRs and
-// waits mostly on LDS), else two.
+// Waves of the one workgroup per CU: sixteen (128 registers each) for QLC
+// and Huffman; eight for Exp-Golomb, whose parse needs about 200 registers.
 template <int CODEC>
 constexpr int waves_for() {
-    return CODEC == EC_CODEC_HUFFMAN ? 12 : 8;
+    return CODEC == EC_CODEC_EXP_GOLOMB ? 8 : 16;
 }
 constexpr uint32_t kLdsBytes = 160 * 1024;
-constexpr uint32_t kRowBytes = 64 * 4;               // one word per lane
-// Rows past the last region that a lane may read: a position is clamped to
-// its region at the start of every 8 codes, which then move it by at most
-// 8 codes of the longest length the codec can read (QLC 11 bits, EG 25,
-// Huffman 40), and a window reads up to three rows from there.
-template <int CODEC>
-constexpr uint32_t guard_rows() {
-    constexpr uint32_t kMaxCode = CODEC == EC_CODEC_QLC ? 11 : CODEC == EC_CODEC_HUFFMAN ? EC_MAX_CODE_LEN : 25;
-    return (8 * kMaxCode + 31) / 32 + 3;
-}
+constexpr uint32_t kRowBytes = 64 * 4;             // one word per lane
+constexpr uint32_t kRingBlocks = 8;                // 16-byte blocks a lane holds in LDS
+constexpr uint32_t kRingRows = 4 * kRingBlocks;    // 32 word rows
+constexpr uint32_t kRegionRows = kRingRows + 2;    // plus copies of rows 0 and 1
+constexpr uint32_t kBatch = 2;                     // blocks per refill buffer
+constexpr uint32_t kNone = 0xffffffffu;            // refill buffer holding no blocks of the lane
 
-// Bits of a lane's sub-chunk staged in its LDS column.  Row r of the wave's
-// region holds word r - 1 of every lane's bits (row 0 is never written: a
-// window at a word boundary reads it and shifts it out).  Y is the position
-// plus 31 plus the region's row offset in bits (its LDS byte address / 8), so
-// the row holding the bit before the position is Y >> 5 and its LDS byte
-// address is (Y >> 5) * 256 + 4 * lane: no base to add, and a 32-bit window
-// never needs a special case.  A valid sub-chunk never leaves its region;
-// for corrupt streams prepare() clamps the position to the region's last row
-// every 8 codes, so reads stay inside the allocation (rows past a lane's data
-// hold other data or guard rows) and the end check flags the stream.
-struct ColBits {
-    uint32_t Y;      // see above
-    uint32_t col;    // 4 * lane
-    uint32_t base;   // Y of the lane's bit 0
-    uint32_t ylim;   // largest Y in the region's last row
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const uint32_t lds_word;
 
-    typedef __attribute__((address_space(3))) const uint32_t lds_word;
-    __device__ __forceinline__ uint32_t at(uint32_t yy) const {
-        lds_word *w = (lds_word *)(size_t)(((yy >> 5) << 8) | col);
-        return __builtin_amdgcn_alignbit(w[0], w[64], ~yy);
+// Bits of a lane's run read from its ring.  Y is the lane-relative bit
+// position plus 31: the row holding the bit before the position is
+// (Y >> 5) mod 32 (word k sits in row k + 1), and a window at a word boundary
+// reads that row and shifts it out.
+struct RingBits {
+    uint32_t Y;
+    uint32_t rbase;   // LDS byte address of the lane's column in row 0
+
+    __device__ __forceinline__ lds_word *row(uint32_t yy) const {
+        return (lds_word *)(size_t)(rbase + (((yy >> 5) & (kRingRows - 1)) << 8));
     }
-    __device__ __forceinline__ uint32_t win() const { return at(Y); }
+    __device__ __forceinline__ uint32_t win() const {
+        lds_word *w = row(Y);
+        return __builtin_amdgcn_alignbit(w[0], w[64], ~Y);
+    }
     __device__ __forceinline__ uint64_t win64() const {   // rows k, k + 1, k + 2 of the column
-        lds_word *w = (lds_word *)(size_t)(((Y >> 5) << 8) | col);
+        lds_word *w = row(Y);
         const uint32_t d0 = w[0], d1 = w[64], d2 = w[128];
         return ((uint64_t)__builtin_amdgcn_alignbit(d0, d1, ~Y) << 32) | __builtin_amdgcn_alignbit(d1, d2, ~Y);
     }
     __device__ __forceinline__ void adv(uint32_t l) { Y += l; }
-    __device__ __forceinline__ void prepare() { Y = min(Y, ylim); }
-    __device__ __forceinline__ uint64_t bit() const { return Y - base; }   // lane-relative position
+    __device__ __forceinline__ void prepare() {}
+    __device__ __forceinline__ uint32_t bit() const { return Y - 31; }
 };
 
-// Bits of a lane's sub-chunk read straight from global memory (spans that
-// do not fit in LDS): a 64-bit MSB-aligned buffer refilled 32 bits at a time,
+// Bits of a lane's sub-chunk read straight from global memory (runs the ring
+// did not serve): a 64-bit MSB-aligned buffer refilled 32 bits at a time,
 // loads clamped to the payload.
 struct GlobalBits {
     const uint32_t *base;   // lane's first payload word
-    uint32_t last;          // last readable word, relative to base
+    uint32_t last;          // last readable word, relative to base (clamped)
     uint64_t buf;           // next stream bits, MSB-aligned
     uint32_t nb;            // valid bits in buf (>= 32 between calls)
     uint32_t nxt;           // next word to fetch, relative to base
@@ -104,7 +107,8 @@ struct GlobalBits {
         const uint64_t lastw = n_words - 1;
         const uint64_t b = w0 < lastw ? w0 : lastw;
         base = payload + b;
-        last = (uint32_t)(lastw - b);
+        // a run never reads more than a few hundred words past its start
+        last = (uint32_t)min(lastw - b, (uint64_t)0xffffffffu);
         base0 = w0;
         const uint32_t o = (uint32_t)(bitpos & 31);
         buf = (((uint64_t)word(0) << 32) | word(1)) << o;
@@ -148,8 +152,10 @@ struct DeepTables {
 
 // Huffman code longer than 13 bits (rare): canonical limit search on a
 // 40-bit left-justified window.  Returns length | symbol << 8, the format
-// of the decode table's entries.
-__device__ __noinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt, const uint8_t *sym, uint32_t mx) {
+// of the decode table's entries.  Inlined: a called function starts by
+// waiting for every memory operation in flight, which would drain the
+// decoder's refill loads each time a wave meets a long code.
+__device__ __forceinline__ uint32_t huff_deep(uint64_t window, const DeepTables *dt, const uint8_t *sym, uint32_t mx) {
     const uint64_t w40 = window >> (64 - EC_MAX_CODE_LEN);
     uint32_t l = kHuffBits + 1;
     while (l < mx && w40 >= dt->limit[l - kHuffBits - 1]) ++l;
@@ -177,26 +183,30 @@ __device__ __noinline__ bool padding_set(const uint32_t *payload, uint64_t from,
     return any != 0;
 }
 
-// Decode one 256-symbol run (or the cnt < 256 symbols of a segment's last
-// run) from source S into dst; returns the bits of the QLC / EG "not a
-// codeword" flags (bit 8 and up).  FULL > 0: half HALF (symbols
-// 128 * HALF ..; 2: both halves) of a whole run from an LDS column (the
-// common case), in code with a fixed number of stores, so that the compiler
-// can count the memory operations in flight across it.
-template <int CODEC, int PAIRS, int FULL, class Src, int HALF = 0>
-__device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *dst, const uint16_t *l1,
-                                               const uint8_t *symtab, const DeepTables *dt, uint32_t max_len,
-                                               uint32_t lens, uint32_t k_eg) {
-    uint32_t bad = 0;
-    // QLC code lengths by area, one byte each: areas 0-3 in llo, 4-7 in lhi
-    uint32_t llo = 0, lhi = 0;
-    if (CODEC == EC_CODEC_QLC) {
+// Code parsing over a bit source S.  bad collects the QLC / EG "not a
+// codeword" flags (bit 8 and up).
+template <int CODEC, int PAIRS, class Src>
+struct Codes {
+    Src &S;
+    const uint16_t *l1;
+    const uint8_t *symtab;
+    const DeepTables *dt;
+    uint32_t max_len, k_eg;
+    uint32_t llo, lhi;   // QLC code lengths by area, one byte each: areas 0-3 in llo, 4-7 in lhi
+    uint32_t bad;
+
+    __device__ __forceinline__ Codes(Src &s, const uint16_t *l1_, const uint8_t *symtab_, const DeepTables *dt_,
+                                     uint32_t max_len_, uint32_t lens, uint32_t k_eg_)
+        : S(s), l1(l1_), symtab(symtab_), dt(dt_), max_len(max_len_), k_eg(k_eg_), llo(0), lhi(0), bad(0) {
+        if (CODEC == EC_CODEC_QLC) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            llo |= ((lens >> (4 * k)) & 15u) << (8 * k);
-            lhi |= ((lens >> (4 * k + 16)) & 15u) << (8 * k);
+            for (int k = 0; k < 4; ++k) {
+                llo |= ((lens >> (4 * k)) & 15u) << (8 * k);
+                lhi |= ((lens >> (4 * k + 16)) & 15u) << (8 * k);
+            }
         }
     }
+
     // The code that starts window w: its table entry and its length.  QLC
     // and EG entries hold the symbol in byte 0 (QLC: bit 8 flags an unused
     // suffix); Huffman entries hold the length in byte 0 and the symbol in
@@ -207,7 +217,7 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
     struct Code {
         uint32_t e, len;
     };
-    auto code_at = [&](uint32_t w) __attribute__((always_inline)) -> Code {
+    __device__ __forceinline__ Code code_at(uint32_t w) {
         if (CODEC == EC_CODEC_QLC) {
             const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, w, 29);   // 0x0c0c0c00 | w >> 29
             return Code{l1[w >> 21], __builtin_amdgcn_perm(lhi, llo, sel)};
@@ -223,22 +233,22 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             bad |= rank | (zr > 8u ? kQlcInvalid : 0u);
             return Code{symtab[rank & 255u], l};
         }
-    };
+    }
     // the symbol of an entry, and the byte permute that takes the symbols of
     // two entries (first in byte 0, second in byte 1)
-    constexpr uint32_t kSymShift = CODEC == EC_CODEC_HUFFMAN ? 8 : 0;
-    constexpr uint32_t kPairSel = CODEC == EC_CODEC_HUFFMAN ? 0x0c0c0501u : 0x0c0c0400u;
-    auto one = [&]() __attribute__((always_inline)) -> uint32_t {
+    static constexpr uint32_t kSymShift = CODEC == EC_CODEC_HUFFMAN ? 8 : 0;
+    static constexpr uint32_t kPairSel = CODEC == EC_CODEC_HUFFMAN ? 0x0c0c0501u : 0x0c0c0400u;
+
+    __device__ __forceinline__ uint32_t one() {
         const Code c = code_at(S.win());
         if (CODEC == EC_CODEC_QLC) bad |= c.e;
         S.adv(c.len);
         return (c.e >> kSymShift) & 0xffu;
-    };
+    }
     // two codes from one window when both fit in it; returns byte0 | byte1 << 8
-    auto two = [&]() __attribute__((always_inline)) -> uint32_t {
+    __device__ __forceinline__ uint32_t two() {
         const uint32_t w = S.win();
         Code c1, c2;
-        if (CODEC != EC_CODEC_HUFFMAN) c1 = code_at(w);
         if (CODEC == EC_CODEC_HUFFMAN) {
             // Both table reads from the one window: a code the table covers
             // has at most 13 bits, so 19 bits of the window follow it.  A
@@ -260,18 +270,19 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             c1.e = e1;
             c2.e = e2;
         } else {
+            c1 = code_at(w);
             c2 = code_at(w << c1.len);
             S.adv(c1.len + c2.len);
             if (CODEC == EC_CODEC_QLC) bad |= c1.e | c2.e;
         }
         return __builtin_amdgcn_perm(c2.e, c1.e, kPairSel);   // c1's symbol, c2's symbol
-    };
+    }
     // Four codes from one 64-bit window: the second pair's 32-bit window lies
     // inside the 64 bits when a pair has at most 32 bits (QLC: codes of at
     // most 11 bits; EG in pair mode: at most 16; Huffman: codes the table
     // covers, at most 13 bits each, else (rare) the pair step twice).
     // Returns the four bytes in order.
-    auto four = [&]() __attribute__((always_inline)) -> uint32_t {
+    __device__ __forceinline__ uint32_t four() {
         const uint64_t W = S.win64();
         const uint32_t w = (uint32_t)(W >> 32);
         if (CODEC != EC_CODEC_HUFFMAN) {
@@ -299,17 +310,13 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
         }
         S.adv((e12 + e3 + e4) & 0xffu);
         return __builtin_amdgcn_perm(e2, e1, kPairSel) | (__builtin_amdgcn_perm(e4, e3, kPairSel) << 16);
-    };
+    }
     // eight codes -> two output words
-    auto eight = [&](uint32_t &lo, uint32_t &hi) __attribute__((always_inline)) {
+    __device__ __forceinline__ void eight(uint32_t &lo, uint32_t &hi) {
         S.prepare();
-        if (FULL && PAIRS) {
+        if (PAIRS) {
             lo = four();
             hi = four();
-        } else if (PAIRS) {
-            const uint32_t p0 = two(), p1 = two(), p2 = two(), p3 = two();
-            lo = p0 | (p1 << 16);
-            hi = p2 | (p3 << 16);
         } else {
             uint32_t b[8];
 #pragma unroll
@@ -317,76 +324,8 @@ __device__ __forceinline__ uint32_t decode_run(Src &S, uint32_t cnt, uint8_t *ds
             lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
             hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
         }
-    };
-
-    if constexpr (FULL == 2) {
-        // A loop of 16 codes a pass (Huffman, EG): the whole run unrolled
-        // would not fit the instruction cache next to the Huffman pair step's
-        // rare long code path, and the EG loop would spill.  The words of a
-        // half run still gather in registers (placed by the uniform pass
-        // counter) and leave as one whole 128-byte line per lane: 16-byte
-        // stores to 64 lanes' separate lines leave partial lines in L2 that
-        // get written back several times.
-        static_for<(HALF == 2 ? 0 : HALF), (HALF == 2 ? 2 : HALF + 1)>([&](auto hf) __attribute__((always_inline)) {
-            constexpr int half = decltype(hf)::value;
-            uint32_t o[32];
-#pragma nounroll
-            for (int i = 0; i < 8; ++i) {
-                uint32_t w0, w1, w2, w3;
-                eight(w0, w1);
-                eight(w2, w3);
-                // a uniform branch per pass keeps o in registers
-                static_for<0, 8>([&](auto jc) __attribute__((always_inline)) {
-                    constexpr int j = decltype(jc)::value;
-                    if (i == j) {
-                        o[4 * j] = w0;
-                        o[4 * j + 1] = w1;
-                        o[4 * j + 2] = w2;
-                        o[4 * j + 3] = w3;
-                    }
-                });
-            }
-            uint4 *line = reinterpret_cast<uint4 *>(dst + 128 * half);
-            static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int i = decltype(ic)::value;
-                line[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-            });
-        });
-    } else if constexpr (FULL == 1) {
-        // 128 decoded bytes are collected in registers and written as one
-        // whole cache line: 16-byte stores to 64 lanes' separate lines leave
-        // partial lines in L2 that get written back more than once
-        static_for<(HALF == 2 ? 0 : HALF), (HALF == 2 ? 2 : HALF + 1)>([&](auto hf) __attribute__((always_inline)) {
-            constexpr int half = decltype(hf)::value;
-            uint32_t o[32];
-            static_for<0, 16>([&](auto hc) __attribute__((always_inline)) {
-                constexpr int h = decltype(hc)::value;
-                eight(o[2 * h], o[2 * h + 1]);
-                // keep each group's table reads next to their use (without
-                // this the scheduler hoists all 128 symbols' reads and spills)
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            uint4 *line = reinterpret_cast<uint4 *>(dst + 128 * half);
-            static_for<0, 8>([&](auto ic) __attribute__((always_inline)) {
-                constexpr int i = decltype(ic)::value;
-                line[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-            });
-        });
-    } else if (cnt == kSub) {
-        for (int i = 0; i < kSub / 16; ++i) {
-            uint32_t o[4];
-            eight(o[0], o[1]);
-            eight(o[2], o[3]);
-            *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    } else {
-        for (uint32_t k = 0; k < cnt; ++k) {
-            S.prepare();
-            dst[k] = (uint8_t)one();
-        }
     }
-    return bad;
-}
+};
 
 // A lane's sub-chunk: its bits [sb, eb) in the payload and its symbols,
 // and the 16-byte payload blocks that hold them.
@@ -401,14 +340,14 @@ struct LaneTask {
 };
 
 // Index entries of a lane's sub-chunk as loaded (resolved later, so that the
-// loads are in flight while the wave decodes an earlier task).
+// loads are in flight while the wave decodes an earlier run).
 struct IndexRaw {
     uint64_t co0, co1;        // the lane's chunk: byte offsets of its start and end in the payload
     uint32_t e_start, e_end;  // the lane's sub-chunk: start and end bit in its chunk
     bool last;                // the sub-chunk is its chunk's last: the padding after it is checked
 };
 
-// Stream fields the tasks of a segment share (validated once per segment).
+// Stream fields the runs of a segment share (validated once per segment).
 struct StreamInfo {
     const uint8_t *stream;
     uint64_t po, pb;
@@ -448,48 +387,89 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
     return t;
 }
 
-// Blocks FIRST .. FIRST + K - 1 of a lane's sub-chunk, loaded into
-// registers (indexes clamped to the lane's last block, or to the payload's
-// first block for lanes with nothing to decode, so every load stays inside
-// the payload).
-template <int K, int FIRST = 0>
-__device__ __forceinline__ void issue_blocks(const StreamInfo &si, const LaneTask &t, uint4 (&v)[K]) {
+// Blocks first .. first + K - 1 of a lane's sub-chunk, loaded into registers
+// (indexes clamped to the lane's last block, or to the payload's first block
+// for lanes with nothing to decode, so every load stays inside the payload).
+template <int K>
+__device__ __forceinline__ void issue_blocks(const StreamInfo &si, const LaneTask &t, uint32_t first, uint4 (&v)[K]) {
     const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + t.blk0;
     const uint32_t last = t.nv ? t.nv - 1 : 0u;
     static_for<0, K>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
-        v[k] = src[min((uint32_t)(FIRST + k), last)];
+        v[k] = src[min(first + (uint32_t)k, last)];
     });
 }
 
-// Blocks first .. nv_max - 1 of the lanes' sub-chunks (those not
-// prefetched) into their LDS columns, behind a call (whole-run staging).
-__device__ __noinline__ void stage_rest(uint32_t col_word0, const uint4 *src, uint32_t nv, uint32_t first,
-                                        uint32_t nv_max) {
-    typedef __attribute__((address_space(3))) uint32_t lds_u32;
-    for (uint32_t j = first; j < nv_max; j += 4) {   // four loads in flight per lane
-        uint4 v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (j + k < nv) v[k] = src[j + k];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (j + k < nv) {
-                lds_u32 *w = (lds_u32 *)(size_t)(col_word0 + (4 * (j + k)) * kRowBytes);
-                w[0] = v[k].x;
-                w[64] = v[k].y;
-                w[128] = v[k].z;
-                w[192] = v[k].w;
-            }
-        }
+// Two blocks (8 words) into one quarter q of a lane's ring: blocks 8m + 2q
+// and 8m + 2q + 1 hold words 32m + 8q .. + 7, rows 8q + 1 .. 8q + 8 (row 32
+// is row 0's copy, so the last word of quarter 3 also goes to row 0; the
+// first word of quarter 0 also goes to row 33, the copy of row 1).
+__device__ __forceinline__ void write_quarter(uint32_t rbase, uint32_t q, const uint4 (&v)[kBatch]) {
+    lds_u32 *p = (lds_u32 *)(size_t)(rbase + (8 * q + 1) * kRowBytes);
+    static_for<0, kBatch>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        p[(4 * k + 0) * 64] = v[k].x;
+        p[(4 * k + 1) * 64] = v[k].y;
+        p[(4 * k + 2) * 64] = v[k].z;
+        p[(4 * k + 3) * 64] = v[k].w;
+    });
+    if (q == 0 || q == 3) {
+        lds_u32 *e = (lds_u32 *)(size_t)(rbase + (q == 3 ? 0u : 33u) * kRowBytes);
+        e[0] = q == 3 ? v[kBatch - 1].w : v[0].x;
     }
 }
 
-// Everything but a whole run decoded from the lane's column, behind a call,
-// read straight from global memory: a segment's last, shorter run; runs
-// whose halves do not fit the column's stages (data that barely compresses);
-// sub-chunks without bits.
+// Blocks first and first + 1 of a lane's sub-chunk into a refill buffer
+// (the second clamped to the lane's last block); a lane with no block left
+// there loads the payload's first block instead, the same for every such lane
+// (one request).  Returns the buffer's tag: first, or kNone.
+__device__ __forceinline__ uint32_t issue_batch(const StreamInfo &si, const LaneTask &t, uint32_t first,
+                                                uint4 (&v)[kBatch]) {
+    const uint4 *pay = reinterpret_cast<const uint4 *>(si.stream + si.po);
+    const bool need = first < t.nv;
+    const uint64_t b0 = need ? t.blk0 + first : 0;
+    const uint64_t b1 = need ? t.blk0 + min(first + 1, t.nv - 1) : 0;
+    v[0] = pay[b0];
+    v[1] = pay[b1];
+    return need ? first : kNone;
+}
+
+// Lane i's 64-byte output piece of a run (a half line) as four 16-byte parts
+// o[4 s .. 4 s + 3], turned around within each group of four lanes:
+// afterwards part k of lane i holds part i of the piece of lane k of its
+// group, so that store k of the group writes one whole 64-byte piece (4 lanes
+// x 16 bytes) and a store instruction writes sixteen such pieces instead of
+// 16 bytes of 64 lines: partial lines cost L2 extra write-backs (64 MiB
+// written 16 bytes a line at a time takes 25 us, 64 bytes at a time 14 us).
+// Two butterfly stages exchange parts with lane i ^ d (d = 1, 2) through a
+// quad permute: a lane whose bit d is clear keeps its parts s with s & d
+// clear and takes the partner's others, and the reverse.
+__device__ __forceinline__ void transpose4(uint32_t (&o)[16], uint32_t lane) {
+    static_for<0, 2>([&](auto dc) __attribute__((always_inline)) {
+        constexpr int d = 1 << decltype(dc)::value;
+        constexpr int kSel = d == 1 ? 0xb1 : 0x4e;   // quad_perm 1,0,3,2 / 2,3,0,1
+        const bool hi = (lane & d) != 0;
+        static_for<0, 4>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int s0 = decltype(sc)::value;
+            if constexpr ((s0 & d) == 0) {
+                constexpr int s1 = s0 | d;
+                static_for<0, 4>([&](auto wc) __attribute__((always_inline)) {
+                    constexpr int w = decltype(wc)::value;
+                    const uint32_t x = hi ? o[4 * s0 + w] : o[4 * s1 + w];
+                    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kSel, 0xf, 0xf, false);
+                    if (hi)
+                        o[4 * s0 + w] = y;
+                    else
+                        o[4 * s1 + w] = y;
+                });
+            }
+        });
+    });
+}
+
+// Everything the ring did not decode, behind a call, read straight from
+// global memory: a segment's last, shorter run; runs that outran the ring
+// (long codes); sub-chunks without bits.
 template <int CODEC, int PAIRS>
 __device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payload, uint64_t pb, uint8_t *dst,
                                          const uint16_t *l1, const uint8_t *symtab, const DeepTables *dt,
@@ -499,7 +479,18 @@ __device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payl
     if (L.nv > 0) {   // (symbols but no bits: corrupt)
         GlobalBits S;
         S.init(payload, pb >> 2, L.sb);
-        bad = decode_run<CODEC, PAIRS, 0>(S, L.cnt, dst, l1, symtab, dt, max_len, lens, k_eg);
+        Codes<CODEC, PAIRS, GlobalBits> D(S, l1, symtab, dt, max_len, lens, k_eg);
+        if (L.cnt == kSub) {
+            for (uint32_t i = 0; i < kSub / 16; ++i) {
+                uint32_t o[4];
+                D.eight(o[0], o[1]);
+                D.eight(o[2], o[3]);
+                *reinterpret_cast<uint4 *>(dst + 16 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        } else {
+            for (uint32_t k = 0; k < L.cnt; ++k) dst[k] = (uint8_t)D.one();
+        }
+        bad = D.bad;
         end_pos = S.bit();
         want_pos = L.eb;
     }
@@ -508,93 +499,64 @@ __device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payl
     if ((bad & ~0xffu) || end_pos != want_pos || pad) or_status(status, EC_S_CORRUPT);
 }
 
-// Persistent workgroups: workgroup b takes tasks b, b + G, ... (G = grid);
-// a task is 64 consecutive sub-chunks of one stream per wave.
-//
-// A lane's column holds kStage blocks at a time, in two stages.  Stage 1
-// is the sub-chunk's first kStage blocks (prefetched in registers while the
-// wave decoded its previous task); the blocks after them are loaded into
-// registers meanwhile.  At the half-run point (128 symbols) the blocks not
-// yet consumed move down to the column's first slots and the loaded ones
-// follow them (stage 2).  A lane whose first half reads past stage 1, or
-// whose rest does not fit stage 2, decodes its run again from global memory.
+// Persistent workgroups, one per CU.  A task is one run of 64 consecutive
+// sub-chunks for one wave.
+//   One stream: the runs are dealt wave by wave over the whole grid: in
+//   round r, wave w of workgroup b takes run r * G * 16 + w * G + b (G
+//   workgroups), so a partial round still spreads over every CU.
+//   Several streams: workgroup-tasks of 16 consecutive runs of one stream
+//   (one per wave), workgroup b taking b, b + G, ...; the codebook tables of
+//   the stream sit in LDS while the workgroup decodes it.
 template <int CODEC, int PAIRS>
 __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const DecodeArgs a) {
-    constexpr uint32_t kWaves = waves_for<CODEC>();
-    constexpr uint32_t kThreads = 64 * kWaves;
+    constexpr int kWaves = waves_for<CODEC>();
+    constexpr int kThreads = 64 * kWaves;
     constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
                                    : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
                                                                : 1;
     constexpr bool kSym = CODEC != EC_CODEC_QLC;
     constexpr bool kHasDeep = CODEC == EC_CODEC_HUFFMAN;
-    constexpr uint32_t kGuardRows = guard_rows<CODEC>();
     struct Head {
-        uint4 tabv[kTableVec];     // QLC / Huffman decode table
-        uint8_t symtab[kSym ? 256 : 4];       // EG: rank -> byte; Huffman: canonical order -> byte
-        DeepTables deep[kHasDeep ? 1 : 0];    // Huffman only
+        uint4 tabv[kTableVec];                 // QLC / Huffman decode table
+        uint8_t symtab[kSym ? 256 : 4];        // EG: rank -> byte; Huffman: canonical order -> byte
+        DeepTables deep[kHasDeep ? 1 : 0];     // Huffman only
     };
-    // the rest of the CU's LDS: one region of kRows rows per wave, then guard rows
-    constexpr uint32_t kHeadBytes = (sizeof(Head) + kRowBytes - 1) / kRowBytes * kRowBytes;
-    constexpr uint32_t kRows = (kLdsBytes - kHeadBytes - kGuardRows * kRowBytes) / (kWaves * kRowBytes);
-    // Huffman: two stages of kStage blocks; other codecs: the whole run
-    // staged at once (up to kRows rows), kStage blocks of it prefetched
-    constexpr bool kTwo = CODEC == EC_CODEC_HUFFMAN;
-    constexpr int kStage = kTwo ? (int)((kRows - 1) / 4 < 16 ? (kRows - 1) / 4 : 16) : 16;
-    static_assert(kStage >= 8 && (kTwo || 1 + 4 * kStage <= kRows), "column stages too short");
     struct Smem {
         Head h;
-        alignas(256) uint32_t cols[kWaves][kRows * 64];
-        uint32_t guard[kGuardRows * 64];
+        alignas(256) uint32_t ring[kWaves][kRegionRows * 64];
     };
     static_assert(sizeof(Smem) <= kLdsBytes, "LDS budget");
     __shared__ Smem sm;
     const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.h.tabv);
     uint8_t *symtab = sm.h.symtab;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads > 0 ? (a.blocks_per_seg + kThreads - 1) / kThreads
-                                                                           : 1u;
-    const uint32_t n_tasks = gx * a.n_seg;
-    // One stream: the last, partial round of tasks (every task, when the
-    // grid is larger than the task count) is spread over every workgroup
-    // wave by wave (wave w of workgroup b takes the round's (w * G + b)-th
-    // run of 64 sub-chunks), so that its waves sit on the SIMDs of all CUs
-    // instead of filling a few CUs.
-    const uint32_t tail_at = n_tasks / gridDim.x * gridDim.x;   // first task of a partial round
-    const bool spread = a.n_seg == 1 && tail_at != n_tasks;
-    const uint32_t n_iter = spread ? tail_at + gridDim.x : n_tasks;
-    auto seg_of = [&](uint32_t tt) __attribute__((always_inline)) { return spread ? 0u : tt / gx; };
-    // the wave's first sub-chunk in task tt
-    auto first_sub = [&](uint32_t tt) __attribute__((always_inline)) -> uint32_t {
-        if (spread && tt >= tail_at) return tail_at * kThreads + (wave * gridDim.x + blockIdx.x) * 64;
-        return (tt - tt / gx * gx) * kThreads + wave * 64;
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t R = (a.blocks_per_seg + 63) / 64;        // runs per stream
+    const bool one_stream = a.n_seg == 1;
+    const uint32_t Q = (R + kWaves - 1) / kWaves;           // workgroup-tasks per stream (several streams)
+    const uint32_t n_u = one_stream ? (R + G * kWaves - 1) / (G * kWaves) * G : Q * a.n_seg;
+    // stream and run of this wave in workgroup-task u (run >= R: none)
+    auto seg_of = [&](uint32_t u) __attribute__((always_inline)) { return one_stream ? 0u : u / Q; };
+    auto run_of = [&](uint32_t u) __attribute__((always_inline)) -> uint32_t {
+        if (one_stream) return (u / G) * G * kWaves + wave * G + b;
+        return (u - (u / Q) * Q) * kWaves + wave;
     };
-    typedef __attribute__((address_space(3))) uint32_t lds_u32;
-    const uint32_t region = (uint32_t)(size_t)(lds_u32 *)sm.cols[wave];   // 256-byte aligned
-    lds_u32 *my_col = (lds_u32 *)(size_t)(region + 4 * lane);
+    const uint32_t rbase = (uint32_t)(size_t)(lds_u32 *)sm.ring[wave] + 4 * lane;
 
     uint32_t cur_seg = ~0u;
     StreamInfo si = {};
     const DevTables *tab = nullptr;
     uint32_t *status = nullptr;
-    // codebook constants, read once per segment: a global load in the loop
-    // would wait for the prefetch loads issued before it
+    // codebook constants, read once per segment
     uint32_t seg_lens = 0, seg_max_len = 0, seg_k_eg = 0;
-    bool have_cur = false, have_next_raw = false, have_first = false, seg_ok = false;
-    LaneTask cur = {};
+    bool seg_ok = false, have_next = false, have_first = false;
     IndexRaw next_raw = {}, first_raw = {};
-    // blocks in flight: during a first half this task's blocks kStage ..,
-    // during a second half the next task's first kStage blocks
-    uint4 pre[kStage];
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) pre[k] = make_uint4(0u, 0u, 0u, 0u);
 
-    for (uint32_t t = blockIdx.x; t < n_iter; t += gridDim.x) {
-        const uint32_t seg = seg_of(t);
+    for (uint32_t u = b; u < n_u; u += G) {
+        const uint32_t seg = seg_of(u);
         if (seg != cur_seg) {
             __syncthreads();   // the previous segment's tables are no longer read
             tab = seg_tables<DecodeArgs>(seg);
-            // this thread's share of the decode table, in flight while the
-            // header is checked and the first task's index entries are requested
             constexpr int kTabPer = (kTableVec + kThreads - 1) / kThreads;
             uint4 tv[kTabPer];
             const uint4 *tsrc = reinterpret_cast<const uint4 *>(CODEC == EC_CODEC_HUFFMAN ? tab->hl1 : tab->l1);
@@ -626,7 +588,9 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
                 if (po != end || pb % 16 || po + pb > a.in_len || (n > 0 && pb == 0) || pb >= (1ull << 36))
                     bits = EC_S_BAD_HEADER;
             }
-            if (bits && t == seg * gx && tid == 0) flag(status, bits);   // once, by the segment's first task
+            // once per segment: by its first workgroup-task's thread 0
+            const bool first_u = one_stream ? u == 0 : u == seg * Q;
+            if (bits && first_u && tid == 0) flag(status, bits);
             seg_ok = bits == 0;
             cur_seg = seg;
             si.stream = stream;
@@ -634,10 +598,11 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             si.pb = pb;
             si.nch = nch;
             si.spc = C / kSub;
-            have_cur = have_next_raw = false;
-            const uint32_t g0f = first_sub(t);
-            have_first = seg_ok && g0f < a.blocks_per_seg;
-            if (have_first) first_raw = issue_index(a, si, g0f + lane);
+            have_next = false;
+            // this wave's first index entries, in flight across the barrier
+            const uint32_t run0 = run_of(u);
+            have_first = seg_ok && run0 < R;
+            if (have_first) first_raw = issue_index(a, si, run0 * 64 + lane);
 #pragma unroll
             for (int k = 0; k < kTabPer; ++k) {
                 if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kTableVec) sm.h.tabv[tid + k * kThreads] = tv[k];
@@ -657,176 +622,159 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         }
         if (!seg_ok) continue;   // uniform over the workgroup
 
-        const uint32_t g0 = first_sub(t);   // the wave's first sub-chunk
-        // the wave's next task, if it is in the same stream
-        const uint32_t t1 = t + gridDim.x;
-        const bool next_same = t1 < n_iter && seg_of(t1) == seg;
-        const uint32_t g0n = first_sub(t1);
-        const bool next_busy = next_same && g0n < a.blocks_per_seg;
-        if (g0 >= a.blocks_per_seg) {   // uniform over the wave
-            have_cur = have_next_raw = false;
+        const uint32_t run = run_of(u);
+        const uint32_t g0 = run * 64;   // the wave's first sub-chunk
+        if (run >= R) {                 // uniform over the wave
+            have_next = false;
             continue;
         }
-        if (!have_cur) {   // nothing prefetched: this task's index and first blocks now
-            cur = resolve(a, si, have_first ? first_raw : issue_index(a, si, g0 + lane), g0 + lane, status);
-            issue_blocks<kStage>(si, cur, pre);
-        }
+        const LaneTask L = resolve(a, si, have_next ? next_raw : have_first ? first_raw : issue_index(a, si, g0 + lane),
+                                   g0 + lane, status);
         have_first = false;
-        if (next_busy && !have_next_raw) next_raw = issue_index(a, si, g0n + lane);
-        const LaneTask L = cur;
-        const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
-        // a whole run decoded from the lane's column: for two stages of at
-        // most kStage blocks each; else when the wave's longest sub-chunk fits
-        uint32_t nv_max = 0;
-        if constexpr (!kTwo) {
-            nv_max = L.nv;
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) nv_max = max(nv_max, (uint32_t)__shfl_xor((int)nv_max, d, 64));
-        }
-        const bool fits = kTwo || 1 + 4 * nv_max <= kRows;   // uniform over the wave
-        bool full = live && fits && L.cnt == kSub && L.nv > 0 && (!kTwo || L.nv <= (uint32_t)(2 * kStage));
+        // the first four blocks (past a lane's last block: copies of it),
+        // and the next four in the refill buffers, written at the first two
+        // points (so the ring holds eight blocks after 32 symbols)
+        uint4 f[4];
+        issue_blocks<4>(si, L, 0, f);
+        uint4 bufA[kBatch], bufB[kBatch];
+        uint32_t tagA = issue_batch(si, L, 4, bufA);
+        uint32_t tagB = issue_batch(si, L, 6, bufB);
+        // the next task's index entries, in flight during this run
+        const uint32_t u1 = u + G;
+        const uint32_t run1 = u1 < n_u ? run_of(u1) : R;
+        have_next = u1 < n_u && seg_of(u1) == seg && run1 < R;
+        if (have_next) next_raw = issue_index(a, si, run1 * 64 + lane);
 
-        // stage 1 (two stages: the first kStage blocks), from registers
-        if (fits) {
-            static_for<0, kStage>([&](auto kc) __attribute__((always_inline)) {
-                constexpr int k = decltype(kc)::value;
-                if ((uint32_t)k < L.nv) {
-                    lds_u32 *w = my_col + (1 + 4 * k) * 64;   // rows 1 + 4 k ...
-                    w[0] = pre[k].x;
-                    w[64] = pre[k].y;
-                    w[128] = pre[k].z;
-                    w[192] = pre[k].w;
-                }
-            });
-            if (!kTwo && nv_max > (uint32_t)kStage)
-                stage_rest(region + kRowBytes + 4 * lane, reinterpret_cast<const uint4 *>(si.stream + si.po) + L.blk0,
-                           L.nv, kStage, nv_max);
+        const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
+        const bool full = live && L.cnt == kSub && L.nv > 0;
+        {
+            const uint4 q0[kBatch] = {f[0], f[1]}, q1[kBatch] = {f[2], f[3]};
+            write_quarter(rbase, 0, q0);
+            write_quarter(rbase, 1, q1);
         }
+        uint32_t nb = 4;   // blocks written so far
         // each lane reads only its own column: program order suffices
         asm volatile("" ::: "memory");
-        auto prefetch_next = [&]() __attribute__((always_inline)) {
-            // the next task's first blocks, and the index entries of the one after
-            if (next_busy) {
-                cur = resolve(a, si, next_raw, g0n + lane, status);
-                issue_blocks<kStage>(si, cur, pre);
-                have_cur = true;
-                const uint32_t t2 = t1 + gridDim.x;
-                const uint32_t g0nn = first_sub(t2);
-                have_next_raw = t2 < n_iter && seg_of(t2) == seg && g0nn < a.blocks_per_seg;
-                if (have_next_raw) next_raw = issue_index(a, si, g0nn + lane);
-            } else {
-                have_cur = have_next_raw = false;
-            }
-        };
-        if constexpr (kTwo) {
-            // the blocks after stage 1, in flight during the first half
-            if (__ballot(full && L.nv > (uint32_t)kStage)) issue_blocks<kStage, kStage>(si, L, pre);
-        } else {
-            prefetch_next();
-        }
 
         uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + L.first_sym;
-        const uint32_t ylim = region / 8 + kRows * 32 - 1;
-        constexpr int kFull = CODEC == EC_CODEC_QLC ? 1 : 2;
         const uint32_t want = (uint32_t)(L.eb - L.blk0 * 128);
-        ColBits S;
-        S.col = 4 * lane;
-        S.base = region / 8 + 31;
-        S.Y = S.base + (uint32_t)(L.sb - L.blk0 * 128);
-        S.ylim = ylim;
+        RingBits S;
+        S.rbase = rbase;
+        S.Y = 31 + (uint32_t)(L.sb - L.blk0 * 128);
+        bool over = false;   // the run consumed bits the ring did not hold yet
         uint32_t bad = 0;
-        if (full)
-            bad = decode_run<CODEC, PAIRS, kFull, ColBits, kTwo ? 0 : 2>(S, kSub, dst, l1, symtab, sm.h.deep,
-                                                                        seg_max_len, seg_lens, seg_k_eg);
-
-        uint32_t bh = 0;
-        if constexpr (kTwo) {
-            // stage 2: blocks bh .. nv - 1, where bh holds the first bit not
-            // yet consumed.  The first half was read from stage 1 when no bit
-            // before the position lay past it.
+        // A refill point with buffer X (the other one: Y): check the position
+        // against the blocks written; write X if it holds blocks (always the
+        // next ones, with room: see the load condition); reload X with the
+        // next blocks Y does not hold when the ring has room for them now,
+        // and so two points later.
+        auto refill = [&](uint4(&X)[kBatch], uint32_t &tagX, uint32_t tagY) __attribute__((always_inline)) {
             const uint32_t pos = S.bit();
-            bh = pos >> 7;
-            full = full && pos <= (uint32_t)kStage * 128 && bh < L.nv && L.nv - bh <= (uint32_t)kStage;
-            if (full) {
-                // blocks bh .. kStage - 1 move down to slots 0 .. (slot j is
-                // read before any later write lands on it: bh + j >= j)
-                const uint32_t keep = min(L.nv, (uint32_t)kStage) - bh;   // bh <= kStage (pos bound)
-#pragma nounroll
-                for (uint32_t j = 0; j < keep; ++j) {
-                    const lds_u32 *r = my_col + (1 + 4 * (bh + j)) * 64;
-                    const uint32_t x0 = r[0], x1 = r[64], x2 = r[128], x3 = r[192];
-                    lds_u32 *w = my_col + (1 + 4 * j) * 64;
-                    w[0] = x0;
-                    w[64] = x1;
-                    w[128] = x2;
-                    w[192] = x3;
-                }
-                // block kStage + k goes to slot keep + k (at most kStage - 1)
-                static_for<0, kStage>([&](auto kc) __attribute__((always_inline)) {
-                    constexpr int k = decltype(kc)::value;
-                    if ((uint32_t)(kStage + k) < L.nv) {
-                        lds_u32 *w = my_col + (1 + 4 * (keep + k)) * 64;
-                        w[0] = pre[k].x;
-                        w[64] = pre[k].y;
-                        w[128] = pre[k].z;
-                        w[192] = pre[k].w;
-                    }
-                });
-                S.Y -= bh * 128;
-            } else {
-                bh = 0;
+            over = over || pos > nb * 128;
+            if (tagX == nb) {
+                // X's loads were issued two points ago; only the other
+                // buffer's two (and, after a group's stores, those) may
+                // still be in flight: wait for vmcnt <= 2 (expcnt and
+                // lgkmcnt left at their maxima)
+                __builtin_amdgcn_s_waitcnt(0x0f72);
+                write_quarter(rbase, (nb >> 1) & 3, X);
+                nb += kBatch;
             }
-            asm volatile("" ::: "memory");
-            prefetch_next();
+            const uint32_t next = tagY == nb ? nb + kBatch : nb;
+            const bool room = next + kBatch <= (pos >> 7) + kRingBlocks;
+            tagX = issue_batch(si, L, room ? next : kNone, X);
+        };
+        // Every lane runs the ring decode (the output lines are written by
+        // the lane's group together); lanes that are not full decode ring
+        // contents that do not matter, and their lines are not stored.
+        const uint64_t full_mask = __ballot(full);
+        uint8_t *wave_dst = a.out + (uint64_t)seg * a.out_stride + (uint64_t)g0 * kSub;
+        {
+            Codes<CODEC, PAIRS, RingBits> D(S, l1, symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg);
+            // Output words gather in registers, 64 bytes per lane, and leave
+            // as whole 64-byte pieces (see transpose4).
+            constexpr int kOW = 16;   // words per group: a 64-byte piece per lane
+            static_for<0, kSub / (4 * kOW)>([&](auto gc) __attribute__((always_inline)) {
+                constexpr int grp = decltype(gc)::value;
+                uint32_t o[kOW];
+                // 16 symbols -> o[8 i + 4 P ..]; a uniform branch per pass
+                // keeps o in registers
+                auto pass = [&](int i, auto pc) __attribute__((always_inline)) {
+                    constexpr int P = decltype(pc)::value;
+                    uint32_t w0, w1, w2, w3;
+                    D.eight(w0, w1);
+                    D.eight(w2, w3);
+                    static_for<0, kOW / 8>([&](auto jc) __attribute__((always_inline)) {
+                        constexpr int j = decltype(jc)::value;
+                        if (i == j) {
+                            o[8 * j + 4 * P] = w0;
+                            o[8 * j + 4 * P + 1] = w1;
+                            o[8 * j + 4 * P + 2] = w2;
+                            o[8 * j + 4 * P + 3] = w3;
+                        }
+                    });
+                };
+                // two passes of 16 symbols per iteration, a refill point
+                // after each: the buffers' turns are fixed in the code
+#pragma nounroll
+                for (int i = 0; i < kOW / 8; ++i) {
+                    pass(i, std::integral_constant<int, 0>{});
+                    refill(bufA, tagA, tagB);
+                    pass(i, std::integral_constant<int, 1>{});
+                    refill(bufB, tagB, tagA);
+                }
+                transpose4(o, lane);
+                // store k: lane 4 j + p writes part p of the piece of lane 4 j + k
+                uint8_t *part = wave_dst + (lane & ~3u) * kSub + 4 * kOW * grp + 16 * (lane & 3);
+                const uint32_t own = (uint32_t)(full_mask >> (lane & ~3u)) & 0xfu;   // the group's full lanes
+                static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+                    constexpr int k = decltype(kc)::value;
+                    if ((own >> k) & 1)
+                        *reinterpret_cast<uint4 *>(part + k * kSub) =
+                            make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+                });
+            });
+            bad = D.bad;
         }
-
-        bool corrupt = false;
-        if (full) {
-            if constexpr (kTwo)
-                bad |= decode_run<CODEC, PAIRS, kFull, ColBits, 1>(S, kSub, dst, l1, symtab, sm.h.deep, seg_max_len,
-                                                                   seg_lens, seg_k_eg);
-            corrupt = (bad & ~0xffu) || S.bit() + bh * 128 != want;
-        }
+        const uint32_t end = S.bit();
+        over = over || end > nb * 128;
+        bool corrupt = full && !over && ((bad & ~0xffu) || end != want);
         // the zero padding after a chunk's last sub-chunk
-        const bool pad_check = full && !corrupt && L.pad_end > L.eb;
+        const bool pad_check = full && !over && !corrupt && L.pad_end > L.eb;
         if (__ballot(pad_check))
             if (pad_check) corrupt = padding_set(reinterpret_cast<const uint32_t *>(si.stream + si.po), L.eb, L.pad_end);
-        if (__ballot(live && !full))
-            if (live && !full)
+        const bool rest = live && (!full || over);
+        if (__ballot(rest)) {
+            // a lane that outran its ring rewrites the line its group stored
+            // for it: the group's stores complete first
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+            if (rest)
                 decode_rest<CODEC, PAIRS>(L, reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb, dst, l1,
                                           symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg, status);
+        }
         if (corrupt) flag(status, EC_S_CORRUPT);
-        // the column is rewritten at the next task, after this lane's reads
+        // the ring is rewritten at the next task, after this lane's reads
         asm volatile("" ::: "memory");
     }
 }
 
-// Workgroups of a persistent launch: as many as can be resident at once,
-// never more than there are tasks.
-template <class K>
-hipError_t decode_grid(K kernel, uint32_t threads, uint32_t n_tasks, uint32_t *grid) {
+template <int CODEC, int PAIRS>
+hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
+    constexpr int kWaves = waves_for<CODEC>();
+    constexpr int kThreads = 64 * kWaves;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<CODEC, PAIRS>, kThreads, 0);
     if (e != hipSuccess) return e;
-    const uint64_t g = (uint64_t)(per_cu > 0 ? per_cu : 1) * (uint64_t)(cus > 0 ? cus : 1);
-    *grid = g < n_tasks ? (uint32_t)g : n_tasks;
-    return hipSuccess;
-}
-
-template <int CODEC, int PAIRS>
-hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
-    constexpr uint32_t kThreads = 64 * waves_for<CODEC>();
-    uint32_t gx = (a.blocks_per_seg + kThreads - 1) / kThreads;
-    if (gx == 0) gx = 1;   // still validate the header
-    // one stream: up to one workgroup per run of 64 sub-chunks, its waves
-    // spread over the workgroups; else up to one per task
-    const uint32_t runs = (a.blocks_per_seg + 63) / 64;
-    const uint32_t cap = a.n_seg == 1 ? (runs > gx ? runs : gx) : gx * a.n_seg;
-    uint32_t grid = 0;
-    const hipError_t e = decode_grid(decode_kernel<CODEC, PAIRS>, kThreads, cap, &grid);
-    if (e != hipSuccess) return e;
+    const uint32_t R = (a.blocks_per_seg + 63) / 64;
+    // one stream: up to one workgroup per run (its waves dealt over the grid);
+    // several: up to one per workgroup-task
+    uint64_t cap = a.n_seg == 1 ? R : (uint64_t)(R + kWaves - 1) / kWaves * a.n_seg;
+    if (cap == 0) cap = 1;   // still validate the header
+    const uint64_t resident = (uint64_t)(per_cu > 0 ? per_cu : 1) * (uint64_t)(cus > 0 ? cus : 1);
+    const uint32_t grid = (uint32_t)(cap < resident ? cap : resident);
     hipLaunchKernelGGL((decode_kernel<CODEC, PAIRS>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }

@@ -1,11 +1,10 @@
 """The decoder's task mapping at the sizes where it changes: one stream of
-exactly one full round of workgroup tasks on every CU, one sub-chunk more
-(a partial last round, spread wave by wave over the workgroups), a ragged
-size just short of it, and a stream smaller than one task per workgroup.
-Huffman decodes with twelve waves per workgroup (768 sub-chunks a task),
-QLC with eight (512).  A run of 64 sub-chunks lost or decoded twice shows
-up as a round trip that differs from the input or as a status flag; the
-streams themselves are checked against the oracle elsewhere."""
+exactly one full round (sixteen waves of 64 sub-chunks on every CU), one
+sub-chunk more (a second round of one run), a ragged size just past it, one
+just short of it, and a stream smaller than one run per CU.  A run of 64
+sub-chunks lost or decoded twice shows up as a round trip that differs from
+the input or as a status flag; the streams themselves are checked against
+the oracle elsewhere."""
 
 import pytest
 
@@ -33,7 +32,7 @@ def _sizes(task_subchunks):
     return [full, full + 256, full + 256 + 17, full - 1000, 64 * 256 * 7 + 5]
 
 
-@pytest.mark.parametrize("name,task", [("huffman", 768), ("qlc", 512)])
+@pytest.mark.parametrize("name,task", [("huffman", 1024), ("qlc", 1024)])
 def test_round_trip_at_task_round_boundaries(ec, name, task):
     counts = [int(c) for c in stats.histogram(synth.draw("ffn1", 100, 1 << 20))]
     cb = ec.Codebook.huffman(counts) if name == "huffman" else ec.Codebook.qlc(counts)

@@ -216,29 +216,35 @@ def test_chunks_of_mixed_code_length(ec, C, depth):
 
 
 @pytest.mark.parametrize("C", [4096, 16384])
-def test_huffman_sub_chunks_that_leave_the_column_stages(ec, C):
+@pytest.mark.parametrize("codec", ["huffman", "eg0"])
+def test_sub_chunks_that_outrun_the_ring(ec, C, codec):
     """Sub-chunks of different code-length profiles side by side, so that one
-    wave holds lanes decoded from their LDS column in two stages and lanes
-    that decode again from global memory: a first half too long for the
-    first stage, a second half too long for the second, both halves long
-    enough that the second stage takes blocks from registers, and short
-    ones."""
-    counts = [int(c) for c in deep_counts(20)]
-    cb, ocb = ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
-    length = np.array(ocb.length)
-    by_len = {int(l): int(np.flatnonzero(length == l)[0]) for l in (3, 9, 12)}
-    s3, s9, s12 = by_len[3], by_len[9], by_len[12]
+    wave holds lanes the decoder's LDS ring keeps up with and lanes whose long
+    codes (more than 16 bits a symbol over 32 symbols) outrun it and decode
+    again from global memory: long codes in the first half, in the second
+    half, throughout, short ones, and a mix."""
+    if codec == "huffman":
+        counts = [int(c) for c in deep_counts(20)]
+        cb, ocb = ec.Codebook.huffman(counts), cbm.huffman_codebook(counts)
+        length = np.array(ocb.length)
+        long_, mid, short = (int(np.flatnonzero(length == l)[0]) for l in (20, 12, 3))
+    else:   # order-0 Exp-Golomb: ranks 128..255 take 15-17 bits
+        counts = [int(c) for c in np.arange(256, 0, -1)]
+        cb, ocb = ec.Codebook.exp_golomb(counts, 0), cbm.eg_codebook(counts, 0)
+        r2s = ocb.rank_to_sym
+        long_, mid, short = r2s[255], r2s[40], r2s[0]
     rng = np.random.default_rng(C)
     kinds = [
-        np.full(256, s3),                                        # short
-        np.concatenate([np.full(128, s12), np.full(128, s3)]),   # first half past stage 1
-        np.concatenate([np.full(128, s3), np.full(128, s12)]),   # rest past stage 2
-        np.full(256, s9),                                        # both stages full
-        rng.integers(0, 256, 256),                               # mixed
+        np.full(256, short),                                         # short
+        np.concatenate([np.full(128, long_), np.full(128, short)]),  # long first half
+        np.concatenate([np.full(128, short), np.full(128, long_)]),  # long second half
+        np.full(256, long_),                                         # long throughout
+        np.full(256, mid),                                           # middling
+        rng.integers(0, 256, 256),                                   # mixed
     ]
     pick = rng.integers(0, len(kinds), 3 * C // 256 + 5)
-    x = np.concatenate([kinds[k] for k in pick] + [np.full(77, s12)]).astype(np.uint8)
-    print("case huffman stages", C, x.size, flush=True)
+    x = np.concatenate([kinds[k] for k in pick] + [np.full(77, long_)]).astype(np.uint8)
+    print("case ring overrun", codec, C, x.size, flush=True)
     want = st.encode_stream(x, ocb, C)
     got, status = _gpu_encode(ec, cb, x, C)
     assert status == 0 and got == want
