@@ -13,7 +13,17 @@ kernel (its average duration gives the roofline figure); the per-op
 breakdown under "kernels" comes from an untimed pass with events around
 every op, since each recorded event adds a few microseconds of queue time.
 
-Prints ONE JSON line.  Options: --workload {ffn1,tiny_qlc,ffn2,grad,batch,bf16}.
+With no --workload the headline is the 64 MiB FFN1-like shard and
+extra.configs carries every workload: the tiny base-scheme QLC case, FFN1,
+FFN2, the gradient shard and the 64 x 4 MiB batch (single-stage and
+three-stage paths), each with per-op times, a roofline object and the CPU
+oracle timed on one core and on all cores.  A plain 64 MiB device copy is
+timed in the same run as the practical bandwidth ceiling.
+
+All host-side work (synthetic data, CPU oracle legs) runs before the GPU is
+first touched, so the process pools fork from a process without GPU state.
+
+Prints ONE JSON line.  --workload NAME runs just that workload (profiling).
 """
 
 from __future__ import annotations
@@ -21,6 +31,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import multiprocessing as mp
 import os
 import platform
 import re
@@ -35,6 +46,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "encode & decode GB/s (uncompressed e4m3) on 1 MI355X, % HBM roofline; compression %"
 HBM_PEAK_GBPS = 8000.0
+CONFIG_ORDER = ["tiny_qlc", "ffn1", "ffn2", "grad", "batch"]
+HEADLINE = "ffn1"
+BATCH_SHARDS, BATCH_SHARD_N, BATCH_CHUNK = 64, 1 << 22, 16384
 
 WORKLOAD_TEXT = {
     "tiny_qlc": "tiny base-scheme QLC: 2^20 e4m3 bytes, N(0,1), seed 0; codebook from a 2^20 calibration draw (seed 1)",
@@ -52,6 +66,7 @@ CODECS = {
     "ffn1": ["qlc", "huffman"],
     "ffn2": ["qlc_adapted", "qlc", "qlc_opt", "huffman"],
     "grad": ["eg", "qlc", "qlc_opt", "huffman"],
+    "batch": ["huffman"],
 }
 
 
@@ -60,10 +75,16 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="ffn1", choices=list(WORKLOAD_TEXT))
+    p.add_argument("--workload", default=None, choices=list(WORKLOAD_TEXT),
+                   help="run only this workload (default: headline FFN1 plus every workload under extra.configs)")
+    p.add_argument("--extra-steps", type=int, default=20, help="timed steps per workload under extra.configs")
     p.add_argument("--sets", type=int, default=3, help="buffer sets rotated per step (defeats the 256 MB MALL)")
-    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    p.add_argument("--copy-ref", action="store_true", help="also run plain device copies (counter calibration)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baselines")
+    p.add_argument("--cpu-workers", type=int, default=0,
+                   help="processes for the all-core oracle leg (default: OMP_NUM_THREADS, else the CPUs this "
+                        "process may run on)")
+    p.add_argument("--copy-ref", action="store_true",
+                   help="accepted for older recorded commands; the 64 MiB copy now runs in every run")
     p.add_argument("--verbose", action="store_true")
     return p.parse_args()
 
@@ -71,20 +92,6 @@ def parse_args():
 def log(args, *a):
     if args.verbose:
         print(*a, file=sys.stderr, flush=True)
-
-
-def make_codebook(ec, name, counts):
-    if name == "qlc":
-        return ec.Codebook.qlc(counts)
-    if name == "qlc_adapted":
-        return ec.Codebook.qlc(counts, *ec.QLC_ADAPTED)
-    if name == "qlc_opt":   # the cheapest layout with four code lengths
-        return ec.Codebook.qlc(counts, *ec.qlc_optimal_area_layout(counts, 4))
-    if name == "huffman":
-        return ec.Codebook.huffman(counts)
-    if name == "eg":
-        return ec.Codebook.exp_golomb(counts, -1)
-    raise KeyError(name)
 
 
 def source_hash(*names):
@@ -109,48 +116,228 @@ def load_traffic(kernel_file, workload, op):
     return None
 
 
-# ---------------------------------------------------------------- CPU leg
+def roofline_obj(kernel, moved, avg_us, traffic, copy_gbps):
+    achieved = moved / avg_us / 1e3
+    return dict(kernel=kernel, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=traffic, algorithmic_bytes=moved,
+                avg_us=round(avg_us, 2), copy_ceiling_GBps=copy_gbps,
+                frac_of_copy=round(achieved / copy_gbps, 4) if copy_gbps else None)
 
-def cpu_baseline(x, counts, codec_names, chunk, calib_rows):
-    """The oracle as it stands (single-threaded C + Python), timed on the
-    host over the same step on the same shard."""
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_workers(args):
+    if args.cpu_workers > 0:
+        return args.cpu_workers
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+# ---------------------------------------------------------------- host data
+
+def _gen(task):
+    import synth
+    kind = task[0]
+    if kind == "x":
+        return synth.workload(task[1])
+    if kind == "calib":                     # one calibration shard of a workload
+        w = synth.WORKLOADS[task[1]]
+        return synth.draw(w.calib_recipe, task[2], w.calib_n)
+    if kind == "batch":                     # one shard of the multi-shard batch
+        return synth.batch_shards(1, BATCH_SHARD_N, first_seed=1000 + task[1])[0]
+    if kind == "bf16":
+        w = synth.BF16_WORKLOAD
+        return synth.bf16_draw(w["seed"], w["n"], w["sigma"])
+    raise KeyError(kind)
+
+
+def make_data(names, workers):
+    """Synthetic inputs of the named workloads, drawn in a process pool."""
+    import synth
+    tasks = []
+    for n in names:
+        if n == "batch":
+            tasks += [("batch", i) for i in range(BATCH_SHARDS)]
+            tasks += [("calib", "ffn1", s) for s in synth.WORKLOADS["ffn1"].calib_seeds]
+        elif n == "bf16":
+            tasks.append(("bf16",))
+        else:
+            tasks.append(("x", n))
+            tasks += [("calib", n, s) for s in synth.WORKLOADS[n].calib_seeds]
+    # the long draws first, so they do not end up last on one worker
+    order = sorted(range(len(tasks)), key=lambda i: tasks[i][0] not in ("x", "bf16"))
+    with mp.get_context("fork").Pool(min(workers, len(tasks))) as pool:
+        got = pool.map(_gen, [tasks[i] for i in order], chunksize=1)
+    res = dict(zip([tasks[i] for i in order], got))
+    data = {}
+    for n in names:
+        if n == "batch":
+            data[n] = dict(x=np.stack([res[("batch", i)] for i in range(BATCH_SHARDS)]),
+                           calib=np.stack([res[("calib", "ffn1", s)] for s in synth.WORKLOADS["ffn1"].calib_seeds]))
+        elif n == "bf16":
+            data[n] = dict(x=res[("bf16",)])
+        else:
+            data[n] = dict(x=res[("x", n)],
+                           calib=np.stack([res[("calib", n, s)] for s in synth.WORKLOADS[n].calib_seeds]))
+    return data
+
+
+# ---------------------------------------------------------------- CPU leg
+#
+# The oracle as it stands: plain Python around the bit-serial C encoder and
+# decoder.  Single core: one process over a bounded sample of the shard.
+# All cores: the shard split into contiguous ranges of whole chunks (whole
+# shards for the batch), one process per range, each running the same step
+# on its range as a stream of its own; the wall time is the slowest range.
+
+_CPU = {}
+
+
+def _oracle_codebook(name, counts):
     from oracle import codebooks as cbm
+    if name == "qlc":
+        return cbm.qlc_codebook(counts)
+    if name == "qlc_adapted":
+        return cbm.qlc_codebook(counts, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX)
+    if name == "qlc_opt":
+        return cbm.qlc_codebook(counts, *cbm.qlc_optimal_areas(counts, 4))
+    if name == "huffman":
+        return cbm.huffman_codebook(counts)
+    if name == "eg":
+        return cbm.eg_codebook(counts)
+    raise KeyError(name)
+
+
+def _cpu_step(name, lo, hi):
+    """One step of the oracle over bytes [lo, hi) of a workload (over shards
+    [lo, hi) for the batch); returns its duration in seconds."""
     from oracle import stats
     from oracle import stream as st
-    builders = {
-        "qlc": lambda c: cbm.qlc_codebook(c),
-        "qlc_adapted": lambda c: cbm.qlc_codebook(c, cbm.QLC_ADAPTED_AREAS, cbm.QLC_ADAPTED_SUFFIX),
-        "qlc_opt": lambda c: cbm.qlc_codebook(c, *cbm.qlc_optimal_areas(c, 4)),
-        "huffman": lambda c: cbm.huffman_codebook(c),
-        "eg": lambda c: cbm.eg_codebook(c),
-    }
-    cbs = [builders[n](counts) for n in codec_names]
+    d = _CPU[name]
     t0 = time.perf_counter()
-    h = stats.histogram(x)
-    stats.kl_bits(h, counts, q_add=1)
-    for cb in cbs:
-        s = st.encode_stream(x, cb, chunk)
-        y = st.decode_stream(s, cb)
-        assert np.array_equal(y, x)
-    dt = time.perf_counter() - t0
-    return dict(value=round(len(codec_names) * x.size / dt / 1e9, 5), unit="GB/s", cores=1, kind="oracle",
-                sample="one full step on the same %d-byte shard (histogram, KL, %s encode+decode), "
-                       "single-threaded, %.1f s, host %s" % (x.size, "/".join(codec_names), dt,
-                                                             platform.processor() or platform.machine()))
+    parts = [d["x"][i] for i in range(lo, hi)] if name == "batch" else [d["x"][lo:hi]]
+    for x in parts:
+        h = stats.histogram(x)
+        stats.kl_bits(h, d["counts"], q_add=1)
+        for cb in d["cbs"]:
+            s = st.encode_stream(x, cb, d["chunk"])
+            if not np.array_equal(st.decode_stream(s, cb), x):
+                raise RuntimeError("oracle round trip failed (%s)" % name)
+    return time.perf_counter() - t0
 
 
-# ---------------------------------------------------------------- GPU leg
+def cpu_baselines(data, names, workers, sample_bytes=8 << 20):
+    """{workload: cpu_baseline object}: one core over a bounded sample, all
+    cores over the whole shard."""
+    import synth
+    from oracle import _clib, stats
+    _clib.lib()                       # load the C core once, before the fork
+    plan = {}
+    for n in names:
+        d = data[n]
+        counts = [int(c) for c in stats.histogram(d["calib"].reshape(-1))]
+        chunk = BATCH_CHUNK if n == "batch" else synth.WORKLOADS[n].chunk_symbols
+        _CPU[n] = dict(x=d["x"], counts=counts, chunk=chunk,
+                       cbs=[_oracle_codebook(c, counts) for c in CODECS[n]])
+        if n == "batch":
+            units, unit_bytes = BATCH_SHARDS, BATCH_SHARD_N
+        else:
+            units, unit_bytes = d["x"].size // chunk, chunk
+            if d["x"].size % chunk:
+                units += 1
+        plan[n] = (units, unit_bytes)
+    out = {}
+    model = cpu_model()
+    with mp.get_context("fork").Pool(workers) as pool:
+        for n in names:
+            units, ub = plan[n]
+            N = data[n]["x"].size
+            k = len(CODECS[n])
+            # one core, bounded sample (whole chunks / shards from the start)
+            s_units = max(1, min(units, sample_bytes // ub))
+            hi = s_units if n == "batch" else min(N, s_units * ub)
+            one = _cpu_step(n, 0, hi)
+            s_bytes = s_units * ub if n == "batch" else hi
+            # all cores, whole workload
+            P = min(workers, units)
+            cuts = [units * i // P for i in range(P + 1)]
+            ranges = [(n, cuts[i], cuts[i + 1]) if n == "batch" else
+                      (n, cuts[i] * ub, min(N, cuts[i + 1] * ub)) for i in range(P)]
+            t0 = time.perf_counter()
+            pool.starmap(_cpu_step, ranges, chunksize=1)
+            wall = time.perf_counter() - t0
+            out[n] = dict(
+                value=round(k * N / wall / 1e9, 5), unit="GB/s", cores=P, kind="oracle",
+                sample="the whole %d-byte workload, one step (histogram, KL, %s encode+decode) split over %d "
+                       "processes by contiguous %s; wall %.2f s; CPU %s"
+                       % (N, "/".join(CODECS[n]), P, "shards" if n == "batch" else "chunk ranges", wall, model),
+                one_core=dict(value=round(k * s_bytes / one / 1e9, 5), unit="GB/s", cores=1,
+                              sample="the first %d bytes, one step, %.2f s" % (s_bytes, one)),
+                cpu_model=model)
+    _CPU.clear()
+    return out
 
-def run_single(args, ec, torch):
+
+# ---------------------------------------------------------------- GPU legs
+
+def make_codebook(ec, name, counts):
+    if name == "qlc":
+        return ec.Codebook.qlc(counts)
+    if name == "qlc_adapted":
+        return ec.Codebook.qlc(counts, *ec.QLC_ADAPTED)
+    if name == "qlc_opt":   # the cheapest layout with four code lengths
+        return ec.Codebook.qlc(counts, *ec.qlc_optimal_area_layout(counts, 4))
+    if name == "huffman":
+        return ec.Codebook.huffman(counts)
+    if name == "eg":
+        return ec.Codebook.exp_golomb(counts, -1)
+    raise KeyError(name)
+
+
+def ev_us(a, b):
+    return a.elapsed_time(b) * 1e3
+
+
+def copy_ceiling(torch, x_d, reps=30, pairs=3):
+    """Plain device-to-device copies of x_d's size (read N, write N),
+    rotating over `pairs` source/destination pairs so that the working set
+    (pairs x 2N) exceeds the 256 MB last-level cache: mean event time and
+    GB/s moved."""
+    srcs = [x_d] + [x_d.clone() for _ in range(pairs - 1)]
+    dsts = [torch.empty_like(x_d) for _ in range(pairs)]
+    for i in range(2 * pairs):
+        dsts[i % pairs].copy_(srcs[i % pairs])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        dsts[i % pairs].copy_(srcs[i % pairs])
+        b.record()
+    torch.cuda.synchronize()
+    if not all(torch.equal(d, x_d) for d in dsts):
+        raise SystemExit("device copy mismatch")
+    us = statistics.mean(ev_us(a, b) for a, b in evs)
+    nb = x_d.numel() * x_d.element_size()
+    return dict(bytes=nb, us=round(us, 2), GBps=round(2 * nb / us / 1e3, 1), buffer_pairs=pairs)
+
+
+def run_single(name, d, args, ec, torch, steps, warmup, copy_gbps):
     import synth
     dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[args.workload]
-    codec_names = CODECS[args.workload]
+    w = synth.WORKLOADS[name]
+    codec_names = CODECS[name]
     C = w.chunk_symbols
-    t = time.perf_counter()
-    x = synth.workload(args.workload)
-    calib = synth.calibration_shards(args.workload)
-    log(args, "data %.1f s, sha256 %s" % (time.perf_counter() - t, synth.sha256(x)[:16]))
+    x, calib = d["x"], d["calib"]
     N = x.size
 
     # calibration (off the critical path): GPU histograms, host codebook build
@@ -203,9 +390,9 @@ def run_single(args, ec, torch):
             rec(4 + 2 * j)
 
     def new_events():
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(args.steps)]
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(steps)]
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
@@ -213,10 +400,10 @@ def run_single(args, ec, torch):
     # event costs a few microseconds of queue time, so the timed steps below
     # record only the two around the dominant kernel)
     evs = new_events()
-    for i in range(args.steps):
+    for i in range(steps):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
-    per_op = {o: [e[k].elapsed_time(e[k + 1]) * 1e3 for e in evs] for k, o in enumerate(op_names)}   # us
+    per_op = {o: [ev_us(e[k], e[k + 1]) for e in evs] for k, o in enumerate(op_names)}
     dominant = max((o for o in op_names if o.endswith("code")), key=lambda o: statistics.mean(per_op[o]))
     dom_k = op_names.index(dominant)
 
@@ -224,33 +411,27 @@ def run_single(args, ec, torch):
     evs = new_events()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(sets[i % len(sets)], evs[i], only=dom_k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_us = [e[dom_k].elapsed_time(e[dom_k + 1]) * 1e3 for e in evs]
-
-    if args.copy_ref:   # plain copies of N bytes, for the hardware-counter scale factor
-        dst = torch.empty_like(x_d)
-        for _ in range(5):
-            dst.copy_(sets[-1]["x"])
-        torch.cuda.synchronize()
+    dom_us = [ev_us(e[dom_k], e[dom_k + 1]) for e in evs]
 
     # correctness of what was timed
     st = status.cpu().numpy()
     if st.any():
-        raise SystemExit("device status bits set: %s" % st)
+        raise SystemExit("device status bits set (%s): %s" % (name, st))
     for S in sets:
         for B in S["bufs"]:
             if not torch.equal(B["y"], S["x"]):
-                raise SystemExit("round trip mismatch")
+                raise SystemExit("round trip mismatch (%s)" % name)
     hist_ok = np.array_equal(sets[0]["hist"].cpu().numpy()[0], np.bincount(x, minlength=256))
 
     stream_len = [int(B["n"].item()) for B in sets[0]["bufs"]]
     kernels = {}
     for o in op_names:
         us = statistics.mean(per_op[o])
-        d = dict(us=round(us, 2), us_median=round(statistics.median(per_op[o]), 2))
+        dd = dict(us=round(us, 2), us_median=round(statistics.median(per_op[o]), 2))
         if o == "byte_histogram":
             moved = N + 256 * 8
         elif o.endswith("_encode") or o.endswith("_decode"):
@@ -258,10 +439,10 @@ def run_single(args, ec, torch):
             moved = N + stream_len[j]
         else:
             moved = 2 * 256 * 8
-        d["GBps_uncompressed"] = round(N / us / 1e3, 1) if o != "pmf_kl" else None
-        d["hbm_GBps"] = round(moved / us / 1e3, 1)
-        d["roofline_frac"] = round(moved / us / 1e3 / HBM_PEAK_GBPS, 4)
-        kernels[o] = d
+        dd["GBps_uncompressed"] = round(N / us / 1e3, 1) if o != "pmf_kl" else None
+        dd["hbm_GBps"] = round(moved / us / 1e3, 1)
+        dd["roofline_frac"] = round(moved / us / 1e3 / HBM_PEAK_GBPS, 4)
+        kernels[o] = dd
 
     compression = {}
     idx = ec.index_bytes(N, C)
@@ -273,50 +454,29 @@ def run_single(args, ec, torch):
         if n == "qlc_opt":
             compression[n]["layout"] = ec.qlc_optimal_area_layout(counts, 4)
 
-    ms_per_step = wall / args.steps * 1e3
-    value = len(codec_names) * N / (wall / args.steps) / 1e9
     j = codec_names.index(dominant.rsplit("_", 1)[0])
-    moved = N + stream_len[j]
     kfile = "decode.hip" if dominant.endswith("decode") else "encode.hip"
-    traffic = load_traffic(kfile, args.workload, dominant)
-    avg_us = statistics.mean(dom_us)   # measured inside the timed steps
-    roofline = dict(kernel=dominant, bound="hbm", achieved=round(moved / avg_us / 1e3, 1),
-                    peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(moved / avg_us / 1e3 / HBM_PEAK_GBPS, 4),
-                    traffic=traffic, algorithmic_bytes=moved, avg_us=round(avg_us, 2))
-
-    kl = float(sets[0]["kl"].item())
-    out = dict(metric=METRIC, value=round(value, 2), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-               ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
-               dtype="u8", data="synthetic",
-               config=dict(workload=WORKLOAD_TEXT[args.workload], name=args.workload, n_bytes=N, chunk_symbols=C,
-                           codecs=codec_names, buffer_sets=args.sets,
-                           step="byte_histogram + pmf_kl + per codec entropy_encode + entropy_decode"),
-               roofline=roofline, kernels=kernels,
-               kernels_note="per-op event times from an untimed pass with events around every op",
-               compression=compression,
-               extra=dict(kl_bits_vs_calibration=kl, histogram_exact=hist_ok, codebook_build_us=round(build_us, 1),
-                          avg_pmf_top=float(avg_pmf_d.max().item()), numpy=np.__version__,
-                          input_sha256=synth.sha256(x)[:16]))
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x, counts, codec_names, C, None)
-    else:
-        out["cpu_baseline"] = None
-    return out
+    roofline = roofline_obj(dominant, N + stream_len[j], statistics.mean(dom_us),
+                            load_traffic(kfile, name, dominant), copy_gbps)
+    res = dict(value=round(len(codec_names) * N / (wall / steps) / 1e9, 2), unit="GB/s", steps=steps,
+               warmup=warmup, ms_per_step=round(wall / steps * 1e3, 4), n_bytes=N, chunk_symbols=C,
+               codecs=codec_names, workload=WORKLOAD_TEXT[name],
+               step="byte_histogram + pmf_kl + per codec entropy_encode + entropy_decode",
+               roofline=roofline, kernels=kernels, compression=compression,
+               kl_bits_vs_calibration=float(sets[0]["kl"].item()), histogram_exact=hist_ok,
+               codebook_build_us=round(build_us, 1), avg_pmf_top=float(avg_pmf_d.max().item()))
+    return res
 
 
-def run_batch(args, ec, torch):
+def run_batch(d, args, ec, torch, steps, warmup, copy_gbps):
     """64 x 4 MiB shards: single-stage (one fixed avg-PMF Huffman codebook)
     against three-stage (per-shard histogram, per-shard codebook, codebook
     lengths embedded in each stream), the codebooks built on the GPU
     (three_stage) or on the host after a copy of the histograms
     (three_stage_host)."""
-    import synth
     dev = torch.device("cuda:0")
-    C = 16384
-    t = time.perf_counter()
-    x = synth.batch_shards(64, 1 << 22)
-    calib = synth.calibration_shards("ffn1")
-    log(args, "data %.1f s" % (time.perf_counter() - t))
+    C = BATCH_CHUNK
+    x, calib = d["x"], d["calib"]
     S, n = x.shape
     x_d = torch.from_numpy(x).to(dev)
     pooled_d = ec.byte_histogram(torch.from_numpy(calib).to(dev).view(-1))[0]
@@ -334,63 +494,111 @@ def run_batch(args, ec, torch):
     tables = torch.empty((S, ec.device_codebook_bytes()), dtype=torch.uint8, device=dev)
     rtables = torch.empty_like(tables)
 
-    def single():
-        ec.byte_histogram(x_d, out=hist)
-        ec.pmf_kl(hist, pooled_d, q_add=1, out=kl)
-        ec.encode_batch(fixed, x_d, C, out=out, out_len=lens, status=status)
-        ec.decode_batch(fixed, out, n, out=y, status=status)
+    # each path is a list of (op name, callable); the host path's codebook
+    # build is one op that includes the copy of the histograms to the host
+    single = [("byte_histogram", lambda: ec.byte_histogram(x_d, out=hist)),
+              ("pmf_kl", lambda: ec.pmf_kl(hist, pooled_d, q_add=1, out=kl)),
+              ("huffman_encode_batch", lambda: ec.encode_batch(fixed, x_d, C, out=out, out_len=lens, status=status)),
+              ("huffman_decode_batch", lambda: ec.decode_batch(fixed, out, n, out=y, status=status))]
+    three = [("byte_histogram", lambda: ec.byte_histogram(x_d, out=hist)),                 # frequency analysis
+             ("build_huffman_device", lambda: ec.build_huffman_device(hist, out=tables, status=status)),
+             ("encode_batch_device", lambda: ec.encode_batch_device(tables, x_d, C, embed_lengths=True, out=out,
+                                                                    out_len=lens, status=status)),
+             # the receiver rebuilds each codebook from the lengths its stream carries
+             ("huffman_tables_from_streams", lambda: ec.huffman_tables_from_streams(out, out=rtables,
+                                                                                    status=status)),
+             ("decode_batch_device", lambda: ec.decode_batch_device(rtables, out, n, out=y, status=status))]
+    host_cbs = []
 
-    def three():
-        ec.byte_histogram(x_d, out=hist)                                  # frequency analysis
-        ec.build_huffman_device(hist, out=tables, status=status)          # codebook generation
-        ec.encode_batch_device(tables, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
-        # the receiver rebuilds each codebook from the lengths its stream carries
-        ec.huffman_tables_from_streams(out, out=rtables, status=status)
-        ec.decode_batch_device(rtables, out, n, out=y, status=status)
-
-    def three_host():
-        ec.byte_histogram(x_d, out=hist)
+    def host_build():
         h = hist.cpu().numpy()          # histograms -> host
-        cbs = [ec.Codebook.huffman([int(c) for c in row]) for row in h]
-        ec.encode_batch(cbs, x_d, C, embed_lengths=True, out=out, out_len=lens, status=status)
-        ec.decode_batch(cbs, out, n, out=y, status=status)
-        return cbs
+        host_cbs[:] = [ec.Codebook.huffman([int(c) for c in row]) for row in h]
 
-    res = {}
-    for name, fn in (("single_stage", single), ("three_stage", three), ("three_stage_host", three_host)):
-        for _ in range(args.warmup):
-            fn()
+    three_host = [("byte_histogram", lambda: ec.byte_histogram(x_d, out=hist)),
+                  ("host_codebooks", host_build),
+                  ("encode_batch", lambda: ec.encode_batch(host_cbs, x_d, C, embed_lengths=True, out=out,
+                                                           out_len=lens, status=status)),
+                  ("decode_batch", lambda: ec.decode_batch(host_cbs, out, n, out=y, status=status))]
+
+    def check(label):
+        if status.cpu().numpy().any() or not torch.equal(y, x_d):
+            raise SystemExit("batch round trip failed (%s)" % label)
+
+    res, per_shard = {}, {}
+    for label, ops in (("single_stage", single), ("three_stage", three), ("three_stage_host", three_host)):
+        for _ in range(warmup):
+            for _, f in ops:
+                f()
+        torch.cuda.synchronize()
+        # per-op breakdown (untimed pass, events around every op)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)]
+        for e in evs:
+            for k, (_, f) in enumerate(ops):
+                e[k].record()
+                f()
+            e[len(ops)].record()
+        torch.cuda.synchronize()
+        check(label)
+        per_op = {o: statistics.mean(ev_us(e[k], e[k + 1]) for e in evs) for k, (o, _) in enumerate(ops)}
+        # timed steps: events around the decode only (last op)
+        dk = len(ops) - 1
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            keep = fn()
+        for a, b in evs:
+            for k, (_, f) in enumerate(ops):
+                if k == dk:
+                    a.record()
+                f()
+            b.record()
         torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / args.steps
-        if status.cpu().numpy().any() or not torch.equal(y, x_d):
-            raise SystemExit("batch round trip failed (%s)" % name)
-        L = lens.cpu().numpy()
-        res[name] = dict(ms_per_step=round(dt * 1e3, 4), GBps=round(S * n / dt / 1e9, 2),
-                         stream_pct=round(100 * (1 - L.sum() / (S * n)), 3))
-        del keep
-    klv = kl.cpu().numpy()
-    value = res["single_stage"]["GBps"]
-    return dict(metric=METRIC, value=value, unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-                ms_per_step=res["single_stage"]["ms_per_step"], higher_is_better=True, scaling="weak",
-                vs_baseline=None, dtype="u8", data="synthetic",
-                config=dict(workload=WORKLOAD_TEXT["batch"], name="batch", n_bytes=S * n, chunk_symbols=C,
-                            codecs=["huffman"], step="histogram + KL + batch encode + batch decode"),
-                paths=res, kl_bits=dict(min=float(klv.min()), max=float(klv.max()), mean=float(klv.mean())),
-                roofline=None, cpu_baseline=None)
+        dt = (time.perf_counter() - t0) / steps
+        check(label)
+        L = lens.cpu().numpy().astype(np.int64)
+        moved_dec = S * n + int(L.sum())
+        dec_us = statistics.mean(ev_us(a, b) for a, b in evs)
+        kernels = {}
+        for o, us in per_op.items():
+            kk = dict(us=round(us, 2))
+            if "code" in o and "codebook" not in o and "tables" not in o:
+                kk["hbm_GBps"] = round(moved_dec / us / 1e3, 1)
+                kk["roofline_frac"] = round(moved_dec / us / 1e3 / HBM_PEAK_GBPS, 4)
+            elif o == "byte_histogram":
+                kk["hbm_GBps"] = round(S * n / us / 1e3, 1)
+                kk["roofline_frac"] = round(S * n / us / 1e3 / HBM_PEAK_GBPS, 4)
+            kernels[o] = kk
+        res[label] = dict(ms_per_step=round(dt * 1e3, 4), GBps=round(S * n / dt / 1e9, 2),
+                          stream_pct=round(100 * (1 - L.sum() / (S * n)), 3), kernels=kernels,
+                          decode_roofline=roofline_obj(ops[dk][0], moved_dec, dec_us, None, copy_gbps))
+        per_shard[label] = [round(100 * (1 - int(v) / n), 3) for v in L]
+    klv = kl.cpu().numpy().astype(np.float64)
+    diff = np.array(per_shard["three_stage"]) - np.array(per_shard["single_stage"])
+    ss = res["single_stage"]
+    # the dominant kernel of the single-stage step, with its own event time
+    dom = max(("huffman_encode_batch", "huffman_decode_batch"), key=lambda o: ss["kernels"][o]["us"])
+    roof = ss["decode_roofline"] if dom == "huffman_decode_batch" else roofline_obj(
+        dom, ss["decode_roofline"]["algorithmic_bytes"], ss["kernels"][dom]["us"], None, copy_gbps)
+    roof["traffic"] = load_traffic("decode.hip" if dom.endswith("decode_batch") else "encode.hip", "batch", dom)
+    return dict(value=ss["GBps"], unit="GB/s", steps=steps, warmup=warmup, ms_per_step=ss["ms_per_step"],
+                n_bytes=S * n, chunk_symbols=C, codecs=["huffman"], workload=WORKLOAD_TEXT["batch"],
+                step="single stage: byte_histogram + pmf_kl + batch encode + batch decode (64 shards)",
+                roofline=roof, paths=res,
+                per_shard=dict(kl_bits_vs_average=[round(float(v), 6) for v in klv],
+                               single_stage_stream_pct=per_shard["single_stage"],
+                               three_stage_stream_pct=per_shard["three_stage"],
+                               three_minus_single_pct=dict(mean=round(float(diff.mean()), 4),
+                                                           max=round(float(diff.max()), 4))),
+                kl_bits=dict(min=float(klv.min()), max=float(klv.max()), mean=float(klv.mean())))
 
 
-def run_bf16(args, ec, torch):
+def run_bf16(d, args, ec, torch, steps, warmup, copy_gbps):
     """BF16 exponent coding: one step = bf16_exp_encode + bf16_exp_decode of
     one 64 MiB tensor."""
     import synth
     dev = torch.device("cuda:0")
     w = synth.BF16_WORKLOAD
     n, chunk = w["n"], w["chunk"]
-    x = synth.bf16_draw(w["seed"], n, w["sigma"])
+    x = d["x"]
     table = ec.bf16_exp_table_from_sigma(w["sigma"])
     x_d = torch.from_numpy(x.view(np.int16)).to(dev)
     sets = []
@@ -411,25 +619,20 @@ def run_bf16(args, ec, torch):
         if ev:
             ev[2].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
-    enc_us = statistics.mean(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
-    dec_us = statistics.mean(e[1].elapsed_time(e[2]) * 1e3 for e in evs)
+    enc_us = statistics.mean(ev_us(e[0], e[1]) for e in evs)
+    dec_us = statistics.mean(ev_us(e[1], e[2]) for e in evs)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if args.copy_ref:   # plain copies of the input, for the hardware-counter scale factor
-        dst = torch.empty_like(x_d)
-        for _ in range(5):
-            dst.copy_(sets[-1]["x"])
-        torch.cuda.synchronize()
     if status.cpu().numpy().any():
         raise SystemExit("device status bits set: %s" % status.cpu().numpy())
     for S in sets:
@@ -441,17 +644,36 @@ def run_bf16(args, ec, torch):
     kernels = {o: dict(us=round(u, 2), GBps_uncompressed=round(2 * n / u / 1e3, 1),
                        roofline_frac=round(moved / u / 1e3 / HBM_PEAK_GBPS, 4))
                for o, u in (("bf16_exp_encode", enc_us), ("bf16_exp_decode", dec_us))}
-    return dict(metric=METRIC, value=round(2 * n / (wall / args.steps) / 1e9, 2), unit="GB/s", n_gpus=1,
-                steps=args.steps, warmup=args.warmup, ms_per_step=round(wall / args.steps * 1e3, 4),
-                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="u16", data="synthetic",
-                config=dict(workload=WORKLOAD_TEXT["bf16"], name="bf16", n_bytes=2 * n, chunk_values=chunk,
-                            table=list(table), step="bf16_exp_encode + bf16_exp_decode"),
-                roofline=dict(kernel=dom, bound="hbm", achieved=round(moved / dom_us / 1e3, 1), peak=HBM_PEAK_GBPS,
-                              unit="GB/s", frac=round(moved / dom_us / 1e3 / HBM_PEAK_GBPS, 4),
-                              traffic=load_traffic("bf16exp.hip", "bf16", dom),
-                              algorithmic_bytes=moved, avg_us=round(dom_us, 2)),
-                kernels=kernels, compression=dict(stream_bytes=L, stream_pct=round(100 * (1 - L / (2 * n)), 3)),
-                cpu_baseline=None)
+    return dict(value=round(2 * n / (wall / steps) / 1e9, 2), unit="GB/s", steps=steps, warmup=warmup,
+                ms_per_step=round(wall / steps * 1e3, 4), n_bytes=2 * n, chunk_values=chunk,
+                workload=WORKLOAD_TEXT["bf16"], table=list(table), step="bf16_exp_encode + bf16_exp_decode",
+                roofline=roofline_obj(dom, moved, dom_us, load_traffic("bf16exp.hip", "bf16", dom), copy_gbps),
+                kernels=kernels, compression=dict(stream_bytes=L, stream_pct=round(100 * (1 - L / (2 * n)), 3)))
+
+
+def run_gpu(name, d, args, ec, torch, steps, warmup, copy_gbps):
+    if name == "batch":
+        return run_batch(d, args, ec, torch, steps, warmup, copy_gbps)
+    if name == "bf16":
+        return run_bf16(d, args, ec, torch, steps, warmup, copy_gbps)
+    return run_single(name, d, args, ec, torch, steps, warmup, copy_gbps)
+
+
+def line(name, r, args, cpu):
+    """The one JSON line, headed by workload `name`'s result r."""
+    cfg = dict(workload=r["workload"], name=name, n_bytes=r["n_bytes"], step=r["step"])
+    for k in ("chunk_symbols", "chunk_values", "codecs", "table"):
+        if k in r:
+            cfg[k] = r[k]
+    cfg["buffer_sets"] = args.sets
+    out = dict(metric=METRIC, value=r["value"], unit="GB/s", n_gpus=1, steps=r["steps"], warmup=r["warmup"],
+               ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="u16" if name == "bf16" else "u8", data="synthetic", config=cfg, roofline=r["roofline"])
+    for k in ("kernels", "compression", "paths", "per_shard"):
+        if k in r:
+            out[k] = r[k]
+    out["cpu_baseline"] = cpu.get(name)
+    return out
 
 
 def main():
@@ -460,18 +682,64 @@ def main():
         print("bench.py: this engine runs on one GPU; --gpus %d is not supported (multi-GPU sharding is a "
               "design note only)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    names = [args.workload] if args.workload else CONFIG_ORDER
+    workers = cpu_workers(args)
+
+    # host side first: no GPU state exists yet when the pools fork
+    t = time.perf_counter()
+    data = make_data(names, workers)
+    log(args, "data %.1f s" % (time.perf_counter() - t))
+    cpu = {}
+    if not args.no_cpu:
+        t = time.perf_counter()
+        cpu = cpu_baselines(data, [n for n in names if n != "bf16"], workers)
+        log(args, "cpu baselines %.1f s" % (time.perf_counter() - t))
+
     import torch
     import lossless_entropy_coding_amd as ec
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     ec.lib()
-    if args.workload == "batch":
-        out = run_batch(args, ec, torch)
-    elif args.workload == "bf16":
-        out = run_bf16(args, ec, torch)
+    # the practical ceiling: a plain copy of 64 MiB on the device
+    flat = np.ascontiguousarray(data[names[0]]["x"]).reshape(-1).view(np.uint8)
+    if flat.size >= 1 << 26:
+        probe = torch.from_numpy(flat[:1 << 26].copy()).to("cuda:0")
     else:
-        out = run_single(args, ec, torch)
+        probe = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda:0")
+    copy = copy_ceiling(torch, probe)
+    del probe
+    copy_gbps = copy["GBps"]
+
+    head = args.workload or HEADLINE
+    results = {}
+    for n in names:
+        t = time.perf_counter()
+        full = n == head
+        results[n] = run_gpu(n, data[n], args, ec, torch, args.steps if full else min(args.steps, args.extra_steps),
+                             args.warmup if full else min(args.warmup, 5), copy_gbps)
+        log(args, "%s %.1f s" % (n, time.perf_counter() - t))
+        torch.cuda.empty_cache()
+
+    out = line(head, results[head], args, cpu)
+    out["roofline"]["copy_ceiling"] = copy
+    extra = dict(numpy=np.__version__, copy_ceiling=copy)
+    if not args.workload:
+        confs = {}
+        for n in names:
+            r = dict(results[n])
+            r["cpu_baseline"] = cpu.get(n)
+            confs[n] = r
+        extra["configs"] = confs
+        extra["configs_note"] = ("every workload of the run; the %s entry is the headline above. Per-op times come "
+                                 "from an untimed pass with events around every op; roofline.avg_us from events "
+                                 "around the dominant kernel inside the timed steps" % head)
+    else:
+        r = results[head]
+        for k in ("kl_bits_vs_calibration", "histogram_exact", "codebook_build_us", "avg_pmf_top", "kl_bits"):
+            if k in r:
+                extra[k] = r[k]
+    out["extra"] = extra
     print(json.dumps(out), flush=True)
 
 
