@@ -38,10 +38,15 @@
 //            canonical code limits.
 //   EG       count leading zeros z; the code is 2z + k + 1 bits; rank -> byte
 //            through a 256-entry LDS table.
-// Decoded bytes gather in registers and leave as one whole 128-byte line per
-// lane and half run.  After its last symbol a lane checks that it stopped
-// exactly where the index says its sub-chunk ends, and the lane of a chunk's
-// last sub-chunk checks that the padding after it is zero.
+// Decoded bytes gather in registers, 64 bytes per lane, and leave as whole
+// 64-byte pieces after a turn-around among four lanes, one 16-byte streaming
+// store per refill point (so that a store is never among the memory
+// operations a refill waits for; see the kernel).  The ring path serves waves
+// whose 64 lanes all hold whole sub-chunks; a wave with a shorter or missing
+// sub-chunk (a segment's last run) or an index found corrupt decodes straight
+// from global memory instead.  After its last symbol a lane checks that it
+// stopped exactly where the index says its sub-chunk ends, and the lane of a
+// chunk's last sub-chunk checks that the padding after it is zero.
 #include "dev_common.h"
 
 namespace ec {
@@ -342,7 +347,7 @@ struct LaneTask {
 // Index entries of a lane's sub-chunk as loaded (resolved later, so that the
 // loads are in flight while the wave decodes an earlier run).
 struct IndexRaw {
-    uint64_t co0, co1;        // the lane's chunk: byte offsets of its start and end in the payload
+    uint32_t co0, co1;        // the lane's chunk: offsets of its start and end in the payload, 16-byte units
     uint32_t e_start, e_end;  // the lane's sub-chunk: start and end bit in its chunk
     bool last;                // the sub-chunk is its chunk's last: the padding after it is checked
 };
@@ -360,10 +365,15 @@ __device__ __forceinline__ IndexRaw issue_index(const DecodeArgs &a, const Strea
     const uint32_t gl = g < a.blocks_per_seg ? g : a.blocks_per_seg - 1;
     const uint32_t c = gl / si.spc, j = gl - c * si.spc;
     IndexRaw r;
-    r.co0 = chunk_off[c];
-    r.co1 = chunk_off[c + 1];
+    // offsets are 16-byte aligned and below 2^36 (checked with the header):
+    // kept as 32-bit counts of 16 bytes; a misaligned one reads as corrupt
+    const uint64_t o0 = chunk_off[c], o1 = chunk_off[c + 1];
+    r.co0 = (o0 & 15) || (o0 >> 36) ? 0xffffffffu : (uint32_t)(o0 >> 4);
+    r.co1 = (o1 & 15) || (o1 >> 36) ? 0u : (uint32_t)(o1 >> 4);
     r.e_end = sub_end[(uint64_t)c * si.spc + j];
-    r.e_start = j ? sub_end[(uint64_t)c * si.spc + j - 1] : 0u;
+    // (loaded for every lane, so that the number of loads is fixed)
+    const uint32_t prev = sub_end[(uint64_t)c * si.spc + j - (j ? 1u : 0u)];
+    r.e_start = j ? prev : 0u;
     r.last = j == si.spc - 1 || gl == a.blocks_per_seg - 1;
     return r;
 }
@@ -373,12 +383,12 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
                                             uint32_t *status) {
     const bool active = g < a.blocks_per_seg;
     LaneTask t;
-    t.ok = active && r.co0 <= r.co1 && r.co1 <= si.pb && !(r.co0 & 15) && (uint64_t)r.e_end <= (r.co1 - r.co0) * 8 &&
-           r.e_start <= r.e_end;
+    const uint64_t co0 = (uint64_t)r.co0 * 16, co1 = (uint64_t)r.co1 * 16;
+    t.ok = active && r.co0 <= r.co1 && co1 <= si.pb && (uint64_t)r.e_end <= (co1 - co0) * 8 && r.e_start <= r.e_end;
     if (active && !t.ok) flag(status, EC_S_CORRUPT);
-    t.sb = r.co0 * 8 + r.e_start;
-    t.eb = r.co0 * 8 + r.e_end;
-    t.pad_end = r.last ? r.co1 * 8 : 0;
+    t.sb = co0 * 8 + r.e_start;
+    t.eb = co0 * 8 + r.e_end;
+    t.pad_end = r.last ? co1 * 8 : 0;
     t.first_sym = (uint64_t)g * kSub;
     t.cnt = !active ? 0u : (a.seg_n - t.first_sym < kSub ? (uint32_t)(a.seg_n - t.first_sym) : (uint32_t)kSub);
     const bool live = t.ok && t.cnt > 0 && t.eb > t.sb;
@@ -391,9 +401,10 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
 // (indexes clamped to the lane's last block, or to the payload's first block
 // for lanes with nothing to decode, so every load stays inside the payload).
 template <int K>
-__device__ __forceinline__ void issue_blocks(const StreamInfo &si, const LaneTask &t, uint32_t first, uint4 (&v)[K]) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + t.blk0;
-    const uint32_t last = t.nv ? t.nv - 1 : 0u;
+__device__ __forceinline__ void issue_blocks(const StreamInfo &si, uint32_t blk0, uint32_t nv, uint32_t first,
+                                             uint4 (&v)[K]) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + blk0;
+    const uint32_t last = nv ? nv - 1 : 0u;
     static_for<0, K>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         v[k] = src[min(first + (uint32_t)k, last)];
@@ -423,15 +434,23 @@ __device__ __forceinline__ void write_quarter(uint32_t rbase, uint32_t q, const 
 // (the second clamped to the lane's last block); a lane with no block left
 // there loads the payload's first block instead, the same for every such lane
 // (one request).  Returns the buffer's tag: first, or kNone.
-__device__ __forceinline__ uint32_t issue_batch(const StreamInfo &si, const LaneTask &t, uint32_t first,
+__device__ __forceinline__ uint32_t issue_batch(const StreamInfo &si, uint32_t blk0, uint32_t nv, uint32_t first,
                                                 uint4 (&v)[kBatch]) {
     const uint4 *pay = reinterpret_cast<const uint4 *>(si.stream + si.po);
-    const bool need = first < t.nv;
-    const uint64_t b0 = need ? t.blk0 + first : 0;
-    const uint64_t b1 = need ? t.blk0 + min(first + 1, t.nv - 1) : 0;
+    const bool need = first < nv;
+    const uint32_t b0 = need ? blk0 + first : 0;
+    const uint32_t b1 = need ? blk0 + min(first + 1, nv - 1) : 0;
     v[0] = pay[b0];
     v[1] = pay[b1];
     return need ? first : kNone;
+}
+
+// 16 bytes of decoded output, stored with the streaming (non-temporal) hint:
+// nothing reads them again in this kernel.
+__device__ __forceinline__ void stream_store(uint8_t *p, uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = {x, y, z, w};
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(p));
 }
 
 // Lane i's 64-byte output piece of a run (a half line) as four 16-byte parts
@@ -529,7 +548,9 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
     __shared__ Smem sm;
     const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.h.tabv);
     uint8_t *symtab = sm.h.symtab;
-    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index is uniform: kept in a scalar register, so that run
+    // and stream positions derived from it are too)
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t G = gridDim.x, b = blockIdx.x;
     const uint32_t R = (a.blocks_per_seg + 63) / 64;        // runs per stream
     const bool one_stream = a.n_seg == 1;
@@ -631,22 +652,39 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         const LaneTask L = resolve(a, si, have_next ? next_raw : have_first ? first_raw : issue_index(a, si, g0 + lane),
                                    g0 + lane, status);
         have_first = false;
-        // the first four blocks (past a lane's last block: copies of it),
-        // and the next four in the refill buffers, written at the first two
-        // points (so the ring holds eight blocks after 32 symbols)
-        uint4 f[4];
-        issue_blocks<4>(si, L, 0, f);
-        uint4 bufA[kBatch], bufB[kBatch];
-        uint32_t tagA = issue_batch(si, L, 4, bufA);
-        uint32_t tagB = issue_batch(si, L, 6, bufB);
+        const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
+        const bool full = live && L.cnt == kSub && L.nv > 0;
         // the next task's index entries, in flight during this run
         const uint32_t u1 = u + G;
         const uint32_t run1 = u1 < n_u ? run_of(u1) : R;
         have_next = u1 < n_u && seg_of(u1) == seg && run1 < R;
+        uint8_t *const wave_out = a.out + (uint64_t)seg * a.out_stride + (uint64_t)g0 * kSub;
+        const uint32_t *payload = reinterpret_cast<const uint32_t *>(si.stream + si.po);
+        if (__ballot(full) != ~0ull) {
+            // a segment's last, shorter run, or an index found corrupt: every
+            // live lane decodes from global memory
+            if (have_next) next_raw = issue_index(a, si, run1 * 64 + lane);
+            if (live)
+                decode_rest<CODEC, PAIRS>(L, payload, si.pb, wave_out + lane * kSub, l1, symtab, sm.h.deep,
+                                          seg_max_len, seg_lens, seg_k_eg, status);
+            asm volatile("" ::: "memory");
+            continue;
+        }
+        // what the end of the run needs, relative to the lane's first block
+        const uint32_t blk0 = (uint32_t)L.blk0;   // payloads are below 2^36 bytes
+        const uint32_t nv = L.nv;
+        const uint32_t start = (uint32_t)(L.sb - L.blk0 * 128);
+        const uint32_t want = (uint32_t)(L.eb - L.blk0 * 128);
+        const uint32_t pad_to = L.pad_end > L.eb ? (uint32_t)(L.pad_end - L.blk0 * 128) : 0u;
+        // the first four blocks, then the next task's index, then the next
+        // four blocks in the refill buffers, written at the first two points
+        // (so the ring holds eight blocks after 32 symbols)
+        uint4 f[4];
+        issue_blocks<4>(si, blk0, nv, 0, f);
         if (have_next) next_raw = issue_index(a, si, run1 * 64 + lane);
-
-        const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
-        const bool full = live && L.cnt == kSub && L.nv > 0;
+        uint4 bufA[kBatch], bufB[kBatch];
+        uint32_t tagA = issue_batch(si, blk0, nv, 4, bufA);
+        uint32_t tagB = issue_batch(si, blk0, nv, 6, bufB);
         {
             const uint4 q0[kBatch] = {f[0], f[1]}, q1[kBatch] = {f[2], f[3]};
             write_quarter(rbase, 0, q0);
@@ -656,101 +694,137 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         // each lane reads only its own column: program order suffices
         asm volatile("" ::: "memory");
 
-        uint8_t *dst = a.out + (uint64_t)seg * a.out_stride + L.first_sym;
-        const uint32_t want = (uint32_t)(L.eb - L.blk0 * 128);
         RingBits S;
         S.rbase = rbase;
-        S.Y = 31 + (uint32_t)(L.sb - L.blk0 * 128);
+        S.Y = 31 + start;
         bool over = false;   // the run consumed bits the ring did not hold yet
         uint32_t bad = 0;
-        // A refill point with buffer X (the other one: Y): check the position
-        // against the blocks written; write X if it holds blocks (always the
-        // next ones, with room: see the load condition); reload X with the
-        // next blocks Y does not hold when the ring has room for them now,
-        // and so two points later.
-        auto refill = [&](uint4(&X)[kBatch], uint32_t &tagX, uint32_t tagY) __attribute__((always_inline)) {
-            const uint32_t pos = S.bit();
-            over = over || pos > nb * 128;
-            if (tagX == nb) {
-                // X's loads were issued two points ago; only the other
-                // buffer's two (and, after a group's stores, those) may
-                // still be in flight: wait for vmcnt <= 2 (expcnt and
-                // lgkmcnt left at their maxima)
-                __builtin_amdgcn_s_waitcnt(0x0f72);
-                write_quarter(rbase, (nb >> 1) & 3, X);
-                nb += kBatch;
-            }
-            const uint32_t next = tagY == nb ? nb + kBatch : nb;
-            const bool room = next + kBatch <= (pos >> 7) + kRingBlocks;
-            tagX = issue_batch(si, L, room ? next : kNone, X);
+        // store k of a group's output: lane 4 j + p writes part p of the piece
+        // of lane 4 j + k (see transpose4)
+        const uint32_t part = (lane & ~3u) * kSub + 16 * (lane & 3);
+        constexpr int kOW = 16;   // words per group: a 64-byte piece per lane
+        uint32_t o[kOW];
+        auto store_part = [&](int grp, auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            stream_store(wave_out + part + (4 * kOW * grp + k * kSub), o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
         };
-        // Every lane runs the ring decode (the output lines are written by
-        // the lane's group together); lanes that are not full decode ring
-        // contents that do not matter, and their lines are not stored.
-        const uint64_t full_mask = __ballot(full);
-        uint8_t *wave_dst = a.out + (uint64_t)seg * a.out_stride + (uint64_t)g0 * kSub;
         {
             Codes<CODEC, PAIRS, RingBits> D(S, l1, symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg);
-            // Output words gather in registers, 64 bytes per lane, and leave
-            // as whole 64-byte pieces (see transpose4).
-            constexpr int kOW = 16;   // words per group: a 64-byte piece per lane
+            // A group is 64 symbols: four passes of 16, pass p into o[4 p ..],
+            // each followed by a refill point.  Output leaves one 16-byte store
+            // per point: the previous group's parts 1, 2, 3 at points 0, 1, 2
+            // (before passes 1, 2, 3 reuse their registers), and at point 3,
+            // after the group's turn-around, its own part 0.  Every point so
+            // issues one store and then its two loads, and a buffer's loads
+            // are followed by exactly three memory operations (two before the
+            // first group's stores begin) when its turn comes two points
+            // later: the wait at each point is exact and never covers the
+            // loads or stores of the point just before.
             static_for<0, kSub / (4 * kOW)>([&](auto gc) __attribute__((always_inline)) {
                 constexpr int grp = decltype(gc)::value;
-                uint32_t o[kOW];
-                // 16 symbols -> o[8 i + 4 P ..]; a uniform branch per pass
-                // keeps o in registers
+                // vmcnt <= 2 (expcnt and lgkmcnt left at their maxima): the
+                // other buffer's two loads may still be in flight (a store
+                // may complete after later loads, so stores are not counted)
+                constexpr int kWait = 0x0f72;
+                // 16 symbols -> o[8 i + 4 P ..], chosen by value: every index
+                // into o is a constant (an index chosen at run time would move
+                // o to memory)
                 auto pass = [&](int i, auto pc) __attribute__((always_inline)) {
                     constexpr int P = decltype(pc)::value;
-                    uint32_t w0, w1, w2, w3;
-                    D.eight(w0, w1);
-                    D.eight(w2, w3);
-                    static_for<0, kOW / 8>([&](auto jc) __attribute__((always_inline)) {
-                        constexpr int j = decltype(jc)::value;
-                        if (i == j) {
-                            o[8 * j + 4 * P] = w0;
-                            o[8 * j + 4 * P + 1] = w1;
-                            o[8 * j + 4 * P + 2] = w2;
-                            o[8 * j + 4 * P + 3] = w3;
-                        }
+                    uint32_t w[4];
+                    D.eight(w[0], w[1]);
+                    D.eight(w[2], w[3]);
+                    static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+                        constexpr int k = decltype(kc)::value;
+                        o[4 * P + k] = i == 0 ? w[k] : o[4 * P + k];
+                        o[8 + 4 * P + k] = i == 0 ? o[8 + 4 * P + k] : w[k];
                     });
+                };
+                // A refill point with buffer X (the other one: Y): check the
+                // position against the blocks written; write X if it holds
+                // blocks (always the next ones, with room: see the load
+                // condition); store; reload X with the next blocks Y does not
+                // hold when the ring has room for them now, and so two
+                // points later.
+                auto refill = [&](uint4(&X)[kBatch], uint32_t &tagX, uint32_t tagY, auto &&store)
+                                  __attribute__((always_inline)) {
+                    const uint32_t pos = S.bit();
+                    over = over || pos > nb * 128;
+                    if (tagX == nb) {
+                        __builtin_amdgcn_s_waitcnt(kWait);
+                        write_quarter(rbase, (nb >> 1) & 3, X);
+                        nb += kBatch;
+                    }
+                    store();
+                    const uint32_t next = tagY == nb ? nb + kBatch : nb;
+                    const bool room = next + kBatch <= (pos >> 7) + kRingBlocks;
+                    tagX = issue_batch(si, blk0, nv, room ? next : kNone, X);
+                };
+                // the parts a point may store, read at fixed indexes and
+                // chosen by value (a choice of index would move o to memory)
+                auto part_of = [&](auto kc) __attribute__((always_inline)) {
+                    constexpr int k = decltype(kc)::value;
+                    return make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+                };
+                // one of two parts, chosen word by word
+                auto put = [&](uint32_t off, bool first, const uint4 &v, const uint4 &w) __attribute__((always_inline)) {
+                    stream_store(wave_out + part + off, first ? v.x : w.x, first ? v.y : w.y, first ? v.z : w.z,
+                                 first ? v.w : w.w);
                 };
                 // two passes of 16 symbols per iteration, a refill point
                 // after each: the buffers' turns are fixed in the code
 #pragma nounroll
                 for (int i = 0; i < kOW / 8; ++i) {
                     pass(i, std::integral_constant<int, 0>{});
-                    refill(bufA, tagA, tagB);
+                    refill(bufA, tagA, tagB, [&]() __attribute__((always_inline)) {
+                        if constexpr (grp > 0) {
+                            // the previous group's part 1 (first step) or 3
+                            const uint4 p1 = part_of(std::integral_constant<int, 1>{});
+                            const uint4 p3 = part_of(std::integral_constant<int, 3>{});
+                            put(4 * kOW * (grp - 1) + (i == 0 ? 1 : 3) * kSub, i == 0, p1, p3);
+                        }
+                    });
                     pass(i, std::integral_constant<int, 1>{});
-                    refill(bufB, tagB, tagA);
+                    refill(bufB, tagB, tagA, [&]() __attribute__((always_inline)) {
+                        // first step: the previous group's part 2; second:
+                        // this group, turned around, its part 0
+                        if (i != 0) transpose4(o, lane);
+                        const uint4 p2 = part_of(std::integral_constant<int, 2>{});
+                        const uint4 p0 = part_of(std::integral_constant<int, 0>{});
+                        if (grp > 0 || i != 0) put(i == 0 ? 4 * kOW * (grp - 1) + 2 * kSub : 4 * kOW * grp, i == 0, p2, p0);
+                    });
                 }
-                transpose4(o, lane);
-                // store k: lane 4 j + p writes part p of the piece of lane 4 j + k
-                uint8_t *part = wave_dst + (lane & ~3u) * kSub + 4 * kOW * grp + 16 * (lane & 3);
-                const uint32_t own = (uint32_t)(full_mask >> (lane & ~3u)) & 0xfu;   // the group's full lanes
-                static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
-                    constexpr int k = decltype(kc)::value;
-                    if ((own >> k) & 1)
-                        *reinterpret_cast<uint4 *>(part + k * kSub) =
-                            make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
-                });
             });
+            constexpr int kLast = kSub / (4 * kOW) - 1;
+            store_part(kLast, std::integral_constant<int, 1>{});
+            store_part(kLast, std::integral_constant<int, 2>{});
+            store_part(kLast, std::integral_constant<int, 3>{});
             bad = D.bad;
         }
         const uint32_t end = S.bit();
         over = over || end > nb * 128;
-        bool corrupt = full && !over && ((bad & ~0xffu) || end != want);
+        bool corrupt = !over && ((bad & ~0xffu) || end != want);
         // the zero padding after a chunk's last sub-chunk
-        const bool pad_check = full && !over && !corrupt && L.pad_end > L.eb;
+        const bool pad_check = !over && !corrupt && pad_to != 0;
         if (__ballot(pad_check))
-            if (pad_check) corrupt = padding_set(reinterpret_cast<const uint32_t *>(si.stream + si.po), L.eb, L.pad_end);
-        const bool rest = live && (!full || over);
-        if (__ballot(rest)) {
+            if (pad_check) corrupt = padding_set(payload, (uint64_t)blk0 * 128 + want, (uint64_t)blk0 * 128 + pad_to);
+        if (__ballot(over)) {
             // a lane that outran its ring rewrites the line its group stored
             // for it: the group's stores complete first
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-            if (rest)
-                decode_rest<CODEC, PAIRS>(L, reinterpret_cast<const uint32_t *>(si.stream + si.po), si.pb, dst, l1,
-                                          symtab, sm.h.deep, seg_max_len, seg_lens, seg_k_eg, status);
+            if (over) {
+                LaneTask T;
+                T.sb = (uint64_t)blk0 * 128 + start;
+                T.eb = (uint64_t)blk0 * 128 + want;
+                T.pad_end = pad_to ? (uint64_t)blk0 * 128 + pad_to : 0;
+                T.first_sym = (uint64_t)(g0 + lane) * kSub;
+                T.blk0 = blk0;
+                T.nv = nv;
+                T.cnt = kSub;
+                T.ok = true;
+                decode_rest<CODEC, PAIRS>(T, payload, si.pb, wave_out + lane * kSub, l1, symtab, sm.h.deep,
+                                          seg_max_len, seg_lens, seg_k_eg, status);
+            }
         }
         if (corrupt) flag(status, EC_S_CORRUPT);
         // the ring is rewritten at the next task, after this lane's reads

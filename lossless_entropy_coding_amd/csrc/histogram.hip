@@ -1,14 +1,14 @@
 // Byte histogram and the PMF statistics kernels.
 //
 // Histogram, two launches:
-//   1. histogram_kernel: the workgroups of a segment sweep it together in
-//      rounds of 32 KiB per workgroup, counting into LDS counters; each then
-//      stores its 256 partial counts with plain stores.  Every wave owns 16 columns of 256 counters; lane l adds
-//      into column l & 15, so the counter of byte b is word 16 b + (l & 15):
-//      whatever bytes the 32 lanes of one LDS pass hold, at most two of them
-//      share a bank (random addresses into one shared table, and the skewed
-//      e4m3 distributions where a few bytes dominate, cost several times
-//      more);
+//   1. histogram_kernel: each workgroup of 1024 threads takes whole 128 KiB
+//      pieces of a segment (8 vectors of 16 bytes per thread, all loads in
+//      flight before the first count) and counts them into one table of
+//      32 columns x 256 bins in LDS: lane l adds into column l & 31, so the
+//      32 lanes of one LDS pass always hit 32 different banks and two lanes
+//      of one instruction meet on a counter only when they are l and l + 32
+//      with equal bytes.  The table is then summed over its columns and the
+//      workgroup stores its 256 partial counts (bin-major rows).
 //   2. histogram_reduce_kernel: sums the partial rows of each segment into
 //      the 64-bit counts, one wave per bin.
 // No global atomics: same-address atomics from many workgroups serialise at
@@ -19,24 +19,22 @@ namespace ec {
 
 namespace {
 
-constexpr int kHistThreads = 256;
-constexpr int kHistCols = 16;                          // counter columns per wave (lane & 15)
-constexpr int kHistWaveWords = 256 * kHistCols;        // 16 KiB of counters per wave
-constexpr int kHistRoundVec = 8;                       // 16-byte loads in flight per thread per round
-constexpr uint64_t kHistRound = (uint64_t)kHistRoundVec * kHistThreads;   // vectors per workgroup round
-constexpr int kHistRoundsPerBlock = 4;                 // target rounds per workgroup (128 KiB)
+constexpr int kHistThreads = 1024;
+constexpr int kHistCols = 32;                          // counter columns (lane & 31)
+constexpr int kHistWords = 256 * kHistCols;            // 32 KiB of counters per workgroup
+constexpr int kHistVec = 8;                            // 16-byte loads per thread per piece
+constexpr uint64_t kHistPiece = (uint64_t)kHistVec * kHistThreads;   // vectors per piece (128 KiB)
 
+// Small segments take pieces of one vector per thread (16 KiB), so that
+// they still spread over many compute units.
+template <int V>
 __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
                                                                  uint64_t seg_n, uint64_t in_stride,
                                                                  uint32_t *__restrict__ partial) {
-    constexpr int kWaves = kHistThreads / 64;
-    __shared__ uint4 hv[kWaves * kHistWaveWords / 4];
+    constexpr uint64_t kPiece = (uint64_t)V * kHistThreads;
+    __shared__ uint4 hv[kHistWords / 4];
     uint32_t *h = reinterpret_cast<uint32_t *>(hv);
-    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (uint32_t i = tid; i < kWaves * kHistWaveWords / 4; i += kHistThreads) hv[i] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    // a word takes the bytes of 4 lanes of one workgroup: far below 2^32
-    uint32_t *mine = h + wave * kHistWaveWords + (lane & (kHistCols - 1));
+    const uint32_t tid = threadIdx.x;
 
     const uint32_t seg = blockIdx.y;
     const uint8_t *base = in + (uint64_t)seg * in_stride;
@@ -47,53 +45,64 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
     const uint64_t n_vec = (seg_n - head) / 16;
     const uint64_t tail = (seg_n - head) % 16;
     const uint4 *vp = reinterpret_cast<const uint4 *>(vbase);
-    auto count = [&](const uint4 &q) __attribute__((always_inline)) {
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+
+    // the first piece's loads go out before the table is cleared; lanes past
+    // the end of the segment (last piece only) load its last vector again and
+    // do not count it (unconditional loads keep the waits per load)
+    const uint64_t stride = (uint64_t)gridDim.x * kPiece;
+    uint64_t p0 = (uint64_t)blockIdx.x * kPiece;
+    uint4 q[V];
+    auto load = [&](uint64_t p) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            atomicAdd(&mine[(w[k] & 0xff) * kHistCols], 1u);
-            atomicAdd(&mine[((w[k] >> 8) & 0xff) * kHistCols], 1u);
-            atomicAdd(&mine[((w[k] >> 16) & 0xff) * kHistCols], 1u);
-            atomicAdd(&mine[(w[k] >> 24) * kHistCols], 1u);
+        for (int k = 0; k < V; ++k) {
+            const uint64_t v = p + tid + k * kHistThreads;
+            q[k] = vp[v < n_vec ? v : n_vec - 1];
         }
     };
-    // grid-stride rounds: at any time the workgroups of a segment read one
-    // contiguous window of it; every load of a round is issued before its
-    // first count, and each count waits for its own load only
-    for (uint64_t r0 = (uint64_t)blockIdx.x * kHistRound; r0 < n_vec; r0 += (uint64_t)gridDim.x * kHistRound) {
-        const uint64_t v = r0 + tid;
-        uint4 q[kHistRoundVec];
-        if (r0 + kHistRound <= n_vec) {
+    // counter of byte b in column c: word 32 b + c
+    uint32_t *mine = h + (tid & (kHistCols - 1));
+    auto count = [&](uint32_t w) __attribute__((always_inline)) {
+        atomicAdd(&mine[(w & 0xff) * kHistCols], 1u);
+        atomicAdd(&mine[((w >> 8) & 0xff) * kHistCols], 1u);
+        atomicAdd(&mine[((w >> 16) & 0xff) * kHistCols], 1u);
+        atomicAdd(&mine[(w >> 24) * kHistCols], 1u);
+    };
+    auto count_piece = [&](uint64_t p) __attribute__((always_inline)) {
 #pragma unroll
-            for (int k = 0; k < kHistRoundVec; ++k) q[k] = vp[v + k * kHistThreads];
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < kHistRoundVec; ++k) count(q[k]);
-        } else {   // the segment's last, partial round
-#pragma unroll
-            for (int k = 0; k < kHistRoundVec; ++k) {
-                if (v + k * kHistThreads < n_vec) q[k] = vp[v + k * kHistThreads];
+        for (int k = 0; k < V; ++k) {
+            if (p + tid + k * kHistThreads < n_vec) {
+                count(q[k].x);
+                count(q[k].y);
+                count(q[k].z);
+                count(q[k].w);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < kHistRoundVec; ++k) {
-                if (v + k * kHistThreads < n_vec) count(q[k]);
-            }
+        }
+    };
+    const bool any = p0 < n_vec;
+    if (any) load(p0);
+    for (uint32_t i = tid; i < kHistWords / 4; i += kHistThreads) hv[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    if (any) {
+        count_piece(p0);
+        for (p0 += stride; p0 < n_vec; p0 += stride) {
+            load(p0);
+            count_piece(p0);
         }
     }
     if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid] * kHistCols], 1u);
     if (blockIdx.x == 0 && tid < tail) atomicAdd(&mine[vbase[n_vec * 16 + tid] * kHistCols], 1u);
     __syncthreads();
 
-    // thread t sums byte t over all columns, starting at column t & 15 so
-    // that the lanes of one access spread over the banks
+    // thread t sums eight columns of bin t >> 2 (quarter t & 3), rotated by
+    // the bin so that the 32 lanes of one pass read 32 different banks; the
+    // four quarters are then added across lanes
+    const uint32_t bin = tid >> 2, qtr = tid & 3;
     uint32_t sum = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-#pragma unroll
-        for (int j = 0; j < kHistCols; ++j) sum += h[w * kHistWaveWords + tid * kHistCols + ((j + tid) & (kHistCols - 1))];
-    }
-    partial[((uint64_t)seg * 256 + tid) * gridDim.x + blockIdx.x] = sum;   // bin-major rows
+    for (int j = 0; j < 8; ++j) sum += h[bin * kHistCols + qtr * 8 + ((j + bin) & 7)];
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if (qtr == 0) partial[((uint64_t)seg * 256 + bin) * gridDim.x + blockIdx.x] = sum;   // bin-major rows
 }
 
 // Workgroup (bin, seg), one wave: lane l adds the partial counts of rows
@@ -234,13 +243,21 @@ __global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict_
 
 }  // namespace
 
-// Workgroups per segment: one per kHistRoundsPerBlock rounds of the
-// segment, at most 65536 rows of partial counts over all segments (but at
-// least one per segment).
+// Workgroups per segment: one per piece of the segment (128 KiB, or
+// 16 KiB when the whole launch has fewer than 256 large pieces), at most
+// 4096 rows of partial counts over all segments (but at least one per
+// segment); a workgroup then takes every gridDim.x-th piece of its segment.
+// A workgroup reads at most max(seg_n, n_seg * seg_n / 4096) bytes plus a
+// piece (2^28 for the largest accepted segment), a 32-bit partial count
+// holds that, and one counter sees a 1/32 share of it.
+static bool histogram_small(uint64_t seg_n, uint32_t n_seg) {
+    return (seg_n / 16 + kHistPiece - 1) / kHistPiece * n_seg < 256;
+}
+
 uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
-    const uint64_t rounds = (seg_n / 16 + kHistRound - 1) / kHistRound;
-    uint64_t blocks = (rounds + kHistRoundsPerBlock - 1) / kHistRoundsPerBlock;
-    const uint64_t cap = n_seg < 65536 ? 65536 / n_seg : 1;
+    const uint64_t piece = histogram_small(seg_n, n_seg) ? kHistThreads : kHistPiece;
+    uint64_t blocks = (seg_n / 16 + piece - 1) / piece;
+    const uint64_t cap = n_seg < 4096 ? 4096 / n_seg : 1;
     if (blocks > cap) blocks = cap;
     return blocks ? (uint32_t)blocks : 1u;
 }
@@ -248,8 +265,12 @@ uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
 hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
                             uint64_t *counts, uint32_t *partial, hipStream_t s) {
     const uint32_t blocks = histogram_blocks(seg_n, n_seg);
-    hipLaunchKernelGGL(histogram_kernel, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n, in_stride,
-                       partial);
+    if (histogram_small(seg_n, n_seg))
+        hipLaunchKernelGGL(histogram_kernel<1>, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n, in_stride,
+                           partial);
+    else
+        hipLaunchKernelGGL(histogram_kernel<kHistVec>, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n,
+                           in_stride, partial);
     hipLaunchKernelGGL(histogram_reduce_kernel, dim3(256, n_seg), dim3(64), 0, s, partial, blocks, counts);
     return hipGetLastError();
 }
