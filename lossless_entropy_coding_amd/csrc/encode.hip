@@ -441,7 +441,8 @@ __device__ __forceinline__ void emit_row(const PairCache<ROWS> &cc, int r, uint3
             pos += (cc.pk[r][u >> 2] >> (8 * (u & 3))) & 0xffu;
         });
     } else {
-        const uint4 v = *reinterpret_cast<const uint4 *>(piece);
+        // (a piece past the segment's end reads nothing)
+        const uint4 v = vb ? *reinterpret_cast<const uint4 *>(piece) : make_uint4(0u, 0u, 0u, 0u);
         static_for<0, kPiece>([&](auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             const uint32_t e = (uint32_t)k < vb ? lut32[byte_k<k>(v)] : 0u;
