@@ -42,6 +42,8 @@ struct BuildSmem {
     uint64_t w[256];          // weight by byte; later the code length by byte, as a 64-bit key
     uint64_t sw[256 + 2];     // leaf weights in sorted order (+2 heavy sentinels)
     uint64_t iw[256 + 2];     // merged-node weights in creation order
+    uint32_t sw32[256 + 4];   // the same as 32-bit weights (small shards), +4 heavy sentinels
+    uint32_t iw32[256 + 4];
     uint64_t fcode[48];       // first canonical code of each length
     uint32_t fidx[48];        // first canonical position of each length
     uint32_t blc[64];         // codes of each length
@@ -52,7 +54,7 @@ struct BuildSmem {
     uint8_t sidx[256];        // byte at sorted position
     uint8_t len[256];         // code length by byte
     uint8_t symc[256];        // byte at canonical position
-    uint32_t bad, max_len;
+    uint32_t bad, max_len, wide;
 };
 
 // Rank of (key[s], s) among the 256 pairs (key[j], j) in lexicographic
@@ -63,6 +65,16 @@ __device__ __forceinline__ uint32_t rank256(const uint64_t *key, uint64_t ks, ui
 #pragma unroll 8
     for (uint32_t j = 0; j < 256; ++j) {
         const uint64_t kj = key[j];
+        r += (kj < ks || (kj == ks && j < s)) ? 1u : 0u;
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint32_t rank256_32(const uint32_t *key, uint32_t ks, uint32_t s) {
+    uint32_t r = 0;
+#pragma unroll 8
+    for (uint32_t j = 0; j < 256; ++j) {
+        const uint32_t kj = key[j];
         r += (kj < ks || (kj == ks && j < s)) ? 1u : 0u;
     }
     return r;
@@ -158,6 +170,79 @@ __device__ void canonical_tables(BuildSmem &sm, DevTables *t, uint32_t tid) {
     }
 }
 
+// Step 2 for weights that fit 32 bits, in as few scalar instructions a step
+// as the merge allows (one wave issues an instruction at most every few
+// cycles, so the step's length is its instruction count): the fronts of
+// both queues (L0 L1, Q0 Q1) stay in scalar registers, and the entries
+// that may become fronts next (leaves li + 2, li + 3; merged nodes qh + 2,
+// qh + 3) are read at the start of each step and taken up at its end.  A
+// merged node at or past qt reads as heavy, the one made in the step as its
+// sum.  Same takes as the 64-bit loop: the lighter front, the leaf on a tie.
+__device__ __forceinline__ uint32_t rfl(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ void merge32(BuildSmem &sm) {
+    constexpr uint32_t H = 0xffffffffu;
+    uint32_t li = 0, qh = 0, qt = 0;
+    uint32_t L0 = rfl(sm.sw32[0]), L1 = rfl(sm.sw32[1]), Q0 = H, Q1 = H;
+#pragma unroll 3
+    for (uint32_t k = 0; k < 255; ++k) {
+        const uint32_t l2 = sm.sw32[li + 2], l3 = sm.sw32[li + 3];
+        const uint32_t q2 = sm.iw32[qh + 2], q3 = sm.iw32[qh + 3];
+        uint32_t id0, id1, sum, cl, cq;
+        if (L0 <= Q0) {
+            if (L1 <= Q0) {
+                id0 = li;
+                id1 = li + 1;
+                sum = L0 + L1;
+                cl = 2;
+                cq = 0;
+            } else {
+                id0 = li;
+                id1 = 256 + qh;
+                sum = L0 + Q0;
+                cl = 1;
+                cq = 1;
+            }
+        } else if (L0 <= Q1) {
+            id0 = 256 + qh;
+            id1 = li;
+            sum = Q0 + L0;
+            cl = 1;
+            cq = 1;
+        } else {
+            id0 = 256 + qh;
+            id1 = 256 + qh + 1;
+            sum = Q0 + Q1;
+            cl = 0;
+            cq = 2;
+        }
+        // every lane writes the same values (no branch on the lane)
+        sm.iw32[qt] = sum;
+        sm.par[id0] = (uint16_t)(256 + qt);
+        sm.par[id1] = (uint16_t)(256 + qt);
+        // leaf fronts
+        const uint32_t L2 = rfl(l2), L3 = rfl(l3);
+        if (cl == 1) {
+            L0 = L1;
+            L1 = L2;
+        } else if (cl == 2) {
+            L0 = L2;
+            L1 = L3;
+        }
+        // merged-node fronts at qh + cq and qh + cq + 1 (node qt is new)
+        const uint32_t Q2 = rfl(q2), Q3 = rfl(q3);
+        const uint32_t a = cq, b = cq + 1;   // window offsets, 0..3
+        const uint32_t va = a == 0 ? Q0 : a == 1 ? Q1 : Q2;
+        const uint32_t vb = b == 1 ? Q1 : b == 2 ? Q2 : Q3;
+        const uint32_t pa = qh + a, pb = qh + b;
+        Q0 = pa < qt ? va : pa == qt ? sum : H;
+        Q1 = pb < qt ? vb : pb == qt ? sum : H;
+        li += cl;
+        qh += cq;
+        ++qt;
+    }
+}
+
 __global__ __launch_bounds__(kBuildThreads) void huff_build_kernel(const uint64_t *counts, DevTables *tabs,
                                                                    uint32_t *status) {
     __shared__ BuildSmem sm;
@@ -171,14 +256,33 @@ __global__ __launch_bounds__(kBuildThreads) void huff_build_kernel(const uint64_
     if (tid == 0) {
         sm.bad = 0;
         sm.max_len = 0;
+        sm.wide = 0;
     }
     if (tid < 64) sm.blc[tid] = 0;
     sm.w[tid] = ws;
     __syncthreads();
     if (c >= kMaxCount) sm.bad = 1;
-    const uint32_t r = rank256(sm.w, ws, tid);
+    // counts below 2^23 keep every node weight (at most 256 * 2^23) in 32 bits
+    if (c >= (1ull << 23)) sm.wide = 1;
+    __syncthreads();   // sm.wide settled
+    uint32_t r;
+    if (!sm.wide) {
+        // 32-bit keys (count + 1 below 2^23 + 1): half the compares
+        uint32_t *k32 = reinterpret_cast<uint32_t *>(sm.iw32);   // scratch until the merge
+        k32[tid] = (uint32_t)ws;
+        __syncthreads();
+        r = rank256_32(k32, (uint32_t)ws, tid);
+        __syncthreads();   // the keys are read by all before iw32 is reused
+    } else {
+        r = rank256(sm.w, ws, tid);
+    }
     sm.sw[r] = ws;
+    sm.sw32[r] = (uint32_t)ws;
     sm.sidx[r] = (uint8_t)tid;
+    if (tid < 4) {
+        sm.sw32[256 + tid] = 0xffffffffu;
+        sm.iw32[256 + tid] = 0xffffffffu;
+    }
     if (tid < 2) {
         sm.sw[256 + tid] = kHeavy;
         sm.iw[256 + tid] = kHeavy;
@@ -190,7 +294,10 @@ __global__ __launch_bounds__(kBuildThreads) void huff_build_kernel(const uint64_
     // all it can need: they are read together at the start of the step.
     // Every take finds a node in one of the queues (a step starts with at
     // least two), so li <= 256 and qh < qt whatever the weights.
-    if (wave == 0) {
+    if (wave == 0 && !sm.wide) {
+        merge32(sm);
+        sm.par[kRoot] = (uint16_t)kRoot;
+    } else if (wave == 0) {
         uint32_t li = 0, qh = 0, qt = 0;
         for (uint32_t k = 0; k < 255; ++k) {
             uint64_t l0 = uniform64(sm.sw[li]), l1 = uniform64(sm.sw[li + 1]);
