@@ -39,7 +39,9 @@ def _special_rows():
     rng = np.random.default_rng(7)
     rows = [[0] * 256, [1] * 256, [10 ** 9] + [0] * 255, list(range(256)),
             [int(v) for v in rng.integers(0, 4, 256) * 1000],            # many ties
-            [int(v) for v in rng.integers(0, 1 << 40, 256)]]             # large counts
+            [int(v) for v in rng.integers(0, 1 << 40, 256)],             # large counts
+            # at and just past the largest counts of the builder's 32-bit merge
+            [(1 << 23) - 1] * 256, [(1 << 23) - 1 - 997 * i for i in range(256)], [1 << 23] + [5] * 255]
     for d in (20, 26, 27, 33, 40, 41, 47):
         rows.append([int(c) for c in deep_counts(d)])
     for s in range(12):
