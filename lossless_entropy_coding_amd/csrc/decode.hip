@@ -649,6 +649,13 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             have_next = false;
             continue;
         }
+        // Issue priority follows progress: a wave sets the highest level for
+        // its task's setup and fill, then one level lower for each group of
+        // 64 symbols it finishes.  Without it the SIMD's arbiter favours the
+        // oldest wave, which starves the younger waves' setup while it
+        // decodes (their fills wait up to 15 us) and leaves one wave per
+        // SIMD decoding alone at the end.
+        __builtin_amdgcn_s_setprio(3);
         const LaneTask L = resolve(a, si, have_next ? next_raw : have_first ? first_raw : issue_index(a, si, g0 + lane),
                                    g0 + lane, status);
         have_first = false;
@@ -703,6 +710,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         // of lane 4 j + k (see transpose4)
         const uint32_t part = (lane & ~3u) * kSub + 16 * (lane & 3);
         constexpr int kOW = 16;   // words per group: a 64-byte piece per lane
+        static_assert(kSub / (4 * kOW) <= 4, "one issue priority level per group");
         uint32_t o[kOW];
         auto store_part = [&](int grp, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
@@ -722,6 +730,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             // loads or stores of the point just before.
             static_for<0, kSub / (4 * kOW)>([&](auto gc) __attribute__((always_inline)) {
                 constexpr int grp = decltype(gc)::value;
+                __builtin_amdgcn_s_setprio(3 - grp);
                 // vmcnt <= 2 (expcnt and lgkmcnt left at their maxima): the
                 // other buffer's two loads may still be in flight (a store
                 // may complete after later loads, so stores are not counted)
@@ -801,6 +810,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             store_part(kLast, std::integral_constant<int, 3>{});
             bad = D.bad;
         }
+        __builtin_amdgcn_s_setprio(0);
         const uint32_t end = S.bit();
         over = over || end > nb * 128;
         bool corrupt = !over && ((bad & ~0xffu) || end != want);
@@ -826,7 +836,10 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
                                           seg_max_len, seg_lens, seg_k_eg, status);
             }
         }
-        if (corrupt) flag(status, EC_S_CORRUPT);
+        // one status update per wave (a same-address atomic per lane of a
+        // corrupt stream would serialise 64 times over)
+        const uint64_t bad_lanes = __ballot(corrupt);
+        if (bad_lanes && lane == (uint32_t)__builtin_ctzll(bad_lanes)) flag(status, EC_S_CORRUPT);
         // the ring is rewritten at the next task, after this lane's reads
         asm volatile("" ::: "memory");
     }
