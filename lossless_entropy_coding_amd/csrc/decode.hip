@@ -193,16 +193,16 @@ __device__ __noinline__ bool padding_set(const uint32_t *payload, uint64_t from,
 template <int CODEC, int PAIRS, class Src>
 struct Codes {
     Src &S;
-    const uint16_t *l1;
+    const void *tab;   // QLC: u32 entries; Huffman: u16 entries
     const uint8_t *symtab;
     const DeepTables *dt;
     uint32_t max_len, k_eg;
     uint32_t llo, lhi;   // QLC code lengths by area, one byte each: areas 0-3 in llo, 4-7 in lhi
     uint32_t bad;
 
-    __device__ __forceinline__ Codes(Src &s, const uint16_t *l1_, const uint8_t *symtab_, const DeepTables *dt_,
+    __device__ __forceinline__ Codes(Src &s, const void *tab_, const uint8_t *symtab_, const DeepTables *dt_,
                                      uint32_t max_len_, uint32_t lens, uint32_t k_eg_)
-        : S(s), l1(l1_), symtab(symtab_), dt(dt_), max_len(max_len_), k_eg(k_eg_), llo(0), lhi(0), bad(0) {
+        : S(s), tab(tab_), symtab(symtab_), dt(dt_), max_len(max_len_), k_eg(k_eg_), llo(0), lhi(0), bad(0) {
         if (CODEC == EC_CODEC_QLC) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -222,12 +222,13 @@ struct Codes {
     struct Code {
         uint32_t e, len;
     };
+    __device__ __forceinline__ const uint16_t *hl1() const { return static_cast<const uint16_t *>(tab); }
     __device__ __forceinline__ Code code_at(uint32_t w) {
         if (CODEC == EC_CODEC_QLC) {
             const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, w, 29);   // 0x0c0c0c00 | w >> 29
-            return Code{l1[w >> 21], __builtin_amdgcn_perm(lhi, llo, sel)};
+            return Code{static_cast<const uint32_t *>(tab)[w >> 21], __builtin_amdgcn_perm(lhi, llo, sel)};
         } else if (CODEC == EC_CODEC_HUFFMAN) {
-            uint32_t e = l1[w >> (32 - kHuffBits)];
+            uint32_t e = hl1()[w >> (32 - kHuffBits)];
             if (e == 0u) e = huff_deep(S.win64(), dt, symtab, max_len);
             return Code{e, e & 0xffu};
         } else {
@@ -261,12 +262,12 @@ struct Codes {
             // canonical search and a fresh window for the second code.
             // (shifts take their amount modulo 32: a shift by the entry is
             // a shift by the code's length)
-            uint32_t e1 = l1[w >> (32 - kHuffBits)];
-            uint32_t e2 = l1[(w << (e1 & 31u)) >> (32 - kHuffBits)];
+            uint32_t e1 = hl1()[w >> (32 - kHuffBits)];
+            uint32_t e2 = hl1()[(w << (e1 & 31u)) >> (32 - kHuffBits)];
             if (min(e1, e2) == 0u) {
                 if (e1 == 0u) e1 = huff_deep(S.win64(), dt, symtab, max_len);
                 S.adv(e1 & 0xffu);
-                e2 = l1[S.win() >> (32 - kHuffBits)];
+                e2 = hl1()[S.win() >> (32 - kHuffBits)];
                 if (e2 == 0u) e2 = huff_deep(S.win64(), dt, symtab, max_len);
                 S.adv(e2 & 0xffu);
             } else {
@@ -303,12 +304,12 @@ struct Codes {
         }
         // entries hold the length in their low byte: shifts by an entry (or
         // by the sum of two, for the 64-bit shift, modulo 64) move past the codes
-        const uint32_t e1 = l1[w >> (32 - kHuffBits)];
-        const uint32_t e2 = l1[(w << (e1 & 31u)) >> (32 - kHuffBits)];
+        const uint32_t e1 = hl1()[w >> (32 - kHuffBits)];
+        const uint32_t e2 = hl1()[(w << (e1 & 31u)) >> (32 - kHuffBits)];
         const uint32_t e12 = e1 + e2;   // lengths add in the low byte (at most 26)
         const uint32_t v = (uint32_t)((W << (e12 & 63u)) >> 32);
-        const uint32_t e3 = l1[v >> (32 - kHuffBits)];
-        const uint32_t e4 = l1[(v << (e3 & 31u)) >> (32 - kHuffBits)];
+        const uint32_t e3 = hl1()[v >> (32 - kHuffBits)];
+        const uint32_t e4 = hl1()[(v << (e3 & 31u)) >> (32 - kHuffBits)];
         if (min(min(e1, e2), min(e3, e4)) == 0u) {
             const uint32_t p0 = two(), p1 = two();
             return p0 | (p1 << 16);
@@ -491,7 +492,7 @@ __device__ __forceinline__ void transpose4(uint32_t (&o)[16], uint32_t lane) {
 // (long codes); sub-chunks without bits.
 template <int CODEC, int PAIRS>
 __device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payload, uint64_t pb, uint8_t *dst,
-                                         const uint16_t *l1, const uint8_t *symtab, const DeepTables *dt,
+                                         const void *l1, const uint8_t *symtab, const DeepTables *dt,
                                          uint32_t max_len, uint32_t lens, uint32_t k_eg, uint32_t *status) {
     uint32_t bad = 0;
     uint64_t end_pos = 1, want_pos = 0;
@@ -530,13 +531,13 @@ template <int CODEC, int PAIRS>
 __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const DecodeArgs a) {
     constexpr int kWaves = waves_for<CODEC>();
     constexpr int kThreads = 64 * kWaves;
-    constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 2 / 16
+    constexpr uint32_t kTableVec = CODEC == EC_CODEC_QLC       ? kL1Size * 4 / 16
                                    : CODEC == EC_CODEC_HUFFMAN ? kHuffSize * 2 / 16
                                                                : 1;
     constexpr bool kSym = CODEC != EC_CODEC_QLC;
     constexpr bool kHasDeep = CODEC == EC_CODEC_HUFFMAN;
     struct Head {
-        uint4 tabv[kTableVec];                 // QLC / Huffman decode table
+        uint4 tabv[kTableVec];                 // QLC (u32 entries) / Huffman (u16 entries) decode table
         uint8_t symtab[kSym ? 256 : 4];        // EG: rank -> byte; Huffman: canonical order -> byte
         DeepTables deep[kHasDeep ? 1 : 0];     // Huffman only
     };
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
     };
     static_assert(sizeof(Smem) <= kLdsBytes, "LDS budget");
     __shared__ Smem sm;
-    const uint16_t *l1 = reinterpret_cast<const uint16_t *>(sm.h.tabv);
+    const void *l1 = sm.h.tabv;
     uint8_t *symtab = sm.h.symtab;
     // (the wave index is uniform: kept in a scalar register, so that run
     // and stream positions derived from it are too)
@@ -578,12 +579,15 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         if (seg != cur_seg) {
             __syncthreads();   // the previous segment's tables are no longer read
             tab = seg_tables<DecodeArgs>(seg);
-            constexpr int kTabPer = (kTableVec + kThreads - 1) / kThreads;
+            // the table's 16-bit entries as stored; QLC's are widened to 32
+            // bits in LDS (a 16-bit LDS read costs a mask at every use)
+            constexpr uint32_t kSrcVec = CODEC == EC_CODEC_QLC ? kL1Size * 2 / 16 : kTableVec;
+            constexpr int kTabPer = (kSrcVec + kThreads - 1) / kThreads;
             uint4 tv[kTabPer];
             const uint4 *tsrc = reinterpret_cast<const uint4 *>(CODEC == EC_CODEC_HUFFMAN ? tab->hl1 : tab->l1);
 #pragma unroll
             for (int k = 0; k < kTabPer; ++k) {
-                if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kTableVec) tv[k] = tsrc[tid + k * kThreads];
+                if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kSrcVec) tv[k] = tsrc[tid + k * kThreads];
             }
             const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
             status = a.status ? a.status + seg : nullptr;
@@ -626,7 +630,14 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             if (have_first) first_raw = issue_index(a, si, run0 * 64 + lane);
 #pragma unroll
             for (int k = 0; k < kTabPer; ++k) {
-                if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kTableVec) sm.h.tabv[tid + k * kThreads] = tv[k];
+                const uint32_t i = tid + k * kThreads;
+                if (CODEC == EC_CODEC_QLC && i < kSrcVec) {
+                    const uint4 v = tv[k];
+                    sm.h.tabv[2 * i] = make_uint4(v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16);
+                    sm.h.tabv[2 * i + 1] = make_uint4(v.z & 0xffffu, v.z >> 16, v.w & 0xffffu, v.w >> 16);
+                } else if (CODEC == EC_CODEC_HUFFMAN && i < kSrcVec) {
+                    sm.h.tabv[i] = tv[k];
+                }
             }
             if constexpr (kSym) {
                 if (tid < 256) symtab[tid] = tab->sym[tid];
