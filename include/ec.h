@@ -276,8 +276,19 @@ int entropy_encode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const ui
                          uint32_t embed_lengths, uint8_t *d_out, uint64_t out_stride,
                          uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream);
 
-/* Decode n_seg streams at d_in + s * in_stride (in_stride readable bytes
- * each) into d_out + s * out_stride (seg_n bytes each). */
+/*
+ * The receiving side of entropy_encode_batch: decode n_seg (1..EC_MAX_BATCH)
+ * streams in one launch (single-stage Huffman page, methodology step 4 and
+ * "Practical Implications": every accelerator holds the same precomputed
+ * codebook, so a receiver decodes each shard it gets with cbs[s] and
+ * nothing else; the three-stage path passes each shard's own codebook).
+ * Stream s is read at d_in + s * in_stride (in_stride readable bytes, at
+ * least its length); its seg_n decoded bytes go to d_out + s * out_stride.
+ * cbs[s] must be the codebook stream s was coded with (same codec and id,
+ * else EC_S_CODEBOOK_MISMATCH in d_status[s]).  d_status: device u32[n_seg],
+ * caller-zeroed, or NULL; per-stream bits as for entropy_decode.  No read
+ * leaves [d_in + s * in_stride, + in_stride) for stream s.
+ */
 int entropy_decode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in,
                          uint64_t in_stride, uint8_t *d_out, uint64_t seg_n, uint64_t out_stride,
                          uint32_t *d_status, hipStream_t stream);

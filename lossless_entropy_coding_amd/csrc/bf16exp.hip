@@ -8,9 +8,9 @@
 // read with coalesced stores and loads.
 //
 // Encode, two launches:
-//   1. bf16_encode_kernel (one workgroup per chunk): loads 8 values per
-//      thread and 16-byte load, writes their sign-mantissa bytes (one 8-byte
-//      store) and one byte of each plane, and stages the chunk's escaped
+//   1. bf16_encode_kernel (one workgroup per chunk): each thread takes
+//      pieces of 16 values (two 16-byte loads), writes their sign-mantissa
+//      bytes (one 16-byte store) and two bytes of each plane, and stages the chunk's escaped
 //      exponents, in value order, in scratch (each row's gathered in LDS
 //      first, then stored contiguously); records the chunk's count.
 //   2. bf16_place_kernel (one workgroup per chunk): sums the counts of the
