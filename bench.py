@@ -29,6 +29,7 @@ Prints ONE JSON line.  --workload NAME runs just that workload (profiling).
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
 import multiprocessing as mp
@@ -124,6 +125,23 @@ def roofline_obj(kernel, moved, avg_us, traffic, copy_gbps):
                 frac_of_copy=round(achieved / copy_gbps, 4) if copy_gbps else None)
 
 
+@contextlib.contextmanager
+def fork_pool(n):
+    """A fork pool whose workers leave on their own (close, then join) rather
+    than by SIGTERM: under rocprofv3 a forked worker carries the profiler's
+    signal handler, and a worker terminated by signal can hang in it, which
+    leaves the parent waiting forever in the pool's shutdown."""
+    pool = mp.get_context("fork").Pool(n)
+    try:
+        yield pool
+        pool.close()
+    except BaseException:
+        pool.terminate()
+        raise
+    finally:
+        pool.join()
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -176,7 +194,7 @@ def make_data(names, workers):
             tasks += [("calib", n, s) for s in synth.WORKLOADS[n].calib_seeds]
     # the long draws first, so they do not end up last on one worker
     order = sorted(range(len(tasks)), key=lambda i: tasks[i][0] not in ("x", "bf16"))
-    with mp.get_context("fork").Pool(min(workers, len(tasks))) as pool:
+    with fork_pool(min(workers, len(tasks))) as pool:
         got = pool.map(_gen, [tasks[i] for i in order], chunksize=1)
     res = dict(zip([tasks[i] for i in order], got))
     data = {}
@@ -258,7 +276,7 @@ def cpu_baselines(data, names, workers, sample_bytes=8 << 20):
         plan[n] = (units, unit_bytes)
     out = {}
     model = cpu_model()
-    with mp.get_context("fork").Pool(workers) as pool:
+    with fork_pool(workers) as pool:
         for n in names:
             units, ub = plan[n]
             N = data[n]["x"].size
