@@ -577,8 +577,13 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
     for (uint32_t u = b; u < n_u; u += G) {
         const uint32_t seg = seg_of(u);
         if (seg != cur_seg) {
-            __syncthreads();   // the previous segment's tables are no longer read
-            tab = seg_tables<DecodeArgs>(seg);
+            // Streams coded with the codebook already in LDS (a batch with one
+            // codebook) keep it: no copy and no barrier.  Uniform over the
+            // workgroup.
+            const DevTables *seg_tab = seg_tables<DecodeArgs>(seg);
+            const bool reload = seg_tab != tab;
+            if (reload) __syncthreads();   // the previous segment's tables are no longer read
+            tab = seg_tab;
             // the table's 16-bit entries as stored; QLC's are widened to 32
             // bits in LDS (a 16-bit LDS read costs a mask at every use)
             constexpr uint32_t kSrcVec = CODEC == EC_CODEC_QLC ? kL1Size * 2 / 16 : kTableVec;
@@ -587,7 +592,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             const uint4 *tsrc = reinterpret_cast<const uint4 *>(CODEC == EC_CODEC_HUFFMAN ? tab->hl1 : tab->l1);
 #pragma unroll
             for (int k = 0; k < kTabPer; ++k) {
-                if (CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kSrcVec) tv[k] = tsrc[tid + k * kThreads];
+                if (reload && CODEC != EC_CODEC_EXP_GOLOMB && tid + k * kThreads < kSrcVec) tv[k] = tsrc[tid + k * kThreads];
             }
             const uint8_t *stream = a.in + (uint64_t)seg * a.in_stride;
             status = a.status ? a.status + seg : nullptr;
@@ -628,29 +633,31 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             const uint32_t run0 = run_of(u);
             have_first = seg_ok && run0 < R;
             if (have_first) first_raw = issue_index(a, si, run0 * 64 + lane);
+            if (reload) {
 #pragma unroll
-            for (int k = 0; k < kTabPer; ++k) {
-                const uint32_t i = tid + k * kThreads;
-                if (CODEC == EC_CODEC_QLC && i < kSrcVec) {
-                    const uint4 v = tv[k];
-                    sm.h.tabv[2 * i] = make_uint4(v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16);
-                    sm.h.tabv[2 * i + 1] = make_uint4(v.z & 0xffffu, v.z >> 16, v.w & 0xffffu, v.w >> 16);
-                } else if (CODEC == EC_CODEC_HUFFMAN && i < kSrcVec) {
-                    sm.h.tabv[i] = tv[k];
+                for (int k = 0; k < kTabPer; ++k) {
+                    const uint32_t i = tid + k * kThreads;
+                    if (CODEC == EC_CODEC_QLC && i < kSrcVec) {
+                        const uint4 v = tv[k];
+                        sm.h.tabv[2 * i] = make_uint4(v.x & 0xffffu, v.x >> 16, v.y & 0xffffu, v.y >> 16);
+                        sm.h.tabv[2 * i + 1] = make_uint4(v.z & 0xffffu, v.z >> 16, v.w & 0xffffu, v.w >> 16);
+                    } else if (CODEC == EC_CODEC_HUFFMAN && i < kSrcVec) {
+                        sm.h.tabv[i] = tv[k];
+                    }
                 }
-            }
-            if constexpr (kSym) {
-                if (tid < 256) symtab[tid] = tab->sym[tid];
-            }
-            if constexpr (CODEC == EC_CODEC_HUFFMAN) {
-                constexpr uint32_t kDeep = EC_MAX_CODE_LEN - kHuffBits;
-                if (tid < kDeep) {
-                    sm.h.deep[0].limit[tid] = tab->limit[kHuffBits + 1 + tid];
-                    sm.h.deep[0].first_code[tid] = tab->first_code[kHuffBits + 1 + tid];
-                    sm.h.deep[0].first_idx[tid] = tab->first_idx[kHuffBits + 1 + tid];
+                if constexpr (kSym) {
+                    if (tid < 256) symtab[tid] = tab->sym[tid];
                 }
+                if constexpr (CODEC == EC_CODEC_HUFFMAN) {
+                    constexpr uint32_t kDeep = EC_MAX_CODE_LEN - kHuffBits;
+                    if (tid < kDeep) {
+                        sm.h.deep[0].limit[tid] = tab->limit[kHuffBits + 1 + tid];
+                        sm.h.deep[0].first_code[tid] = tab->first_code[kHuffBits + 1 + tid];
+                        sm.h.deep[0].first_idx[tid] = tab->first_idx[kHuffBits + 1 + tid];
+                    }
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
         if (!seg_ok) continue;   // uniform over the workgroup
 
