@@ -130,10 +130,19 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+# The current stream's raw handle straight from torch's C layer: building a
+# torch.cuda.Stream object for it costs about 3 us a call, more than a kernel
+# launch (public API as the fallback).
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_CUR_DEVICE = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream) -> int | None:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is not None and _CUR_DEVICE is not None:
+        return _RAW_STREAM(_CUR_DEVICE())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _u8_cuda(t: torch.Tensor, name: str):
@@ -496,7 +505,7 @@ def pmf_average(counts: torch.Tensor, out: torch.Tensor | None = None, stream=No
 
 def pmf_kl(p_counts: torch.Tensor, q_counts: torch.Tensor, q_add: int = 0, out: torch.Tensor | None = None,
            stream=None) -> torch.Tensor:
-    p = p_counts.view(-1, 256)
+    p = p_counts if p_counts.dim() == 2 and p_counts.shape[1] == 256 else p_counts.view(-1, 256)
     if out is None:
         out = torch.empty(p.shape[0], dtype=torch.float32, device=p_counts.device)
     _check(lib().pmf_kl(_ptr(p), p.shape[0], _ptr(q_counts), int(q_add), _ptr(out), _stream(stream)), "pmf_kl")
