@@ -317,13 +317,12 @@ def encode(cb: Codebook, x: torch.Tensor, chunk_symbols: int, out: torch.Tensor 
     the stream is out[:out_len] once the stream has synchronised."""
     _u8_cuda(x, "x")
     n = x.numel()
-    dev = x.device
     if out is None:
-        out = torch.empty(max_encoded_bytes(cb, n, chunk_symbols), dtype=torch.uint8, device=dev)
+        out = torch.empty(max_encoded_bytes(cb, n, chunk_symbols), dtype=torch.uint8, device=x.device)
     if out_len is None:
-        out_len = torch.zeros(1, dtype=torch.int64, device=dev)
+        out_len = torch.zeros(1, dtype=torch.int64, device=x.device)
     if status is None:
-        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
     _check(lib().entropy_encode(cb.handle, _ptr(x), n, chunk_symbols, _ptr(out), out.numel(), _ptr(out_len),
                                 _ptr(status), _stream(stream)), "entropy_encode")
     return out, out_len, status
@@ -350,7 +349,7 @@ def decode(cb: Codebook, data: torch.Tensor, n: int, out: torch.Tensor | None = 
         status = torch.zeros(1, dtype=torch.int32, device=data.device)
     _check(lib().entropy_decode(cb.handle, _ptr(data), data.numel() if in_len is None else in_len, _ptr(out), n,
                                 _ptr(status), _stream(stream)), "entropy_decode")
-    return out[:n], status
+    return (out if out.numel() == n else out[:n]), status
 
 
 def _handles(cbs):
@@ -487,11 +486,14 @@ def byte_histogram(x: torch.Tensor, out: torch.Tensor | None = None, stream=None
     """Histogram of each row (2-D) or of the whole tensor (1-D): int64 [S, 256]
     holding the uint64 counts."""
     _u8_cuda(x, "x")
-    x2 = x.view(1, -1) if x.dim() == 1 else x
-    S, seg_n = x2.shape
+    if x.dim() == 1:
+        S, seg_n, stride = 1, x.numel(), x.numel()
+    else:
+        S, seg_n = x.shape
+        stride = x.stride(0)
     if out is None:
         out = torch.empty((S, 256), dtype=torch.int64, device=x.device)
-    _check(lib().byte_histogram(_ptr(x2), seg_n, S, x2.stride(0), _ptr(out), _stream(stream)), "byte_histogram")
+    _check(lib().byte_histogram(_ptr(x), seg_n, S, stride, _ptr(out), _stream(stream)), "byte_histogram")
     return out
 
 
