@@ -41,7 +41,10 @@ def _special_rows():
             [int(v) for v in rng.integers(0, 4, 256) * 1000],            # many ties
             [int(v) for v in rng.integers(0, 1 << 40, 256)],             # large counts
             # at and just past the largest counts of the builder's 32-bit merge
-            [(1 << 23) - 1] * 256, [(1 << 23) - 1 - 997 * i for i in range(256)], [1 << 23] + [5] * 255]
+            [(1 << 22) - 1] * 256, [(1 << 22) - 1 - 997 * i for i in range(256)], [1 << 22] + [5] * 255,
+            [(1 << 23) - 1] * 256, [(1 << 23) - 1 - 997 * i for i in range(256)], [1 << 23] + [5] * 255,
+            # weights growing geometrically (the merge takes new nodes at once)
+            [int(10 ** 6 * 0.7 ** i) for i in range(256)], [int(10 ** 6 * 0.93 ** i) for i in range(256)]]
     for d in (20, 26, 27, 33, 40, 41, 47):
         rows.append([int(c) for c in deep_counts(d)])
     for s in range(12):
