@@ -22,16 +22,17 @@
  *     function and released with ec_codebook_free.  Its device tables are
  *     allocated on the current device at its first GPU use and freed with
  *     the handle.
- *   - The library keeps four scratch buffers per device, allocated with
- *     hipMalloc on first use, grown by doubling and kept until the process
- *     ends: the encoder's chunk sizes (4 bytes per chunk of a launch), the
- *     histogram's partial counts (1 KiB per partial row), and the BF16
- *     encoder's escape counts and staged escapes.  An allocation or growth
- *     inside an asynchronous entry point synchronises the device implicitly
- *     and cannot happen under stream capture: entropy_encode_noalloc takes
- *     none.  GPU calls of the same kind that overlap in time on one device
- *     (different streams) share one buffer and race: order them (one stream,
- *     or events).
+ *   - The library keeps four scratch buffers per device and stream,
+ *     allocated with hipMalloc on first use, grown by doubling and kept
+ *     until the process ends: the encoder's chunk sizes (4 bytes per chunk
+ *     of a launch), the histogram's partial counts (1 KiB per partial row),
+ *     and the BF16 encoder's escape counts and staged escapes.  Calls on one
+ *     stream run in order and share them; calls on different streams do not.
+ *     An allocation or growth inside an asynchronous entry point synchronises
+ *     the device implicitly and cannot happen under stream capture:
+ *     entropy_encode_noalloc takes none.  A stream destroyed while its work
+ *     runs and a new stream that gets the same handle share the buffers:
+ *     let the old work finish first.
  *   - Device codebook tables (the *_device functions) live in caller-owned
  *     device memory: n_seg consecutive tables of ec_device_codebook_bytes()
  *     bytes each, 16-byte aligned.
@@ -447,8 +448,8 @@ uint64_t bf16_exp_max_encoded_bytes(uint64_t n, uint32_t chunk);
  * sections before the escapes; when the escapes do not fit, nothing is
  * written past out_cap, *d_out_len still gets the needed length and
  * EC_S_CAPACITY is OR-ed into *d_status (device u32 or NULL).  Asynchronous
- * on `stream`; uses library scratch (an escape count per chunk and a staging
- * area of chunk bytes per chunk): two encodes in flight on one device race.
+ * on `stream`; uses library scratch of the device and stream (an escape
+ * count per chunk and a staging area of chunk bytes per chunk).
  */
 int bf16_exp_encode(const uint8_t table[7], const uint16_t *d_in, uint64_t n, uint32_t chunk, uint8_t *d_out,
                     uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream);

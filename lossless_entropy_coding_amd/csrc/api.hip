@@ -6,6 +6,7 @@
 #include <cmath>
 #include <mutex>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "dev_common.h"
@@ -24,18 +25,22 @@ constexpr uint64_t kNoAllocChunks = sizeof(scratch) / sizeof(scratch[0]);
 constexpr uint64_t kMaxSegSymbols = 1ull << 33;   // per stream
 constexpr int kMaxDevices = 16;
 
-// Scratch of one device, one buffer per use (so that an encode and a
-// histogram in flight on different streams never share one): the encoder's
-// chunk sizes, the histogram's partial counts, and the BF16 encoder's
-// per-chunk escape counts and staged escapes.  Grown by doubling;
-// retired buffers are kept (a kernel still in flight may use them) until the
-// process ends.
+// Scratch of one device and stream, one buffer per use: the encoder's chunk
+// sizes, the histogram's partial counts, and the BF16 encoder's per-chunk
+// escape counts and staged escapes.  Calls on one stream run in order, so
+// they may share; calls on different streams have buffers of their own.
+// Grown by doubling; retired buffers are kept (a kernel still in flight may
+// use them) until the process ends.
 enum ScratchSlot { kScratchSizes = 0, kScratchHist = 1, kScratchBfCounts = 2, kScratchBfEsc = 3, kScratchSlots = 4 };
+
+struct StreamScratch {
+    void *buf[kScratchSlots] = {};
+    uint64_t bytes[kScratchSlots] = {};
+};
 
 struct DeviceState {
     std::mutex mu;
-    void *buf[kScratchSlots] = {};
-    uint64_t bytes[kScratchSlots] = {};
+    std::unordered_map<hipStream_t, StreamScratch> by_stream;
     std::vector<void *> retired;
 };
 
@@ -47,23 +52,24 @@ int current_device(int *dev) {
     return EC_OK;
 }
 
-// At least `bytes` of scratch `slot` on the current device.
-int device_scratch(int slot, uint64_t bytes, void **out) {
+// At least `bytes` of scratch `slot` for work on `stream` on the current device.
+int device_scratch(int slot, uint64_t bytes, hipStream_t stream, void **out) {
     int dev;
     int rc = current_device(&dev);
     if (rc) return rc;
     DeviceState &d = g_dev[dev];
     std::lock_guard<std::mutex> lock(d.mu);
-    if (bytes > d.bytes[slot]) {
-        uint64_t cap = d.bytes[slot] ? d.bytes[slot] : (1u << 18);
+    StreamScratch &sc = d.by_stream[stream];
+    if (bytes > sc.bytes[slot]) {
+        uint64_t cap = sc.bytes[slot] ? sc.bytes[slot] : (1u << 18);
         while (cap < bytes) cap *= 2;
         void *p = nullptr;
         if (hipMalloc(&p, cap) != hipSuccess) return EC_E_NOMEM;
-        if (d.buf[slot]) d.retired.push_back(d.buf[slot]);
-        d.buf[slot] = p;
-        d.bytes[slot] = cap;
+        if (sc.buf[slot]) d.retired.push_back(sc.buf[slot]);
+        sc.buf[slot] = p;
+        sc.bytes[slot] = cap;
     }
-    *out = d.buf[slot];
+    *out = sc.buf[slot];
     return EC_OK;
 }
 
@@ -192,7 +198,7 @@ int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n
         a.sizes = fixed_sizes;
     } else if (L.n_chunks) {
         void *p = nullptr;
-        int rc = device_scratch(kScratchSizes, L.n_chunks * n_seg * 4, &p);
+        int rc = device_scratch(kScratchSizes, L.n_chunks * n_seg * 4, s, &p);
         if (rc) return rc;
         a.sizes = static_cast<uint32_t *>(p);
     }
@@ -457,7 +463,7 @@ int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t
     if (n_seg > 1 && in_stride < seg_n) return EC_E_INVAL;
     if (seg_n >= (1ull << 40)) return EC_E_UNSUPPORTED;
     void *partial = nullptr;
-    int rc = device_scratch(kScratchHist, (uint64_t)histogram_blocks(seg_n, n_seg) * n_seg * 1024, &partial);
+    int rc = device_scratch(kScratchHist, (uint64_t)histogram_blocks(seg_n, n_seg) * n_seg * 1024, stream, &partial);
     if (rc) return rc;
     return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, static_cast<uint32_t *>(partial), stream));
 }
@@ -564,10 +570,10 @@ int bf16_exp_encode(const uint8_t table[7], const uint16_t *d_in, uint64_t n, ui
     for (int k = 0; k < 7; ++k) a.table[1 + k] = table[k];
     if (L.n_chunks) {
         void *p = nullptr;
-        int rc = device_scratch(kScratchBfCounts, L.n_chunks * 4, &p);
+        int rc = device_scratch(kScratchBfCounts, L.n_chunks * 4, stream, &p);
         if (rc) return rc;
         a.counts = static_cast<uint32_t *>(p);
-        rc = device_scratch(kScratchBfEsc, L.n_chunks * chunk, &p);
+        rc = device_scratch(kScratchBfEsc, L.n_chunks * chunk, stream, &p);
         if (rc) return rc;
         a.esc_tmp = static_cast<uint8_t *>(p);
     }

@@ -266,6 +266,38 @@ def test_encode_is_deterministic(ec):
         assert int(status.item()) == 0 and torch.equal(s, ref)
 
 
+def test_calls_on_two_streams_at_once(ec):
+    """Histograms and encodes enqueued on two streams with no ordering between
+    them (the library's scratch is kept per stream): every result equals the
+    same call made alone."""
+    counts = _calib_counts()
+    cb, _ = _pair(ec, "huffman", counts)
+    xs = [torch.from_numpy(synth.draw(r, 60 + k, (8 << 20) + 4096 * k)).to(DEV) for k, r in enumerate(["ffn1", "grad"])]
+    ref = []
+    for x in xs:
+        out, out_len, status = ec.encode(cb, x, 16384)
+        ref.append(out[: int(out_len.item())].cpu())
+        assert int(status.item()) == 0
+    hist_ref = [stats.histogram(x.cpu().numpy()) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty(ec.max_encoded_bytes(cb, x.numel(), 16384), dtype=torch.uint8, device=DEV) for x in xs]
+    lens = [torch.zeros(1, dtype=torch.int64, device=DEV) for _ in xs]
+    sts = [torch.zeros(1, dtype=torch.int32, device=DEV) for _ in xs]
+    hists = [torch.zeros((1, 256), dtype=torch.int64, device=DEV) for _ in xs]
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                ec.byte_histogram(xs[k], out=hists[k])
+                ec.encode(cb, xs[k], 16384, out=outs[k], out_len=lens[k], status=sts[k])
+        torch.cuda.synchronize()
+        for k in range(2):
+            L = int(lens[k].item())
+            assert int(sts[k].item()) == 0 and L == ref[k].numel(), (rep, k)
+            assert torch.equal(outs[k][:L].cpu(), ref[k]), (rep, k)
+            assert np.array_equal(hists[k].cpu().numpy()[0].astype(np.uint64), hist_ref[k]), (rep, k)
+
+
 @pytest.mark.parametrize("segs,seg_n", [(1, 1000), (3, 4 << 20), (8, 12345), (2, 1 << 16)])
 def test_histogram_matches_oracle(ec, segs, seg_n):
     x = np.stack([synth.draw("ffn2", 50 + s, seg_n) for s in range(segs)])
