@@ -152,6 +152,21 @@ def test_unusable_table_is_flagged(ec):
         assert torch.equal(y[i], x_d[i])
 
 
+def test_counts_at_the_64_bit_weight_limit(ec):
+    """A count of 2^55 or more could overflow the 64-bit node weights: the
+    builder flags the row and leaves its table unusable; a count just below
+    builds the host's table."""
+    rows = [[1 << 55] + [0] * 255, [(1 << 55) - 1] + [3] * 255, [0] * 255 + [(1 << 60) + 7]]
+    tables, status = ec.build_huffman_device(torch.tensor(rows, dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    tb = tables.cpu().numpy()
+    assert status.cpu().numpy().tolist() == [ec.S_BAD_CODEBOOK, 0, ec.S_BAD_CODEBOOK]
+    assert not tb[0].any() and not tb[2].any()
+    assert tb[1].tobytes() == ec.Codebook.huffman(rows[1]).export()
+    ora = cbm.huffman_codebook(rows[1])
+    assert parse_table(tb[1].tobytes())["code_len"] == ora.length
+
+
 @pytest.mark.parametrize("codec", ["qlc", "qlc_adapted", "eg", "eg8", "huffman"])
 def test_uploaded_host_tables(ec, codec):
     """Host-built codebooks exported and uploaded as a device table array
