@@ -263,6 +263,21 @@ int entropy_decode(const ec_codebook *cb, const uint8_t *d_in, uint64_t in_len,
                    uint8_t *d_out, uint64_t n, uint32_t *d_status, hipStream_t stream);
 
 /*
+ * entropy_encode with the chunk sizes already made by byte_histogram_sized
+ * for this codebook, input and chunk_symbols (its d_sizes row for cb): no
+ * sizing pass, the input is read once.  The stream is the one
+ * entropy_encode makes.
+ *   d_sizes   device u32[ceil(n / chunk_symbols)], 4-byte aligned; read only
+ *   Codebooks whose codes exceed 26 bits, or chunks of more than 16384
+ *   symbols: EC_E_UNSUPPORTED.  A chunk whose size differs from the one its
+ *   packer computes (sizes made for another codebook or input) sets
+ *   EC_S_CODEBOOK_MISMATCH; the stream is then unusable.
+ */
+int entropy_encode_sized(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols,
+                         const uint32_t *d_sizes, uint8_t *d_out, uint64_t out_cap, uint64_t *d_out_len,
+                         uint32_t *d_status, hipStream_t stream);
+
+/*
  * Encode n_seg (1..EC_MAX_BATCH) segments of seg_n bytes in one launch.
  * Segment s is read at d_in + s * in_stride and coded with cbs[s] (all
  * entries may be the same handle: single-stage path; or one per shard:
@@ -276,6 +291,17 @@ int entropy_encode_batch(const ec_codebook *const *cbs, uint32_t n_seg, const ui
                          uint64_t seg_n, uint64_t in_stride, uint32_t chunk_symbols,
                          uint32_t embed_lengths, uint8_t *d_out, uint64_t out_stride,
                          uint64_t *d_out_len, uint32_t *d_status, hipStream_t stream);
+
+/*
+ * entropy_encode_batch with caller-made chunk sizes, as entropy_encode_sized:
+ * d_sizes[s][c] is the size of segment s's chunk c under cbs[s] (with one
+ * codebook for every segment, its d_sizes block from byte_histogram_sized).
+ */
+int entropy_encode_batch_sized(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in,
+                               uint64_t seg_n, uint64_t in_stride, uint32_t chunk_symbols,
+                               uint32_t embed_lengths, const uint32_t *d_sizes, uint8_t *d_out,
+                               uint64_t out_stride, uint64_t *d_out_len, uint32_t *d_status,
+                               hipStream_t stream);
 
 /*
  * The receiving side of entropy_encode_batch: decode n_seg (1..EC_MAX_BATCH)
@@ -391,6 +417,26 @@ int entropy_decode_batch_device(const void *d_tables, uint32_t codec, uint32_t n
  */
 int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
                    uint64_t *d_counts, hipStream_t stream);
+
+/*
+ * byte_histogram that, in the same pass over the input, also sizes the
+ * chunks an encode of each segment would make with each of n_cb (1..4)
+ * codebooks.  The single-stage design fixes the codebooks before the data
+ * is seen (single-stage Huffman page, TL;DR and method steps 2-4; QLC page,
+ * section 2: fixed tables), so the pass that gathers the statistics can also
+ * add up the code lengths; entropy_encode_sized then reads the input once.
+ *   d_in           16-byte aligned; in_stride a multiple of 16 (n_seg > 1)
+ *   chunk_symbols  a power of two, 256..16384 (32768 and 65536 too when the
+ *                  launch is large); every seg_n a multiple of 16.  Other
+ *                  shapes: EC_E_UNSUPPORTED (use byte_histogram and
+ *                  entropy_encode).
+ *   d_sizes        device u32[n_cb][n_seg][ceil(seg_n / chunk_symbols)]:
+ *                  chunk sizes in 16-byte units, overwritten
+ * d_counts as for byte_histogram.
+ */
+int byte_histogram_sized(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
+                         uint64_t *d_counts, const ec_codebook *const *cbs, uint32_t n_cb,
+                         uint32_t chunk_symbols, uint32_t *d_sizes, hipStream_t stream);
 
 /*
  * Average PMF of n_seg count rows (single-stage Huffman page, TL;DR and

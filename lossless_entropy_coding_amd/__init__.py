@@ -22,7 +22,7 @@ __all__ = [
     "S_BAD_CODEBOOK", "EXPORTS", "device_codebook_bytes", "build_huffman_device", "own_max_encoded_bytes",
     "encode_batch_device", "decode_batch_device", "huffman_tables_from_streams", "qlc_optimal_area_layout",
     "bf16_exp_table_from_counts", "bf16_exp_table_from_sigma", "bf16_exp_max_encoded_bytes", "bf16_exp_encode",
-    "bf16_exp_decode",
+    "bf16_exp_decode", "byte_histogram_sized", "encode_sized", "encode_batch_sized",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libec.so")
@@ -60,6 +60,9 @@ EXPORTS = {
     "entropy_encode": (_int, [_vp, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]),
     "entropy_encode_noalloc": (_int, [_vp, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]),
     "entropy_decode": (_int, [_vp, _vp, _u64, _vp, _u64, _vp, _vp]),
+    "entropy_encode_sized": (_int, [_vp, _vp, _u64, _u32, _vp, _vp, _u64, _vp, _vp, _vp]),
+    "entropy_encode_batch_sized": (_int, [ctypes.POINTER(_vp), _u32, _vp, _u64, _u64, _u32, _u32, _vp, _vp, _u64,
+                                          _vp, _vp, _vp]),
     "entropy_encode_batch": (_int, [ctypes.POINTER(_vp), _u32, _vp, _u64, _u64, _u32, _u32, _vp, _u64, _vp,
                                     _vp, _vp]),
     "entropy_decode_batch": (_int, [ctypes.POINTER(_vp), _u32, _vp, _u64, _vp, _u64, _u64, _vp, _vp]),
@@ -71,6 +74,7 @@ EXPORTS = {
     "entropy_encode_batch_device": (_int, [_vp, _u32, _vp, _u64, _u64, _u32, _u32, _vp, _u64, _vp, _vp, _vp]),
     "entropy_decode_batch_device": (_int, [_vp, _u32, _u32, _vp, _u64, _vp, _u64, _u64, _vp, _vp]),
     "byte_histogram": (_int, [_vp, _u64, _u32, _u64, _vp, _vp]),
+    "byte_histogram_sized": (_int, [_vp, _u64, _u32, _u64, _vp, ctypes.POINTER(_vp), _u32, _u32, _vp, _vp]),
     "pmf_average": (_int, [_vp, _u32, _vp, _vp]),
     "pmf_kl": (_int, [_vp, _u32, _vp, _u32, _vp, _vp]),
     "bf16_exp_table_from_counts": (_int, [_u64p, _u8p]),
@@ -328,6 +332,25 @@ def encode(cb: Codebook, x: torch.Tensor, chunk_symbols: int, out: torch.Tensor 
     return out, out_len, status
 
 
+def encode_sized(cb: Codebook, x: torch.Tensor, chunk_symbols: int, sizes: torch.Tensor,
+                 out: torch.Tensor | None = None, out_len: torch.Tensor | None = None,
+                 status: torch.Tensor | None = None, stream=None):
+    """entropy_encode_sized: entropy_encode with the chunk sizes that
+    byte_histogram_sized made for cb (its int32 row, ceil(n / chunk_symbols)
+    entries).  Returns (out, out_len, status)."""
+    _u8_cuda(x, "x")
+    n = x.numel()
+    if out is None:
+        out = torch.empty(max_encoded_bytes(cb, n, chunk_symbols), dtype=torch.uint8, device=x.device)
+    if out_len is None:
+        out_len = torch.zeros(1, dtype=torch.int64, device=x.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=x.device)
+    _check(lib().entropy_encode_sized(cb.handle, _ptr(x), n, chunk_symbols, _ptr(sizes), _ptr(out), out.numel(),
+                                      _ptr(out_len), _ptr(status), _stream(stream)), "entropy_encode_sized")
+    return out, out_len, status
+
+
 def encode_noalloc(cb: Codebook, x: torch.Tensor, chunk_symbols: int, out: torch.Tensor,
                    out_len: torch.Tensor, status: torch.Tensor | None = None, stream=None):
     """entropy_encode_noalloc: entropy_encode into caller buffers, with no
@@ -377,6 +400,29 @@ def encode_batch(cbs, x: torch.Tensor, chunk_symbols: int, embed_lengths: bool =
     _check(lib().entropy_encode_batch(_handles(cbl), S, _ptr(x), seg_n, x.stride(0), chunk_symbols,
                                       int(embed_lengths), _ptr(out), out.stride(0), _ptr(out_len), _ptr(status),
                                       _stream(stream)), "entropy_encode_batch")
+    return out, out_len, status
+
+
+def encode_batch_sized(cbs, x: torch.Tensor, chunk_symbols: int, sizes: torch.Tensor, embed_lengths: bool = False,
+                       out: torch.Tensor | None = None, out_len: torch.Tensor | None = None,
+                       status: torch.Tensor | None = None, stream=None):
+    """entropy_encode_batch_sized: entropy_encode_batch with chunk sizes
+    [S, chunks] (int32) from byte_histogram_sized."""
+    _u8_cuda(x, "x")
+    S, seg_n = x.shape
+    cbl = [cbs] * S if isinstance(cbs, Codebook) else list(cbs)
+    if out is None:
+        stride = max(max_encoded_bytes(c, seg_n, chunk_symbols, embed_lengths) for c in cbl)
+        stride = (stride + 255) // 256 * 256
+        out = torch.empty((S, stride), dtype=torch.uint8, device=x.device)
+    if out_len is None:
+        out_len = torch.zeros(S, dtype=torch.int64, device=x.device)
+    if status is None:
+        status = torch.zeros(S, dtype=torch.int32, device=x.device)
+    _check(lib().entropy_encode_batch_sized(_handles(cbl), S, _ptr(x), seg_n, x.stride(0), chunk_symbols,
+                                            int(embed_lengths), _ptr(sizes), _ptr(out), out.stride(0),
+                                            _ptr(out_len), _ptr(status), _stream(stream)),
+           "entropy_encode_batch_sized")
     return out, out_len, status
 
 
@@ -495,6 +541,29 @@ def byte_histogram(x: torch.Tensor, out: torch.Tensor | None = None, stream=None
         out = torch.empty((S, 256), dtype=torch.int64, device=x.device)
     _check(lib().byte_histogram(_ptr(x), seg_n, S, stride, _ptr(out), _stream(stream)), "byte_histogram")
     return out
+
+
+def byte_histogram_sized(x: torch.Tensor, cbs, chunk_symbols: int, out: torch.Tensor | None = None,
+                         sizes: torch.Tensor | None = None, stream=None):
+    """byte_histogram of each row (2-D) or of the whole tensor (1-D) that also
+    makes, for each codebook of cbs (1..4), the chunk sizes an encode with
+    chunk_symbols makes.  Returns (counts int64 [S, 256], sizes int32
+    [n_cb, S, chunks])."""
+    _u8_cuda(x, "x")
+    if x.dim() == 1:
+        S, seg_n, stride = 1, x.numel(), x.numel()
+    else:
+        S, seg_n = x.shape
+        stride = x.stride(0)
+    cbl = [cbs] if isinstance(cbs, Codebook) else list(cbs)
+    chunks = (seg_n + chunk_symbols - 1) // chunk_symbols
+    if out is None:
+        out = torch.empty((S, 256), dtype=torch.int64, device=x.device)
+    if sizes is None:
+        sizes = torch.empty((len(cbl), S, max(chunks, 1)), dtype=torch.int32, device=x.device)
+    _check(lib().byte_histogram_sized(_ptr(x), seg_n, S, stride, _ptr(out), _handles(cbl), len(cbl), chunk_symbols,
+                                      _ptr(sizes), _stream(stream)), "byte_histogram_sized")
+    return out, sizes
 
 
 def pmf_average(counts: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

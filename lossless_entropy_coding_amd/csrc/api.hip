@@ -145,10 +145,13 @@ const DevTables *dev_table(const uint8_t *base, uint32_t i) {
 
 // fixed_sizes: chunk-size scratch the caller provides (fixed_chunks entries;
 // the codebook tables must then already be resident), else library scratch.
+// given_sizes: the chunk sizes themselves, made by byte_histogram_sized (no
+// sizes launch).
 int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
                 uint64_t in_stride, uint32_t C, uint32_t embed, uint8_t *d_out, uint64_t out_stride,
                 uint64_t out_cap, uint64_t *d_out_len, uint32_t *d_status, hipStream_t s,
-                uint32_t *fixed_sizes = nullptr, uint64_t fixed_chunks = 0) {
+                uint32_t *fixed_sizes = nullptr, uint64_t fixed_chunks = 0,
+                const uint32_t *given_sizes = nullptr) {
     if ((!ts.cbs && !ts.dev) || n_seg == 0 || n_seg > EC_MAX_BATCH || !d_out || !d_out_len || !chunk_ok(C))
         return EC_E_INVAL;
     if (seg_n > kMaxSegSymbols || (seg_n && !d_in) || !aligned16(ts.dev)) return EC_E_INVAL;
@@ -193,7 +196,13 @@ int encode_impl(TableSrc ts, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n
     a.sub_at = (uint32_t)L.sub_at;
     a.embed_lengths = embed ? 1 : 0;
     a.max_len = max_len;
-    if (L.n_chunks && fixed_sizes) {
+    if (given_sizes) {
+        if (ts.dev) return EC_E_INVAL;
+        if (!encode_sized_supported(C, max_len)) return EC_E_UNSUPPORTED;
+        if ((uintptr_t)given_sizes & 3) return EC_E_INVAL;
+        a.sized = 1;
+        a.sizes = const_cast<uint32_t *>(given_sizes);   // only read
+    } else if (L.n_chunks && fixed_sizes) {
         if (L.n_chunks * n_seg > fixed_chunks) return EC_E_UNSUPPORTED;
         a.sizes = fixed_sizes;
     } else if (L.n_chunks) {
@@ -389,6 +398,24 @@ int entropy_encode_noalloc(const ec_codebook *cb, const uint8_t *d_in, uint64_t 
                        d_status, stream, sizes, kNoAllocChunks);
 }
 
+int entropy_encode_sized(const ec_codebook *cb, const uint8_t *d_in, uint64_t n, uint32_t chunk_symbols,
+                         const uint32_t *d_sizes, uint8_t *d_out, uint64_t out_cap, uint64_t *d_out_len,
+                         uint32_t *d_status, hipStream_t stream) {
+    if (!d_sizes && n) return EC_E_INVAL;
+    const ec_codebook *cbs[1] = {cb};
+    return encode_impl(TableSrc{cbs, nullptr}, 1, d_in, n, 0, chunk_symbols, 0, d_out, 0, out_cap, d_out_len,
+                       d_status, stream, nullptr, 0, n ? d_sizes : nullptr);
+}
+
+int entropy_encode_batch_sized(const ec_codebook *const *cbs, uint32_t n_seg, const uint8_t *d_in, uint64_t seg_n,
+                               uint64_t in_stride, uint32_t chunk_symbols, uint32_t embed_lengths,
+                               const uint32_t *d_sizes, uint8_t *d_out, uint64_t out_stride, uint64_t *d_out_len,
+                               uint32_t *d_status, hipStream_t stream) {
+    if (!cbs || (!d_sizes && seg_n)) return EC_E_INVAL;
+    return encode_impl(TableSrc{cbs, nullptr}, n_seg, d_in, seg_n, in_stride, chunk_symbols, embed_lengths, d_out,
+                       out_stride, out_stride, d_out_len, d_status, stream, nullptr, 0, seg_n ? d_sizes : nullptr);
+}
+
 int entropy_decode(const ec_codebook *cb, const uint8_t *d_in, uint64_t in_len, uint8_t *d_out, uint64_t n,
                    uint32_t *d_status, hipStream_t stream) {
     const ec_codebook *cbs[1] = {cb};
@@ -465,7 +492,37 @@ int byte_histogram(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t
     void *partial = nullptr;
     int rc = device_scratch(kScratchHist, (uint64_t)histogram_blocks(seg_n, n_seg) * n_seg * 1024, stream, &partial);
     if (rc) return rc;
-    return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, static_cast<uint32_t *>(partial), stream));
+    return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, static_cast<uint32_t *>(partial),
+                                   nullptr, stream));
+}
+
+int byte_histogram_sized(const uint8_t *d_in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride, uint64_t *d_counts,
+                         const ec_codebook *const *cbs, uint32_t n_cb, uint32_t chunk_symbols, uint32_t *d_sizes,
+                         hipStream_t stream) {
+    if (!d_counts || n_seg == 0 || n_seg > 65535 || (seg_n && !d_in)) return EC_E_INVAL;
+    if (!cbs || n_cb == 0 || n_cb > kMaxSizeCodebooks || !d_sizes || ((uintptr_t)d_sizes & 3)) return EC_E_INVAL;
+    if (!chunk_ok(chunk_symbols)) return EC_E_INVAL;
+    if (n_seg > 1 && (in_stride < seg_n || in_stride % 16)) return EC_E_INVAL;
+    if (!aligned16(d_in)) return EC_E_INVAL;
+    if (seg_n > kMaxSegSymbols) return EC_E_UNSUPPORTED;
+    if (!histogram_can_size(seg_n, n_seg, chunk_symbols)) return EC_E_UNSUPPORTED;
+    ChunkSizeArgs cs;
+    memset(&cs, 0, sizeof(cs));
+    for (uint32_t i = 0; i < n_cb; ++i) {
+        if (!cbs[i]) return EC_E_INVAL;
+        int rc = device_tables(cbs[i], &cs.tabs[i]);
+        if (rc) return rc;
+    }
+    cs.sizes = d_sizes;
+    cs.n_cb = n_cb;
+    cs.vc_log2 = (uint32_t)__builtin_ctz(chunk_symbols / 16);
+    cs.chunks_per_seg = (uint32_t)((seg_n + chunk_symbols - 1) / chunk_symbols);
+    void *partial = nullptr;
+    int rc = device_scratch(kScratchHist, (uint64_t)histogram_blocks(seg_n, n_seg, true) * n_seg * 1024, stream,
+                            &partial);
+    if (rc) return rc;
+    return hip_rc(launch_histogram(d_in, seg_n, n_seg, in_stride, d_counts, static_cast<uint32_t *>(partial), &cs,
+                                   stream));
 }
 
 int pmf_average(const uint64_t *d_counts, uint32_t n_seg, float *d_pmf, hipStream_t stream) {

@@ -76,6 +76,8 @@ struct EncodeArgs {
                               // the header and the index tail (no separate offsets launch)
     uint32_t staged_rows;     // 1: the staged packer packs a chunk that overflows its stage row by row
                               // in the stage itself (the row packer then skips such chunks)
+    uint32_t sized;           // 1: sizes come from the caller (a histogram pass made them): no sizes
+                              // launch; the packer writes sub_end[] and checks its chunk's size
     const DevTables *tabs[EC_MAX_BATCH];
 };
 
@@ -119,11 +121,32 @@ hipError_t launch_bf16_encode(const BfArgs &a, hipStream_t s);
 hipError_t launch_bf16_decode(const BfDecArgs &a, hipStream_t s);
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s);
+// Whether an encode with caller-made sizes can run: every chunk then goes
+// through the staged packer (codes of up to kNarrowMaxLen bits from tables
+// the host has read, chunks of up to four rows).
+bool encode_sized_supported(uint32_t chunk_symbols, uint32_t max_len);
 hipError_t launch_decode(const DecodeArgs &a, uint32_t codec, uint32_t max_len, hipStream_t s);
-// Partial-count rows per segment of a histogram launch (uint32 x 256 each).
-uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg);
+// Chunk sizes made by the histogram's pass over the input: for each of n_cb
+// codebooks, the size in 16-byte units that an encode with chunk_symbols =
+// 16 << vc_log2 gives every chunk (what its sizes launch would write).
+constexpr uint32_t kMaxSizeCodebooks = 4;
+struct ChunkSizeArgs {
+    const DevTables *tabs[kMaxSizeCodebooks];
+    uint32_t *sizes;          // [n_cb][n_seg][chunks_per_seg]
+    uint32_t n_cb;            // 1..kMaxSizeCodebooks
+    uint32_t vc_log2;         // log2 of the 16-byte vectors of a chunk
+    uint32_t chunks_per_seg;
+};
+
+// Partial-count rows per segment of a histogram launch (uint32 x 256 each),
+// without or with chunk sizes.
+uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg, bool sized = false);
+// Whether a histogram launch can also make the chunk sizes for chunks of
+// chunk_symbols: a power of two that divides the launch's pieces, with
+// every segment a whole number of 16-byte vectors.
+bool histogram_can_size(uint64_t seg_n, uint32_t n_seg, uint32_t chunk_symbols);
 hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
-                            uint64_t *counts, uint32_t *partial, hipStream_t s);
+                            uint64_t *counts, uint32_t *partial, const ChunkSizeArgs *cs, hipStream_t s);
 hipError_t launch_huff_build(const uint64_t *counts, uint32_t n_seg, DevTables *tabs, uint32_t *status,
                              hipStream_t s);
 hipError_t launch_huff_tables_from_streams(const uint8_t *in, uint64_t in_stride, uint64_t in_len,

@@ -21,7 +21,11 @@
 //      chunk at its offset with coalesced stores.
 // Every chunk knows its place before it is packed, so no workgroup ever
 // waits on another one: the launches need no co-residency, tickets or
-// spinning, at the price of reading the input twice.
+// spinning, at the price of reading the input twice.  When the sizes come
+// from the caller (made by the histogram's pass over the same input, see
+// histogram.hip), launch 1 is skipped: the packer writes the sub_end[]
+// entries and checks its chunk's size against the one it was given, and the
+// input is read once by the encode.
 #include "dev_common.h"
 
 namespace ec {
@@ -118,6 +122,20 @@ __device__ __forceinline__ uint32_t scan_pieces(const uint32_t (&plen)[ROWS], ui
 
 // ---------------------------------------------------------------- 1. sizes
 
+// sub_end[]: the end bit of every 256-symbol sub-chunk, written by the
+// thread holding the sub-chunk's last piece
+template <int ROWS>
+__device__ __forceinline__ void write_sub_end(const EncodeArgs &a, const ChunkPos &p, uint32_t tid,
+                                              const uint32_t (&excl)[ROWS], const uint32_t (&plen)[ROWS]) {
+    const uint32_t spc = a.chunk_symbols / kSub;
+    uint32_t *sub_end = reinterpret_cast<uint32_t *>(p.out + a.sub_at) + (uint64_t)p.lc * spc;
+    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        const uint32_t q = (uint32_t)r * kThreads + tid;
+        if ((tid & 15) == 15 && q < a.chunk_symbols / kPiece) sub_end[q >> 4] = excl[r] + plen[r];
+    });
+}
+
 template <int ROWS>
 __global__ __launch_bounds__(kThreads) void encode_sizes_kernel(const EncodeArgs a) {
     __shared__ uint8_t len8[256];
@@ -148,14 +166,7 @@ __global__ __launch_bounds__(kThreads) void encode_sizes_kernel(const EncodeArgs
     });
     uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
     const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
-    // sub_end[]: written by the thread holding a sub-chunk's last piece
-    const uint32_t spc = a.chunk_symbols / kSub;
-    uint32_t *sub_end = reinterpret_cast<uint32_t *>(p.out + a.sub_at) + (uint64_t)p.lc * spc;
-    static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
-        constexpr int r = decltype(rc)::value;
-        const uint32_t q = (uint32_t)r * kThreads + tid;
-        if ((tid & 15) == 15 && q < a.chunk_symbols / kPiece) sub_end[q >> 4] = excl[r] + plen[r];
-    });
+    write_sub_end<ROWS>(a, p, tid, excl, plen);
     if (tid == 0) a.sizes[blockIdx.x] = (chunk_bits + 127) >> 7;
 }
 
@@ -536,6 +547,13 @@ __global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const E
     uint32_t excl[ROWS], row_start[ROWS], row_bits[ROWS];
     const uint32_t chunk_bits = scan_pieces<ROWS>(plen, lane, wave, wave_tot, excl, row_start, row_bits);
     const uint32_t units = (chunk_bits + 127) >> 7;
+    if (a.sized) {
+        // what the sizes launch would have written; a size that differs from
+        // the chunk's own (made for another codebook or input) is flagged
+        write_sub_end<ROWS>(a, p, tid, excl, plen);
+        if (tid == 0 && units != a.sizes[blockIdx.x])
+            or_status(a.status ? a.status + p.seg : nullptr, EC_S_CODEBOOK_MISMATCH);
+    }
     const uint64_t dst_at = chunk_dst(a, p, units, placed);
     // uniform over the workgroup: a chunk that does not fit is packed row by
     // row, here or (without staged_rows) by the row packer that follows
@@ -639,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void encode_pack_rows_kernel(const Encode
 template <int ROWS>
 hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t s) {
     EncodeArgs a = a_in;
-    hipLaunchKernelGGL((encode_sizes_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), 0, s, a);
+    if (!a.sized) hipLaunchKernelGGL((encode_sizes_kernel<ROWS>), dim3(n_chunks), dim3(kThreads), 0, s, a);
     // short streams: the first pack launch places the chunks itself
     const bool place = a.chunks_per_seg <= kPlaceMaxChunks;
     a.place_in_pack = place ? 1u : 0u;
@@ -677,6 +695,14 @@ hipError_t launch_chunks(const EncodeArgs &a_in, uint32_t n_chunks, hipStream_t 
 }
 
 }  // namespace
+
+bool encode_sized_supported(uint32_t chunk_symbols, uint32_t max_len) {
+    if (chunk_symbols > 4 * (uint32_t)kRowSyms || max_len > (uint32_t)kNarrowMaxLen) return false;
+    // the staged packer takes every chunk (the same test as launch_chunks)
+    const uint32_t worst = ((chunk_symbols * max_len + 127) / 128 + 1) * 16;
+    const uint32_t stage = worst < kStageCap ? worst : kStageCap;
+    return worst <= kStageCap || (kRowSyms * max_len / 32 + 8) * 4 <= stage;
+}
 
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t s) {
     const uint32_t n_chunks = a.n_seg * a.chunks_per_seg;

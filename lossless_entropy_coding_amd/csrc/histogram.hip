@@ -13,6 +13,18 @@
 //      the 64-bit counts, one wave per bin.
 // No global atomics: same-address atomics from many workgroups serialise at
 // the memory side.
+//
+// With chunk sizes (the single-stage design fixes the codebooks before the
+// data is seen, so the pass that counts the bytes can also size the chunks
+// an encode will make): a second LDS table in the counters' layout holds,
+// for byte b, the code lengths of the codebooks (up to two: at bits 0 and
+// 16, so that sums need no unpacking; up to four: one byte each), read at
+// the counter's own address plus a constant.  Each 16-byte vector's lengths
+// add up in 16-bit halves of one or two registers, the wave adds
+// its lanes' sums when its 64 vectors lie in one chunk (else every lane adds
+// its own), and per-chunk totals gather in LDS; after each piece they are
+// stored as 16-byte units.  A chunk is a power of two of vectors that
+// divides a piece, so no chunk spans two workgroups.
 #include "dev_common.h"
 
 namespace ec {
@@ -25,16 +37,38 @@ constexpr int kHistWords = 256 * kHistCols;            // 32 KiB of counters per
 constexpr int kHistVec = 8;                            // 16-byte loads per thread per piece
 constexpr uint64_t kHistPiece = (uint64_t)kHistVec * kHistThreads;   // vectors per piece (128 KiB)
 
+// With chunk sizes the large pieces are half as long (64 KiB): the per-byte
+// length reads need registers that eight vectors in flight would take.
+constexpr int kHistVecSized = 4;
+constexpr uint64_t kSizedPiece = (uint64_t)kHistVecSized * kHistThreads;
+constexpr uint32_t kMaxPieceChunks = kSizedPiece / 16;   // chunks of 256 symbols in a piece
+
+// The counters, then the length table in the same layout (word 32 b + c):
+// a counter and its length word are one address apart by a constant, so a
+// byte's address serves both (the LDS instructions' offset field).
+struct SizeSmem {
+    uint4 cnt[kHistWords / 4];
+    uint32_t len[kHistWords];
+    uint32_t acc[kMaxSizeCodebooks][kMaxPieceChunks];   // bits per chunk of the piece
+};
+
 // Small segments take pieces of one vector per thread (16 KiB), so that
 // they still spread over many compute units.
-template <int V>
-__global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *__restrict__ in,
+// (two workgroups per CU: at most 64 VGPRs)
+// NCB: 0 (counts only), 2 or 4 (chunk sizes for up to that many codebooks)
+template <int V, int NCB>
+__global__ __launch_bounds__(kHistThreads, 8) void histogram_kernel(const uint8_t *__restrict__ in,
                                                                  uint64_t seg_n, uint64_t in_stride,
-                                                                 uint32_t *__restrict__ partial) {
+                                                                 uint32_t *__restrict__ partial,
+                                                                 const ChunkSizeArgs cs) {
     constexpr uint64_t kPiece = (uint64_t)V * kHistThreads;
-    __shared__ uint4 hv[kHistWords / 4];
+    constexpr bool SIZES = NCB != 0;
+    __shared__ typename std::conditional<SIZES, SizeSmem, uint4[kHistWords / 4]>::type smem;
+    uint4 *hv;
+    if constexpr (SIZES) hv = smem.cnt;
+    else hv = smem;
     uint32_t *h = reinterpret_cast<uint32_t *>(hv);
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     const uint32_t seg = blockIdx.y;
     const uint8_t *base = in + (uint64_t)seg * in_stride;
@@ -67,26 +101,119 @@ __global__ __launch_bounds__(kHistThreads) void histogram_kernel(const uint8_t *
         atomicAdd(&mine[((w >> 16) & 0xff) * kHistCols], 1u);
         atomicAdd(&mine[(w >> 24) * kHistCols], 1u);
     };
+    // with sizes: eight bytes at a time, their length words are read first,
+    // then their counters bumped, then the lengths summed into ev
+    // (codebooks 0, 2) and od (1, 3), 16 bits each.  A wave's LDS operations
+    // complete in order, so waiting for the reads never waits for the
+    // counters' atomics issued after them (interleaved, every use would wait
+    // for all of them).
+    auto count_sized = [&](uint32_t wa, uint32_t wb, uint32_t &ev, uint32_t &od) __attribute__((always_inline)) {
+        if constexpr (SIZES) {
+            uint32_t e[8], idx[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) idx[j] = (((j < 4 ? wa : wb) >> (8 * (j & 3))) & 0xffu) * kHistCols;
+            const uint32_t *lmine = smem.len + (tid & (kHistCols - 1));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) e[j] = lmine[idx[j]];
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < 8; ++j) atomicAdd(&mine[idx[j]], 1u);
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (NCB == 2) {
+                    ev += e[j];                                // codebook 0 in bits 0-7, 1 in bits 16-23
+                } else {
+                    ev += e[j] & 0x00ff00ffu;                  // codebooks 0, 2
+                    od += (e[j] >> 8) & 0x00ff00ffu;           // codebooks 1, 3
+                }
+            }
+        }
+    };
+    // a chunk's share of the sums
+    auto add_acc = [&](uint32_t cl, uint32_t ev, uint32_t od) __attribute__((always_inline)) {
+        if constexpr (NCB == 2) {
+            atomicAdd(&smem.acc[0][cl], ev & 0xffffu);
+            if (cs.n_cb > 1) atomicAdd(&smem.acc[1][cl], ev >> 16);
+        } else if constexpr (NCB == 4) {
+            atomicAdd(&smem.acc[0][cl], ev & 0xffffu);
+            if (cs.n_cb > 1) atomicAdd(&smem.acc[1][cl], od & 0xffffu);
+            if (cs.n_cb > 2) atomicAdd(&smem.acc[2][cl], ev >> 16);
+            if (cs.n_cb > 3) atomicAdd(&smem.acc[3][cl], od >> 16);
+        }
+    };
     auto count_piece = [&](uint64_t p) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            if (p + tid + k * kHistThreads < n_vec) {
-                count(q[k].x);
-                count(q[k].y);
-                count(q[k].z);
-                count(q[k].w);
+            const uint64_t gv = p + tid + k * kHistThreads;
+            if constexpr (!SIZES) {
+                if (gv < n_vec) {
+                    count(q[k].x);
+                    count(q[k].y);
+                    count(q[k].z);
+                    count(q[k].w);
+                }
+            } else {
+                uint32_t ev = 0, od = 0;
+                if (gv < n_vec) {
+                    count_sized(q[k].x, q[k].y, ev, od);
+                    count_sized(q[k].z, q[k].w, ev, od);
+                }
+                // this vector's chunk within the piece
+                const uint32_t c0 = (uint32_t)(p >> cs.vc_log2);
+                if (cs.vc_log2 >= 6) {
+                    // the wave's 64 vectors lie in one chunk: the wave adds
+                    // its lanes (at most 64 * 16 * 40 bits a half)
+                    ev = __builtin_amdgcn_readlane(wave_incl_scan(ev), 63);
+                    if constexpr (NCB == 4) od = __builtin_amdgcn_readlane(wave_incl_scan(od), 63);
+                    const uint64_t gw = p + wave * 64 + k * kHistThreads;   // the wave's first vector
+                    if (lane == 0 && gw < n_vec) add_acc((uint32_t)(gw >> cs.vc_log2) - c0, ev, od);
+                } else if (gv < n_vec) {
+                    add_acc((uint32_t)(gv >> cs.vc_log2) - c0, ev, od);
+                }
             }
+        }
+    };
+    // the piece's chunk sizes, stored once its counts are in (then cleared
+    // for the next piece)
+    auto store_sizes = [&](uint64_t p) __attribute__((always_inline)) {
+        if constexpr (SIZES) {
+            __syncthreads();
+            const uint32_t cpp = (uint32_t)(kPiece >> cs.vc_log2), c0 = (uint32_t)(p >> cs.vc_log2);
+            for (uint32_t t = tid; t < cpp * cs.n_cb; t += kHistThreads) {
+                const uint32_t cb = t / cpp, cl = t - cb * cpp;
+                if (c0 + cl < cs.chunks_per_seg)
+                    cs.sizes[((uint64_t)cb * gridDim.y + seg) * cs.chunks_per_seg + c0 + cl] = (smem.acc[cb][cl] + 127) >> 7;
+                smem.acc[cb][cl] = 0;
+            }
+            __syncthreads();
         }
     };
     const bool any = p0 < n_vec;
     if (any) load(p0);
     for (uint32_t i = tid; i < kHistWords / 4; i += kHistThreads) hv[i] = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (SIZES) {
+        // byte b's lengths, one byte per codebook, in every column
+        const uint32_t b = tid >> 2;
+        uint32_t word = 0;
+#pragma unroll
+        for (uint32_t cb = 0; cb < (uint32_t)NCB; ++cb)
+            if (cb < cs.n_cb) word |= (uint32_t)cs.tabs[cb]->code_len[b] << (8 * cb);
+        // two codebooks: the second length moves to bits 16-23, so that a
+        // sum over bytes needs no unpacking
+        if constexpr (NCB == 2) word = (word & 0xffu) | (word & 0xff00u) << 8;
+#pragma unroll
+        for (uint32_t c = 0; c < 8; ++c) smem.len[b * kHistCols + 8 * (tid & 3) + c] = word;
+        for (uint32_t i = tid; i < kMaxSizeCodebooks * kMaxPieceChunks; i += kHistThreads) (&smem.acc[0][0])[i] = 0;
+    }
     __syncthreads();
     if (any) {
         count_piece(p0);
+        store_sizes(p0);
         for (p0 += stride; p0 < n_vec; p0 += stride) {
             load(p0);
             count_piece(p0);
+            store_sizes(p0);
         }
     }
     if (blockIdx.x == 0 && tid < head) atomicAdd(&mine[base[tid] * kHistCols], 1u);
@@ -243,8 +370,9 @@ __global__ __launch_bounds__(256) void pmf_kl_kernel(const uint64_t *__restrict_
 
 }  // namespace
 
-// Workgroups per segment: one per piece of the segment (128 KiB, or
-// 16 KiB when the whole launch has fewer than 256 large pieces), at most
+// Workgroups per segment: one per piece of the segment (128 KiB, 64 KiB with
+// chunk sizes, or 16 KiB when the whole launch has fewer than 256 pieces of
+// 128 KiB), at most
 // 4096 rows of partial counts over all segments (but at least one per
 // segment); a workgroup then takes every gridDim.x-th piece of its segment.
 // A workgroup reads at most max(seg_n, n_seg * seg_n / 4096) bytes plus a
@@ -254,8 +382,14 @@ static bool histogram_small(uint64_t seg_n, uint32_t n_seg) {
     return (seg_n / 16 + kHistPiece - 1) / kHistPiece * n_seg < 256;
 }
 
-uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
-    const uint64_t piece = histogram_small(seg_n, n_seg) ? kHistThreads : kHistPiece;
+bool histogram_can_size(uint64_t seg_n, uint32_t n_seg, uint32_t chunk_symbols) {
+    const uint64_t piece_bytes = 16 * (histogram_small(seg_n, n_seg) ? (uint64_t)kHistThreads : kSizedPiece);
+    return chunk_symbols >= 256 && (chunk_symbols & (chunk_symbols - 1)) == 0 && piece_bytes % chunk_symbols == 0 &&
+           seg_n % 16 == 0;
+}
+
+uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg, bool sized) {
+    const uint64_t piece = histogram_small(seg_n, n_seg) ? kHistThreads : sized ? kSizedPiece : kHistPiece;
     uint64_t blocks = (seg_n / 16 + piece - 1) / piece;
     const uint64_t cap = n_seg < 4096 ? 4096 / n_seg : 1;
     if (blocks > cap) blocks = cap;
@@ -263,14 +397,22 @@ uint32_t histogram_blocks(uint64_t seg_n, uint32_t n_seg) {
 }
 
 hipError_t launch_histogram(const uint8_t *in, uint64_t seg_n, uint32_t n_seg, uint64_t in_stride,
-                            uint64_t *counts, uint32_t *partial, hipStream_t s) {
-    const uint32_t blocks = histogram_blocks(seg_n, n_seg);
-    if (histogram_small(seg_n, n_seg))
-        hipLaunchKernelGGL(histogram_kernel<1>, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n, in_stride,
-                           partial);
-    else
-        hipLaunchKernelGGL(histogram_kernel<kHistVec>, dim3(blocks, n_seg), dim3(kHistThreads), 0, s, in, seg_n,
-                           in_stride, partial);
+                            uint64_t *counts, uint32_t *partial, const ChunkSizeArgs *cs, hipStream_t s) {
+    const uint32_t blocks = histogram_blocks(seg_n, n_seg, cs != nullptr);
+    const ChunkSizeArgs none = {};
+    const bool small = histogram_small(seg_n, n_seg);
+    const dim3 grid(blocks, n_seg), wg(kHistThreads);
+    if (cs && cs->n_cb <= 2) {
+        if (small) hipLaunchKernelGGL((histogram_kernel<1, 2>), grid, wg, 0, s, in, seg_n, in_stride, partial, *cs);
+        else hipLaunchKernelGGL((histogram_kernel<kHistVecSized, 2>), grid, wg, 0, s, in, seg_n, in_stride, partial, *cs);
+    } else if (cs) {
+        if (small) hipLaunchKernelGGL((histogram_kernel<1, 4>), grid, wg, 0, s, in, seg_n, in_stride, partial, *cs);
+        else hipLaunchKernelGGL((histogram_kernel<kHistVecSized, 4>), grid, wg, 0, s, in, seg_n, in_stride, partial, *cs);
+    } else if (small) {
+        hipLaunchKernelGGL((histogram_kernel<1, 0>), grid, wg, 0, s, in, seg_n, in_stride, partial, none);
+    } else {
+        hipLaunchKernelGGL((histogram_kernel<kHistVec, 0>), grid, wg, 0, s, in, seg_n, in_stride, partial, none);
+    }
     hipLaunchKernelGGL(histogram_reduce_kernel, dim3(256, n_seg), dim3(64), 0, s, partial, blocks, counts);
     return hipGetLastError();
 }
