@@ -322,6 +322,55 @@ def make_codebook(ec, name, counts):
     raise KeyError(name)
 
 
+class GpuEvent:
+    """A HIP event recorded on torch's current stream (the stream every
+    library call here runs on), created without the system-scope fence
+    (hipEventDisableSystemFence).  torch.cuda.Event records with that fence:
+    each record then held the GPU idle for about 5 us between two kernels in
+    the profiled steps, which the timed step would count."""
+    _hip = None
+    _flags = 0x20000000   # hipEventDisableSystemFence (timing stays enabled)
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            import ctypes
+            import lossless_entropy_coding_amd as ec
+            ec.lib()
+            rts = [p for p in ec._hip_runtimes_mapped() if os.path.exists(p)]
+            if len(rts) != 1:
+                raise SystemExit("expected one mapped HIP runtime, found %s" % rts)
+            h = ctypes.CDLL(rts[0])   # the runtime torch and libec already use
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._e = ctypes.c_void_p()
+        if self._rt().hipEventCreateWithFlags(ctypes.byref(self._e), self._flags) != 0:
+            raise SystemExit("hipEventCreateWithFlags failed")
+
+    def record(self):
+        import lossless_entropy_coding_amd as ec
+        if self._rt().hipEventRecord(self._e, ec._stream(None)) != 0:   # torch's current stream
+            raise SystemExit("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self._rt().hipEventElapsedTime(ctypes.byref(ms), self._e, end._e) != 0:
+            raise SystemExit("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._e:
+            self._hip.hipEventDestroy(self._e)
+
+
 def ev_us(a, b):
     return a.elapsed_time(b) * 1e3
 
@@ -336,7 +385,7 @@ def copy_ceiling(torch, x_d, reps=30, pairs=3):
     for i in range(2 * pairs):
         dsts[i % pairs].copy_(srcs[i % pairs])
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    evs = [(GpuEvent(), GpuEvent()) for _ in range(reps)]
     for i, (a, b) in enumerate(evs):
         a.record()
         dsts[i % pairs].copy_(srcs[i % pairs])
@@ -428,7 +477,7 @@ def run_single(name, d, args, ec, torch, steps, warmup, copy_gbps):
             rec(4 + 2 * j)
 
     def new_events():
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(steps)]
+        return [[GpuEvent() for _ in range(nops + 1)] for _ in range(steps)]
 
     for i in range(warmup):
         step(sets[i % len(sets)])
@@ -471,7 +520,7 @@ def run_single(name, d, args, ec, torch, steps, warmup, copy_gbps):
         for j, cb in enumerate(cbs):
             B = S["bufs"][j]
             ref, ref_len, _ = ec.encode(cb, S["x"], C)
-            evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            evs2 = [(GpuEvent(), GpuEvent()) for _ in range(steps)]
             for a, b in evs2:
                 a.record()
                 ec.encode(cb, S["x"], C, out=ref, out_len=ref_len)
@@ -593,7 +642,7 @@ def run_batch(d, args, ec, torch, steps, warmup, copy_gbps):
                 f()
         torch.cuda.synchronize()
         # per-op breakdown (untimed pass, events around every op)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)]
+        evs = [[GpuEvent() for _ in range(len(ops) + 1)] for _ in range(steps)]
         for e in evs:
             for k, (_, f) in enumerate(ops):
                 e[k].record()
@@ -604,7 +653,7 @@ def run_batch(d, args, ec, torch, steps, warmup, copy_gbps):
         per_op = {o: statistics.mean(ev_us(e[k], e[k + 1]) for e in evs) for k, (o, _) in enumerate(ops)}
         # timed steps: events around the decode only (last op)
         dk = len(ops) - 1
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        evs = [(GpuEvent(), GpuEvent()) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for a, b in evs:
@@ -685,7 +734,7 @@ def run_bf16(d, args, ec, torch, steps, warmup, copy_gbps):
     for i in range(warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[GpuEvent() for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
