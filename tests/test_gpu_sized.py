@@ -143,6 +143,18 @@ def test_workgroups_of_several_pieces(ec):
             assert np.array_equal(sz[j, s], _oracle_sizes(x[s], oras[j], C)), (j, s)
 
 
+def test_empty_input(ec):
+    counts = _counts("ffn1")
+    cb = ec.Codebook.huffman(counts)
+    x = torch.zeros(16, dtype=torch.uint8, device=DEV)[:0]
+    hist, sizes = ec.byte_histogram_sized(x, [cb], 4096)
+    out, out_len, status = ec.encode_sized(cb, x, 4096, sizes[0, 0])
+    torch.cuda.synchronize()
+    assert not hist.any() and int(status.item()) == 0
+    assert out[: int(out_len.item())].cpu().numpy().tobytes() == st.encode_stream(
+        np.zeros(0, np.uint8), cbm.huffman_codebook(counts), 4096)
+
+
 def test_sizes_of_another_codebook_are_flagged(ec):
     counts = _counts("ffn1")
     cb_q, cb_h = ec.Codebook.qlc(counts), ec.Codebook.huffman(counts)
