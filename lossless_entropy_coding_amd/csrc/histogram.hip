@@ -119,14 +119,15 @@ __global__ __launch_bounds__(kHistThreads, 8) void histogram_kernel(const uint8_
 #pragma unroll
             for (int j = 0; j < 8; ++j) atomicAdd(&mine[idx[j]], 1u);
             asm volatile("" ::: "memory");
+            if constexpr (NCB == 2) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if constexpr (NCB == 2) {
-                    ev += e[j];                                // codebook 0 in bits 0-7, 1 in bits 16-23
-                } else {
-                    ev += e[j] & 0x00ff00ffu;                  // codebooks 0, 2
-                    od += (e[j] >> 8) & 0x00ff00ffu;           // codebooks 1, 3
-                }
+                for (int j = 0; j < 8; ++j) ev += e[j];   // codebook 0 in bits 0-7, 1 in bits 16-23
+            } else {
+                // one byte per codebook: six lengths of at most 40 bits sum
+                // within a byte, so bytes are split only twice per eight
+                const uint32_t r1 = e[0] + e[1] + e[2] + e[3] + e[4] + e[5], r2 = e[6] + e[7];
+                ev += (r1 & 0x00ff00ffu) + (r2 & 0x00ff00ffu);                 // codebooks 0, 2
+                od += ((r1 >> 8) & 0x00ff00ffu) + ((r2 >> 8) & 0x00ff00ffu);   // codebooks 1, 3
             }
         }
     };
