@@ -13,18 +13,19 @@
 // bit position is one read of two rows plus a funnel shift, and the 64 lanes
 // of a read always hit 64 different banks.  Rows 32 and 33 repeat rows 0 and
 // 1, so a window that reaches past row 31 reads on without wrapping.  A run
-// starts with its first four blocks in the ring and the next four in two
-// register buffers of two blocks, which take turns at uniform refill points
-// every 16 symbols: a lane writes the turn's buffer into its ring if it
-// holds blocks, then reloads it with its next two blocks not already in the
-// other buffer when the ring will have room for them two points later (else
-// it loads one block that all such lanes share: one request).  So a buffer's
-// blocks are always written at its next turn, two points (32 symbols) after
-// their loads were issued, and every point issues the same two load
-// instructions: the wave waits for the loads of two points before, never for
-// the ones just issued, nothing is fetched twice, and a wave starts decoding
-// as soon as its first four blocks arrive.  Ring addresses are taken modulo the ring, so no read ever leaves
-// the region, whatever the data.  A lane that consumed bits the ring did not
+// starts with its ring full, eight blocks a lane loaded by lane quads (four
+// lanes read 64 consecutive bytes of one lane's sub-chunk per load and write
+// them into that lane's column).  Two register buffers of two blocks then
+// take turns at uniform refill points every 16 symbols: a lane writes the
+// turn's buffer into its ring if it holds blocks, then reloads it with its
+// next two blocks not already in the other buffer when the ring will have
+// room for them two points later (else it loads one block that all such
+// lanes share: one request).  So a buffer's blocks are always written at its
+// next turn, two points (32 symbols) after their loads were issued, and
+// every point issues the same two load instructions: the wave waits for the
+// loads of two points before, never for the ones just issued, and nothing is
+// fetched twice.  Ring addresses are taken modulo the ring, so no read ever
+// leaves the region, whatever the data.  A lane that consumed bits the ring did not
 // yet hold (more than 16 bits a symbol for 32 symbols: long codes only)
 // decodes its run again from global memory afterwards.
 //   QLC      the 3-bit prefix gives the code length through a funnel shift
@@ -398,17 +399,49 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
     return t;
 }
 
-// Blocks first .. first + K - 1 of a lane's sub-chunk, loaded into registers
-// (indexes clamped to the lane's last block, or to the payload's first block
-// for lanes with nothing to decode, so every load stays inside the payload).
-template <int K>
-__device__ __forceinline__ void issue_blocks(const StreamInfo &si, uint32_t blk0, uint32_t nv, uint32_t first,
-                                             uint4 (&v)[K]) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(si.stream + si.po) + blk0;
-    const uint32_t last = nv ? nv - 1 : 0u;
-    static_for<0, K>([&](auto kc) __attribute__((always_inline)) {
+// A run's first eight blocks per lane, the whole ring, loaded by lane quads:
+// in load 2 k + h, lane 4 j + p takes block 4 h + p of lane 4 j + k's
+// sub-chunk, so the quad reads 64 consecutive bytes (one or two line requests
+// where four lanes on their own lines make four).  At the start of a run every
+// wave of the chip asks for its blocks at once, and the cache's request rate,
+// not the bytes, then sets how long the first fills take.  Block indexes are
+// clamped to the owner's last block (every lane of a ring run holds at least
+// one), so every load stays inside the payload.
+__device__ __forceinline__ void issue_fill(const StreamInfo &si, uint32_t blk0, uint32_t nv, uint32_t lane,
+                                           uint4 (&f)[2 * 4]) {
+    const uint4 *pay = reinterpret_cast<const uint4 *>(si.stream + si.po);
+    const uint32_t p = lane & 3;
+    static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
-        v[k] = src[min(first + (uint32_t)k, last)];
+        constexpr int kSel = k | k << 2 | k << 4 | k << 6;   // quad_perm k, k, k, k
+        const uint32_t b_o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)blk0, kSel, 0xf, 0xf, false);
+        const uint32_t last = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nv, kSel, 0xf, 0xf, false) - 1;
+        f[2 * k] = pay[b_o + min(p, last)];
+        f[2 * k + 1] = pay[b_o + min(4 + p, last)];
+    });
+}
+
+// The blocks of issue_fill into their owners' ring columns: block b = 4 h + p
+// of lane 4 j + k goes to rows 4 b + 1 .. 4 b + 4 of that lane's column, with
+// row 33 repeating row 1 and row 0 repeating row 32.  A lane writes other
+// lanes' columns here; the wave's LDS operations complete in order, so the
+// owners' later reads see the writes.
+__device__ __forceinline__ void write_fill(uint32_t rbase, uint32_t lane, const uint4 (&f)[2 * 4]) {
+    const uint32_t p = lane & 3;
+    static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        const uint32_t col = rbase + 4 * k - 4 * p;   // lane 4 j + k's column
+        static_for<0, 2>([&](auto hc) __attribute__((always_inline)) {
+            constexpr int h = decltype(hc)::value;
+            lds_u32 *q = (lds_u32 *)(size_t)(col + (16 * h + 4 * p + 1) * kRowBytes);
+            const uint4 v = f[2 * k + h];
+            q[0] = v.x;
+            q[64] = v.y;
+            q[128] = v.z;
+            q[192] = v.w;
+        });
+        if (p == 0) *(lds_u32 *)(size_t)(col + (kRingRows + 1) * kRowBytes) = f[2 * k].x;
+        if (p == 3) *(lds_u32 *)(size_t)col = f[2 * k + 1].w;
     });
 }
 
@@ -582,7 +615,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
             // workgroup.
             const DevTables *seg_tab = seg_tables<DecodeArgs>(seg);
             const bool reload = seg_tab != tab;
-            if (reload) __syncthreads();   // the previous segment's tables are no longer read
+            if (reload && tab) __syncthreads();   // the previous segment's tables are no longer read
             tab = seg_tab;
             // the table's 16-bit entries as stored; QLC's are widened to 32
             // bits in LDS (a 16-bit LDS read costs a mask at every use)
@@ -701,22 +734,18 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         const uint32_t start = (uint32_t)(L.sb - L.blk0 * 128);
         const uint32_t want = (uint32_t)(L.eb - L.blk0 * 128);
         const uint32_t pad_to = L.pad_end > L.eb ? (uint32_t)(L.pad_end - L.blk0 * 128) : 0u;
-        // the first four blocks, then the next task's index, then the next
-        // four blocks in the refill buffers, written at the first two points
-        // (so the ring holds eight blocks after 32 symbols)
-        uint4 f[4];
-        issue_blocks<4>(si, blk0, nv, 0, f);
-        if (have_next) next_raw = issue_index(a, si, run1 * 64 + lane);
+        // the ring's eight blocks, then the next task's index (loaded in
+        // every case, from this run's entries when there is no next task, so
+        // that the fill's wait never covers it), then the fill into the ring;
+        // the refill buffers start empty
+        uint4 f[2 * 4];
+        issue_fill(si, blk0, nv, lane, f);
+        next_raw = issue_index(a, si, (have_next ? run1 : run) * 64 + lane);
+        write_fill(rbase, lane, f);
         uint4 bufA[kBatch], bufB[kBatch];
-        uint32_t tagA = issue_batch(si, blk0, nv, 4, bufA);
-        uint32_t tagB = issue_batch(si, blk0, nv, 6, bufB);
-        {
-            const uint4 q0[kBatch] = {f[0], f[1]}, q1[kBatch] = {f[2], f[3]};
-            write_quarter(rbase, 0, q0);
-            write_quarter(rbase, 1, q1);
-        }
-        uint32_t nb = 4;   // blocks written so far
-        // each lane reads only its own column: program order suffices
+        uint32_t tagA = kNone, tagB = kNone;
+        uint32_t nb = 8;   // blocks written so far
+        // the wave's LDS operations complete in program order
         asm volatile("" ::: "memory");
 
         RingBits S;
