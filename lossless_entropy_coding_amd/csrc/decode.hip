@@ -558,8 +558,9 @@ __device__ __noinline__ void decode_rest(const LaneTask &L, const uint32_t *payl
 //   round r, wave w of workgroup b takes run r * G * 16 + w * G + b (G
 //   workgroups), so a partial round still spreads over every CU.
 //   Several streams: workgroup-tasks of 16 consecutive runs of one stream
-//   (one per wave), workgroup b taking b, b + G, ...; the codebook tables of
-//   the stream sit in LDS while the workgroup decodes it.
+//   (one per wave); workgroup b takes a range of consecutive tasks, which
+//   mostly lie in one stream, so the header is checked once, the tables stay
+//   in LDS, and each next task's index entries are in flight during a run.
 template <int CODEC, int PAIRS>
 __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const DecodeArgs a) {
     constexpr int kWaves = waves_for<CODEC>();
@@ -590,6 +591,10 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
     const bool one_stream = a.n_seg == 1;
     const uint32_t Q = (R + kWaves - 1) / kWaves;           // workgroup-tasks per stream (several streams)
     const uint32_t n_u = one_stream ? (R + G * kWaves - 1) / (G * kWaves) * G : Q * a.n_seg;
+    // this workgroup's tasks: u_begin, u_begin + u_step, ... below u_end
+    const uint32_t per_wg = (n_u + G - 1) / G;
+    const uint32_t u_begin = one_stream ? b : b * per_wg, u_step = one_stream ? G : 1u;
+    const uint32_t u_end = one_stream ? n_u : min(n_u, u_begin + per_wg);
     // stream and run of this wave in workgroup-task u (run >= R: none)
     auto seg_of = [&](uint32_t u) __attribute__((always_inline)) { return one_stream ? 0u : u / Q; };
     auto run_of = [&](uint32_t u) __attribute__((always_inline)) -> uint32_t {
@@ -607,7 +612,7 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
     bool seg_ok = false, have_next = false, have_first = false;
     IndexRaw next_raw = {}, first_raw = {};
 
-    for (uint32_t u = b; u < n_u; u += G) {
+    for (uint32_t u = u_begin; u < u_end; u += u_step) {
         const uint32_t seg = seg_of(u);
         if (seg != cur_seg) {
             // Streams coded with the codebook already in LDS (a batch with one
@@ -713,9 +718,9 @@ __global__ __launch_bounds__(64 * waves_for<CODEC>()) void decode_kernel(const D
         const bool live = L.ok && L.cnt > 0;   // L.nv == 0 then means a sub-chunk without bits: corrupt
         const bool full = live && L.cnt == kSub && L.nv > 0;
         // the next task's index entries, in flight during this run
-        const uint32_t u1 = u + G;
-        const uint32_t run1 = u1 < n_u ? run_of(u1) : R;
-        have_next = u1 < n_u && seg_of(u1) == seg && run1 < R;
+        const uint32_t u1 = u + u_step;
+        const uint32_t run1 = u1 < u_end ? run_of(u1) : R;
+        have_next = u1 < u_end && seg_of(u1) == seg && run1 < R;
         uint8_t *const wave_out = a.out + (uint64_t)seg * a.out_stride + (uint64_t)g0 * kSub;
         const uint32_t *payload = reinterpret_cast<const uint32_t *>(si.stream + si.po);
         if (__ballot(full) != ~0ull) {
