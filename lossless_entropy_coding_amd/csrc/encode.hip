@@ -396,7 +396,7 @@ struct PairCache {
 // Pass 1 over row r: cache the pairs; returns the piece's bit length and
 // sets wide when a pair exceeds 32 bits.  All 16 bytes are looked up; bytes
 // past the end of a piece are cleared afterwards by clear_tail.
-template <int ROWS>
+template <int ROWS, bool WIDE>
 __device__ __forceinline__ uint32_t cache_row(PairCache<ROWS> &cc, int r, const uint4 &v, const uint32_t *lut32,
                                               bool &wide) {
     uint32_t pk[2] = {0, 0}, mx = 0;
@@ -407,11 +407,20 @@ __device__ __forceinline__ uint32_t cache_row(PairCache<ROWS> &cc, int r, const 
         // the first code has at most 26 bits: the shift takes e1's low 5 bits
         cc.c[r][p] = (e1 & ~63u) | ((e2 & ~63u) >> (e1 & 31u));
         pk[p >> 2] |= l12 << (8 * (p & 3));
-        mx = max(mx, l12);
+        if constexpr (!WIDE) mx = max(mx, l12);
     });
     cc.pk[r][0] = pk[0];
     cc.pk[r][1] = pk[1];
-    wide = mx > 32u;
+    if constexpr (WIDE) {
+        // a length byte above 32, from the packed bytes (at most 52 each:
+        // adding 95 sets bit 7 exactly then, with no carry into the next
+        // byte).  A running maximum over the pairs kept 24 more registers
+        // live through the packer (114 against 90) and cost a CU one of its
+        // five workgroups.
+        wide = (((pk[0] + 0x5f5f5f5fu) | (pk[1] + 0x5f5f5f5fu)) & 0x80808080u) != 0u;
+    } else {
+        wide = mx > 32u;   // (never: codes of at most 16 bits; unused)
+    }
     return __builtin_amdgcn_sad_u8(pk[0], 0u, __builtin_amdgcn_sad_u8(pk[1], 0u, 0u));
 }
 
@@ -536,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 4) void encode_pack_staged_kernel(const E
     bool wide[ROWS];
     static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
         constexpr int r = decltype(rc)::value;
-        plen[r] = cache_row<ROWS>(cc, r, v[r], lut32, wide[r]);
+        plen[r] = cache_row<ROWS, WIDE>(cc, r, v[r], lut32, wide[r]);
     });
     if (p.cn != (uint32_t)(ROWS * kRowSyms)) {   // the segment's last chunk: drop missing symbols
         static_for<0, ROWS>([&](auto rc) __attribute__((always_inline)) {
