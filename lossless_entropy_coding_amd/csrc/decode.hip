@@ -23,8 +23,8 @@
 // lanes share: one request).  So a buffer's blocks are always written at its
 // next turn, two points (32 symbols) after their loads were issued, and
 // every point issues the same two load instructions: the wave waits for the
-// loads of two points before, never for the ones just issued, and nothing is
-// fetched twice.  Ring addresses are taken modulo the ring, so no read ever
+// loads of two points before, never for the ones just issued, and no block
+// is requested twice.  Ring addresses are taken modulo the ring, so no read ever
 // leaves the region, whatever the data.  A lane that consumed bits the ring did not
 // yet hold (more than 16 bits a symbol for 32 symbols: long codes only)
 // decodes its run again from global memory afterwards.
@@ -402,11 +402,12 @@ __device__ __forceinline__ LaneTask resolve(const DecodeArgs &a, const StreamInf
 // A run's first eight blocks per lane, the whole ring, loaded by lane quads:
 // in load 2 k + h, lane 4 j + p takes block 4 h + p of lane 4 j + k's
 // sub-chunk, so the quad reads 64 consecutive bytes (one or two line requests
-// where four lanes on their own lines make four).  At the start of a run every
-// wave of the chip asks for its blocks at once, and the cache's request rate,
-// not the bytes, then sets how long the first fills take.  Block indexes are
-// clamped to the owner's last block (every lane of a ring run holds at least
-// one), so every load stays inside the payload.
+// where four lanes on their own lines make four).  Fewer requests shorten the
+// fills of later runs, which queue behind other waves' refills and stores;
+// the very first fills of a launch, every wave of the chip asking at once,
+// are bound by the bytes either way.  Block indexes are clamped to the
+// owner's last block (every lane of a ring run holds at least one), so every
+// load stays inside the payload.
 __device__ __forceinline__ void issue_fill(const StreamInfo &si, uint32_t blk0, uint32_t nv, uint32_t lane,
                                            uint4 (&f)[2 * 4]) {
     const uint4 *pay = reinterpret_cast<const uint4 *>(si.stream + si.po);
